@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Sparse-decode benchmark on one MI355X.
+
+A step is one decode query for every sequence of the batch through
+cobs_sparse_attn_decode: block scoring + top-k, then the selected-block,
+sliding-window and compressed branches with the gated combine.  Inputs are
+seeded synthetic tensors resident in HBM before timing; the per-block summaries
+are built once per prefix (outside the timed region), as in decoding.
+
+Each timed step reads a different replica of every input (K, V, summaries,
+pooled tokens, Q, gates), with enough replicas that a step's bytes are not
+served from the 256 MB last-level cache by an earlier step; steps are issued as
+HIP graph replays so host launch overhead does not bound the GPU.
+
+Prints one JSON line (last line of stdout).  --gpus > 1 is refused: this build
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, lens, sel, alpha):
+    """Bytes the method must move per decode step (per kernel), from the
+    selection actually made: SLC blocks, the window minus its overlap with SLC,
+    the pooled tokens, summaries of the candidate blocks, Q, gates, output."""
+    es = 2 if w.dtype == "bf16" else 4
+    d, G = w.head_dim, w.group
+    so_ch = 0 if alpha == 0 else (w.rank if w.so_kind == "lowrank" else 1)
+    attn = sel_b = 0
+    for b in range(w.batch):
+        L = int(lens[b])
+        nb = -(-L // 64)
+        nc = (L - 32) // 16 + 1 if (w.cmp_len and L >= 32) else 0
+        win = set(range(max(0, L - w.window), L)) if w.window else set()
+        for h in range(w.n_kv_heads):
+            slc = set()
+            for blk in sel[b, h]:
+                if blk >= 0:
+                    slc.update(range(64 * blk, min(64 * blk + 64, L)))
+            attn += (len(slc) + len(win - slc) + nc) * d * 2 * es
+            sel_b += nb * d * 4 * (1 + so_ch)
+    q = w.batch * w.n_q_heads * d * es
+    attn += q + w.batch * w.n_q_heads * (3 * 4 + d * 4) + sel.size * 4
+    sel_b += q + sel.size * 4
+    return attn, sel_b
+
+
+def cpu_baseline(w, x, seconds):
+    """The fp64 oracle timed on the host for a bounded sample of decode queries."""
+    from threadpoolctl import threadpool_limits
+    from oracle import cobs_oracle as O
+    p = O.params_of(w)
+    G = w.group
+    # summaries are per-prefix state, built once (untimed) as on the GPU side
+    units = {}
+    seqs = list(range(w.batch))
+    for s in seqs[:4]:
+        L = int(x["lens"][s])
+        for h in range(w.n_kv_heads):
+            keys = x["K"][s, h, :L].astype(np.float64)
+            vals = x["V"][s, h, :L].astype(np.float64)
+            units[(s, h)] = (keys, vals, L) + O.build_unit(p, keys, vals, L)
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            s = seqs[done % min(4, len(seqs))]
+            for h in range(w.n_kv_heads):
+                keys, vals, L, summ, kc, vc = units[(s, h)]
+                qg = x["Q"][s, 0, h * G:(h + 1) * G].astype(np.float64)
+                gt = x["gates"][s, 0, h * G:(h + 1) * G].astype(np.float64) if x["gates"] is not None else None
+                O.query_group(p, qg, keys, vals, L, L - 1, summ, kc, vc, gt)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": done / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode queries (all {w.n_kv_heads} kv-head groups each) over sequences "
+                      f"{seqs[:4]} of {w.name}, {el:.1f} s, summaries prebuilt"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="decode_b1_L32k")
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the last-level cache")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+              "(multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_compressed_amd import binding as B
+    from block_sparse_long_compressed_amd import synth
+    from tests import gpu_util as U
+
+    w = synth.WORKLOADS[args.workload]
+    if w.prefill:
+        raise SystemExit("bench.py times decode workloads")
+    alpha = w.alpha if args.alpha is None else args.alpha
+    log(f"[bench] workload {w.name} alpha {alpha}: generating inputs")
+    x = synth.make_inputs(w, args.seed)
+    p = U.params_for(w, alpha=alpha)
+    B.lib()
+    g0 = U.to_device(x)
+    s0 = U.build(p, g0)
+    torch.cuda.synchronize()
+
+    # one untimed step to get the selection for the byte model
+    out0, sel0 = U.decode(p, g0, s0)
+    attn_bytes, sel_bytes = algorithmic_bytes(w, x["lens"], sel0, alpha)
+    step_bytes = attn_bytes + sel_bytes
+    R = args.replicas or max(3, math.ceil(2 * MALL_BYTES / step_bytes))
+    log(f"[bench] step bytes {step_bytes / 2**20:.2f} MiB, replicas {R}")
+
+    reps = []
+    for r in range(R):
+        g = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in g0.items()}
+        s = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in s0.items()}
+        ws = B.alloc_workspace(p, w.batch, w.max_len)
+        out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        sel = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+        reps.append((g, s, ws, out, sel))
+    del g0, s0
+    torch.cuda.synchronize()
+
+    def step(i, with_sel_in=False):
+        g, s, ws, out, sel = reps[i % R]
+        if with_sel_in:
+            B.cobs_sparse_attn_decode(p, g["lens"], g["Q"], g["K"], g["V"], s["mu"], s["so"], s["kc"], s["vc"],
+                                      g["gates"], out, ws, sel_in=sel)
+        else:
+            B.cobs_sparse_attn_decode(p, g["lens"], g["Q"], g["K"], g["V"], s["mu"], s["so"], s["kc"], s["vc"],
+                                      g["gates"], out, ws, sel_out=sel)
+
+    def capture(fn_list):
+        graph = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            for f in fn_list:          # warm the allocator-free path once outside capture
+                f()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for f in fn_list:
+                f()
+        torch.cuda.synchronize()
+        return graph
+
+    full = capture([lambda i=i: step(i) for i in range(R)])
+    singles = [capture([lambda i=i: step(i)]) for i in range(R)]
+    attn_only = capture([lambda i=i: step(i, with_sel_in=True) for i in range(R)])
+
+    def run_steps(n):
+        for _ in range(n // R):
+            full.replay()
+        for i in range(n % R):
+            singles[i].replay()
+
+    log(f"[bench] warmup {args.warmup}")
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    run_steps(args.steps)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {ms_step * 1e3:.2f} us/step (host wall {wall / args.steps * 1e6:.2f} us/step)")
+
+    # dominant kernel alone: the attention kernel, fed the selection of the same step
+    n_attn = max(R, (args.steps // R) * R)
+    for _ in range(2):
+        attn_only.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(n_attn // R):
+        attn_only.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    attn_us = ev0.elapsed_time(ev1) * 1e3 / n_attn
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    log(f"[bench] attention kernel {attn_us:.2f} us, {achieved:.0f} GB/s")
+
+    qps = w.batch / (ms_step * 1e-3)
+    kv_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "sparse-decode queries/s and achieved HBM GB/s (% of peak) at 32k ctx, top-k=16",
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "achieved_GBps": kv_gbps,
+        "pct_of_hbm_peak": 100.0 * kv_gbps / HBM_PEAK_GBPS,
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.max_len,
+                   "seq_len_min": w.min_len, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "block": 64, "top_k": w.top_k, "window": w.window,
+                   "cmp": [w.cmp_len, w.cmp_stride], "second_order": w.so_kind, "rank": w.rank,
+                   "alpha": alpha, "step_bytes": step_bytes, "replicas": R, "graph_replay": True},
+        "roofline": {"bound": "hbm", "kernel": "k_attn_decode", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "bytes_per_launch": attn_bytes, "avg_launch_us": attn_us},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

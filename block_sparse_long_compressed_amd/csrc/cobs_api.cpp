@@ -1,0 +1,254 @@
+// C ABI of the library: argument validation, workspace planning and launches.
+// Every check happens on the host before the first HIP call, so an invalid call
+// enqueues nothing (see include/cobs.h for the contract).
+#include "../../include/cobs.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "cobs_launch.h"
+
+namespace {
+
+using namespace cobs;
+
+constexpr int kTargetWaves = 4096;      // wave-tiles that keep 256 CUs busy
+constexpr size_t kAlign = 256;
+constexpr int kMaxBlocks = 4096;        // per sequence (selection keeps <= 16 keys per thread)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+int64_t nb_of(int max_len) { return (max_len + 63) / 64; }
+int64_t nc_of(const cobs_params* p, int max_len) {
+  return (p->cmp_len > 0 && max_len >= 32) ? (max_len - 32) / 16 + 1 : 0;
+}
+float scale_of(const cobs_params* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim); }
+int group_of(const cobs_params* p) { return p->n_q_heads / p->n_kv_heads; }
+
+cobs_status check_params(const cobs_params* p) {
+  if (!p) return COBS_ERR_INVALID_ARG;
+  if (p->n_q_heads < 1 || p->n_kv_heads < 1 || p->n_q_heads % p->n_kv_heads) return COBS_ERR_INVALID_ARG;
+  if (p->top_k < 1 || p->top_k > 64) return COBS_ERR_INVALID_ARG;
+  if (p->window < 0) return COBS_ERR_INVALID_ARG;
+  if (p->cmp_len < 0 || p->cmp_stride < 0) return COBS_ERR_INVALID_ARG;
+  if (p->so_kind != COBS_SO_DIAG && p->so_kind != COBS_SO_LOWRANK) return COBS_ERR_INVALID_ARG;
+  if (p->so_kind == COBS_SO_LOWRANK && (p->rank < 1 || p->rank > 8)) return COBS_ERR_INVALID_ARG;
+  if (!(p->alpha >= 0.f) || !isfinite(p->alpha)) return COBS_ERR_INVALID_ARG;
+  if (!(p->scale >= 0.f) || !isfinite(p->scale)) return COBS_ERR_INVALID_ARG;
+  if (p->kv_dtype != COBS_BF16 && p->kv_dtype != COBS_F32) return COBS_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return COBS_ERR_UNSUPPORTED;
+  if (p->block_size != 64) return COBS_ERR_UNSUPPORTED;
+  const int G = group_of(p);
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return COBS_ERR_UNSUPPORTED;
+  if (p->cmp_len != 0 && !(p->cmp_len == 32 && p->cmp_stride == 16)) return COBS_ERR_UNSUPPORTED;
+  return COBS_OK;
+}
+
+cobs_status check_sizes(int batch, int max_len, int tokens) {
+  if (batch < 1 || max_len < 1 || tokens < 1) return COBS_ERR_INVALID_ARG;
+  if (nb_of(max_len) > kMaxBlocks) return COBS_ERR_UNSUPPORTED;
+  return COBS_OK;
+}
+
+// Launch shapes and the workspace carve-up; a pure function of the sizes so that
+// cobs_workspace_bytes and every call agree.
+struct Plan {
+  int units_sel, units_attn;
+  int sel_tpw, sel_splits;
+  int attn_waves, attn_tpw, wg_slc, wg_win, wg_cmp, attn_P;
+  size_t off_cnt_sel, off_cnt_attn, off_scores, off_lse, off_sel, off_ml, off_o, total;
+};
+
+Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
+  Plan pl;
+  const int hkv = p->n_kv_heads, G = group_of(p), d = p->head_dim;
+  const int nb = (int)nb_of(max_len);
+  const int nb_pad = (nb + 15) / 16 * 16;
+  pl.units_sel = batch * tokens * hkv;
+  pl.units_attn = batch * hkv;
+  // scoring: 16-block tiles, 4 waves per workgroup
+  const int tiles = cdiv(nb, 16);
+  pl.sel_tpw = std::min(8, std::max(1, cdiv(pl.units_sel * tiles, kTargetWaves)));
+  pl.sel_splits = cdiv(tiles, 4 * pl.sel_tpw);
+  // attention: 64-key tiles of the three branches
+  const int t_slc = p->top_k;
+  const int t_win = p->window > 0 ? cdiv(std::min(p->window, max_len), 64) : 0;
+  const int t_cmp = cdiv((int)nc_of(p, max_len), 64);
+  pl.attn_waves = 4;
+  pl.attn_tpw = std::min(8, std::max(1, cdiv(pl.units_attn * (t_slc + t_win + t_cmp), kTargetWaves)));
+  const int per_wg = pl.attn_waves * pl.attn_tpw;
+  pl.wg_slc = cdiv(t_slc, per_wg);
+  pl.wg_win = cdiv(t_win, per_wg);
+  pl.wg_cmp = cdiv(t_cmp, per_wg);
+  pl.attn_P = pl.wg_slc + pl.wg_win + pl.wg_cmp;
+
+  size_t off = 0;
+  pl.off_cnt_sel = off;  off = align_up(off + sizeof(uint32_t) * pl.units_sel);
+  pl.off_cnt_attn = off; off = align_up(off + sizeof(uint32_t) * pl.units_attn);
+  pl.off_scores = off;   off = align_up(off + sizeof(float) * (size_t)pl.units_sel * 16 * nb_pad);
+  pl.off_lse = off;      off = align_up(off + sizeof(float) * (size_t)pl.units_sel * pl.sel_splits * 32);
+  pl.off_sel = off;      off = align_up(off + sizeof(int32_t) * (size_t)pl.units_sel * p->top_k);
+  pl.off_ml = off;       off = align_up(off + sizeof(float) * (size_t)pl.units_attn * pl.attn_P * 32);
+  pl.off_o = off;        off = align_up(off + sizeof(float) * (size_t)pl.units_attn * pl.attn_P * G * d);
+  pl.total = off;
+  return pl;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+cobs_status hip_status(hipError_t e) { return e == hipSuccess ? COBS_OK : COBS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* cobs_status_string(int32_t status) {
+  switch (status) {
+    case COBS_OK: return "ok";
+    case COBS_ERR_INVALID_ARG: return "invalid argument";
+    case COBS_ERR_UNSUPPORTED: return "unsupported configuration";
+    case COBS_ERR_WORKSPACE: return "workspace too small";
+    case COBS_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+cobs_status cobs_validate_params(const cobs_params* p) { return check_params(p); }
+
+cobs_status cobs_summary_shapes(const cobs_params* p, int32_t batch, int32_t max_len, int64_t* nb_max,
+                                int64_t* nc_max, size_t* mu_bytes, size_t* so_bytes, size_t* pooled_bytes) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
+  const int64_t nb = nb_of(max_len), nc = nc_of(p, max_len);
+  const size_t rows = (size_t)batch * p->n_kv_heads;
+  const size_t esz = p->kv_dtype == COBS_BF16 ? 2 : 4;
+  if (nb_max) *nb_max = nb;
+  if (nc_max) *nc_max = nc;
+  if (mu_bytes) *mu_bytes = rows * nb * p->head_dim * sizeof(float);
+  if (so_bytes) *so_bytes = rows * nb * p->head_dim * sizeof(float) * (p->so_kind == COBS_SO_LOWRANK ? p->rank : 1);
+  if (pooled_bytes) *pooled_bytes = rows * nc * p->head_dim * esz;
+  return COBS_OK;
+}
+
+size_t cobs_workspace_bytes(const cobs_params* p, int32_t batch, int32_t max_len, int32_t n_q_tokens) {
+  if (check_params(p) != COBS_OK || check_sizes(batch, max_len, n_q_tokens) != COBS_OK) return 0;
+  return make_plan(p, batch, max_len, n_q_tokens).total;
+}
+
+cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
+                                 const void* K, const void* V, float* mu, float* so, void* kc, void* vc,
+                                 void* stream) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
+  const bool pool = p->cmp_len > 0 && nc_of(p, max_len) > 0;
+  if (!seq_lens || !K || !mu || !so) return COBS_ERR_INVALID_ARG;
+  if (pool && (!V || !kc || !vc)) return COBS_ERR_INVALID_ARG;
+  BuildArgs a;
+  a.batch = batch; a.hkv = p->n_kv_heads; a.max_len = max_len;
+  a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len);
+  a.head_dim = p->head_dim; a.rank = p->rank; a.bf16 = p->kv_dtype == COBS_BF16;
+  const int units = batch * p->n_kv_heads;
+  a.blocks_per_wave = std::min(8, std::max(2, cdiv(units * a.nb_max, 4 * 256 * 4)));
+  a.seq_lens = seq_lens; a.K = K; a.V = pool ? V : K;
+  a.mu = mu;
+  a.var = p->so_kind == COBS_SO_DIAG ? so : nullptr;
+  a.lowrank = p->so_kind == COBS_SO_LOWRANK ? so : nullptr;
+  a.kc = pool ? kc : nullptr; a.vc = pool ? vc : nullptr;
+  a.stream = (hipStream_t)stream;
+  if ((st = hip_status(launch_build_diag(a))) != COBS_OK) return st;
+  if (a.lowrank) st = hip_status(launch_build_lowrank(a));
+  return st;
+}
+
+static cobs_status select_impl(const cobs_params* p, const Plan& pl, int32_t batch, int32_t max_len,
+                               const int32_t* seq_lens, int32_t tokens, int32_t q_pos0, const void* Q,
+                               const float* mu, const float* so, int32_t* sel, float* sel_score, void* ws,
+                               hipStream_t stream) {
+  SelectArgs a;
+  a.batch = batch; a.tokens = tokens; a.hkv = p->n_kv_heads; a.group = group_of(p);
+  a.head_dim = p->head_dim; a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.top_k = p->top_k;
+  a.rank = p->rank; a.so_kind = p->so_kind; a.q_pos0 = q_pos0; a.bf16 = p->kv_dtype == COBS_BF16;
+  a.alpha = p->alpha; a.scale = scale_of(p); a.splits = pl.sel_splits; a.tiles_per_wave = pl.sel_tpw;
+  a.seq_lens = seq_lens; a.Q = Q; a.mu = mu; a.so = so; a.sel = sel; a.sel_score = sel_score;
+  a.counters = at<uint32_t>(ws, pl.off_cnt_sel);
+  a.scores = at<float>(ws, pl.off_scores);
+  a.lse_part = at<float>(ws, pl.off_lse);
+  a.stream = stream;
+  return hip_status(launch_select(a));
+}
+
+cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
+                             int32_t n_q_tokens, int32_t q_pos0, const void* Q, const float* mu, const float* so,
+                             int32_t* sel, float* sel_score, void* ws, size_t ws_bytes, void* stream) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(batch, max_len, n_q_tokens)) != COBS_OK) return st;
+  if (q_pos0 < 0 && n_q_tokens != 1) return COBS_ERR_INVALID_ARG;
+  if (q_pos0 >= 0 && (int64_t)q_pos0 + n_q_tokens > max_len) return COBS_ERR_INVALID_ARG;
+  if (!seq_lens || !Q || !mu || !so || !sel || !ws) return COBS_ERR_INVALID_ARG;
+  const Plan pl = make_plan(p, batch, max_len, n_q_tokens);
+  if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
+  return select_impl(p, pl, batch, max_len, seq_lens, n_q_tokens, q_pos0, Q, mu, so, sel, sel_score, ws,
+                     (hipStream_t)stream);
+}
+
+cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
+                                    const void* Q, const void* K, const void* V, const float* mu, const float* so,
+                                    const void* kc, const void* vc, const float* gates, const int32_t* sel_in,
+                                    int32_t* sel_out, float* out, void* ws, size_t ws_bytes, void* stream) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
+  const bool cmp_on = p->cmp_len > 0 && nc_of(p, max_len) > 0;
+  if (!seq_lens || !Q || !K || !V || !out || !ws) return COBS_ERR_INVALID_ARG;
+  if (!sel_in && (!mu || !so)) return COBS_ERR_INVALID_ARG;
+  if (cmp_on && (!kc || !vc)) return COBS_ERR_INVALID_ARG;
+  const Plan pl = make_plan(p, batch, max_len, 1);
+  if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t* sel = sel_in;
+  if (!sel) {
+    int32_t* dst = sel_out ? sel_out : at<int32_t>(ws, pl.off_sel);
+    if ((st = select_impl(p, pl, batch, max_len, seq_lens, 1, -1, Q, mu, so, dst, nullptr, ws, s)) != COBS_OK)
+      return st;
+    sel = dst;
+  } else if (sel_out && sel_out != sel_in) {
+    if (hipMemcpyAsync(sel_out, sel_in, sizeof(int32_t) * (size_t)batch * p->n_kv_heads * p->top_k,
+                       hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return COBS_ERR_HIP;
+  }
+  AttnArgs a;
+  a.batch = batch; a.hkv = p->n_kv_heads; a.group = group_of(p); a.head_dim = p->head_dim;
+  a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len);
+  a.top_k = p->top_k; a.window = p->window; a.cmp_on = cmp_on ? 1 : 0; a.bf16 = p->kv_dtype == COBS_BF16;
+  a.scale = scale_of(p); a.waves_per_wg = pl.attn_waves; a.tiles_per_wave = pl.attn_tpw;
+  a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
+  a.seq_lens = seq_lens; a.Q = Q; a.K = K; a.V = V; a.kc = kc; a.vc = vc; a.gates = gates; a.sel = sel;
+  a.out = out;
+  a.counters = at<uint32_t>(ws, pl.off_cnt_attn);
+  a.part_ml = at<float>(ws, pl.off_ml);
+  a.part_o = at<float>(ws, pl.off_o);
+  a.stream = s;
+  return hip_status(launch_attn_decode(a));
+}
+
+cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int32_t n_q_tokens, int32_t q_pos0,
+                                     const void* Q, const void* K, const void* V, const float* mu, const float* so,
+                                     const void* kc, const void* vc, const float* gates, int32_t* sel_out,
+                                     float* out, void* ws, size_t ws_bytes, void* stream) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(1, seq_len, n_q_tokens)) != COBS_OK) return st;
+  if (q_pos0 < 0 || (int64_t)q_pos0 + n_q_tokens > seq_len) return COBS_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !mu || !so || !out || !ws) return COBS_ERR_INVALID_ARG;
+  (void)kc; (void)vc; (void)gates; (void)sel_out; (void)ws_bytes; (void)stream;
+  return COBS_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

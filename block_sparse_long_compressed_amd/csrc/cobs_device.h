@@ -1,0 +1,82 @@
+// Device-side helpers for the gfx950 kernels: element types, 16-byte vector
+// loads, MFMA wrappers and wave-level reductions.  Wavefronts are 64 lanes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cobs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 64;      // keys per block (the method's block size)
+constexpr int kWave = 64;       // lanes per wavefront
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// Round-to-nearest-even float -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Element traits.  A 16-byte chunk holds kPer16 elements.
+struct EltBF16 {
+  typedef uint16_t storage;
+  static constexpr int kPer16 = 8;
+  static constexpr int kBytes = 2;
+  // unpack element e (0..7) of a 16-byte chunk
+  __device__ static __forceinline__ float get(const u32x4& c, int e) {
+    uint32_t w = c[e >> 1];
+    return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+  }
+};
+struct EltF32 {
+  typedef float storage;
+  static constexpr int kPer16 = 4;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float get(const u32x4& c, int e) { return __uint_as_float(c[e]); }
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ f32x4 ld_f32x4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ void st_f32x4(float* p, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+// D = A(16x32 bf16) * B(32x16 bf16) + C.  Lane l supplies A[l%16][8*(l/16)+j]
+// and B[8*(l/16)+j][l%16] (j = 0..7), and holds C[4*(l/16)+i][l%16] (i = 0..3).
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// D = A(16x4 f32) * B(4x16 f32) + C.  Lane l supplies A[l%16][l/16] and
+// B[l/16][l%16], and holds C[4*(l/16)+i][l%16].
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Order-preserving map of a float to uint32 (larger float -> larger key); -0 maps as +0.
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace cobs

@@ -1,0 +1,381 @@
+// Sparse decode attention over the three NSA branches with gated combine (gfx950).
+//
+// Branches (Janus issue #181 on NSA: compression, selection and sliding-window
+// paths with gates; COBS explainer, Technisches Resuemee 2.3: only the selector
+// changes): each branch is an exact softmax over its own key set,
+//   SLC - the keys of the top-k selected 64-key blocks,
+//   WIN - the last W positions,
+//   CMP - the mean-pooled tokens (32 keys every 16 positions),
+// and out = g_cmp o_cmp + g_slc o_slc + g_win o_win.
+//
+// Work is split into 64-key tiles.  One wavefront processes its tiles with an
+// online softmax for the whole GQA group at once: S = K Q^T is a 64x16 tile
+// computed with v_mfma_f32_16x16x32_bf16 (keys on the M side, the group's heads
+// on the N side, head_dim as the contraction), so each lane owns one head and a
+// fixed set of 16 keys; the probabilities it holds are exactly the B operand of
+// O^T = V^T P^T, so P never leaves registers.  V is staged in LDS row-major and
+// read as the transposed A operand.  K is loaded straight into the MFMA layout.
+// Every tile is read once from HBM with 16-byte loads.
+//
+// The waves of a workgroup merge their (max, sum, O) in LDS into one partial per
+// workgroup; the last workgroup of a (sequence, kv-head) (atomic counter) merges
+// the partials of each branch by log-sum-exp rescaling and applies the gates.
+#include "cobs_device.h"
+#include "cobs_launch.h"
+
+namespace cobs {
+
+struct AttnParams {
+  int hkv, group, max_len, nc_max, top_k, window, cmp_on;
+  int tiles_per_wave, wg_slc, wg_win, wg_cmp;
+  float scale_log2;                 // scale * log2(e)
+  const int32_t* seq_lens;
+  const void *Q, *K, *V, *kc, *vc;
+  const float* gates;
+  const int32_t* sel;
+  float* out;
+  uint32_t* counters;
+  float* part_ml;
+  float* part_o;
+};
+
+template <typename E, int D>
+struct AttnTiling {
+  static constexpr int kEpl = E::kPer16;                  // elements per 16-byte chunk
+  static constexpr int kChunks = D * E::kBytes / 64;      // 16-byte chunks per lane per key row
+  static constexpr int kLanesPerRow = D * E::kBytes / 16;
+  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
+  static constexpr int kLoads = kBlock / kRowsPerLoad;    // V staging loads per lane
+  static constexpr int kRowStride = D + 4;                // LDS row stride (elements), see reads
+  static constexpr int kDt = D / 16;                      // 16-wide output column tiles
+};
+
+template <typename E, int D>
+constexpr size_t attn_lds_bytes(int waves) {
+  using T = AttnTiling<E, D>;
+  const size_t stage = (size_t)waves * kBlock * T::kRowStride * E::kBytes;
+  const size_t merge = (size_t)waves * 16 * (D + 2) * sizeof(float);
+  return stage > merge ? stage : merge;
+}
+
+// One 64-key tile: rows [0, nvalid) of Kt / Vt (row stride D elements).
+template <typename E, int D>
+__device__ __forceinline__ void attend_tile(const typename E::storage* __restrict__ Kt,
+                                            const typename E::storage* __restrict__ Vt, int nvalid,
+                                            const u32x4 (&qf)[AttnTiling<E, D>::kChunks],
+                                            float scale_log2, typename E::storage* lds,
+                                            float& m_run, float& l_run,
+                                            f32x4 (&acc_o)[AttnTiling<E, D>::kDt]) {
+  using T = AttnTiling<E, D>;
+  constexpr int NCH = T::kChunks, EPL = T::kEpl, LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad;
+  constexpr int SV = T::kRowStride;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+
+  // issue all loads of the tile: K in MFMA layout, V rows for LDS staging
+  u32x4 kf[4][NCH];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = min(16 * t + n, nvalid - 1);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kf[t][c] = ld16(Kt + (size_t)r * D + (4 * c + g) * EPL);
+  }
+  u32x4 vf[T::kLoads];
+  const int vc_col = (lane % LPR) * EPL, vr0 = lane / LPR;
+#pragma unroll
+  for (int i = 0; i < T::kLoads; ++i) {
+    const int r = min(RPL * i + vr0, nvalid - 1);
+    vf[i] = ld16(Vt + (size_t)r * D + vc_col);
+  }
+
+  // S = K Q^T : acc_s[t][i] = q_n . k_{16t + 4g + i}
+  f32x4 acc_s[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if constexpr (E::kBytes == 2) {
+        a = mfma_bf16_16x16x32(kf[t][c], qf[c], a);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a = mfma_f32_16x16x4(__uint_as_float(kf[t][c][e]), __uint_as_float(qf[c][e]), a);
+      }
+    }
+    acc_s[t] = a;
+  }
+
+  // stage V (row-major, padded) in this wave's LDS slice
+#pragma unroll
+  for (int i = 0; i < T::kLoads; ++i) {
+    typename E::storage* dst = lds + (RPL * i + vr0) * SV + vc_col;
+    uint2* d2 = reinterpret_cast<uint2*>(dst);
+    d2[0] = make_uint2(vf[i][0], vf[i][1]);
+    d2[1] = make_uint2(vf[i][2], vf[i][3]);
+  }
+
+  // online softmax in the log2 domain; lane owns head n
+  float mt = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 16 * t + 4 * g + i;
+      const float x = (key < nvalid) ? acc_s[t][i] * scale_log2 : -INFINITY;
+      acc_s[t][i] = x;
+      mt = fmaxf(mt, x);
+    }
+  }
+  mt = fmaxf(mt, shfl_xor_f(mt, 16));
+  mt = fmaxf(mt, shfl_xor_f(mt, 32));
+  const float m_new = fmaxf(m_run, mt);
+  const float corr = fast_exp2(m_run - m_new);     // 0 when m_run = -inf
+  float psum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = fast_exp2(acc_s[t][i] - m_new);
+      acc_s[t][i] = pv;
+      psum += pv;
+    }
+  }
+  l_run = l_run * corr + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int dt = 0; dt < T::kDt; ++dt) acc_o[dt] *= corr;
+
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): V stores visible to this wave
+  __builtin_amdgcn_wave_barrier();
+
+  // O^T += V^T P^T
+  if constexpr (E::kBytes == 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 pb;
+      pb[0] = f32_to_bf16_bits(acc_s[2 * s][0]) | (f32_to_bf16_bits(acc_s[2 * s][1]) << 16);
+      pb[1] = f32_to_bf16_bits(acc_s[2 * s][2]) | (f32_to_bf16_bits(acc_s[2 * s][3]) << 16);
+      pb[2] = f32_to_bf16_bits(acc_s[2 * s + 1][0]) | (f32_to_bf16_bits(acc_s[2 * s + 1][1]) << 16);
+      pb[3] = f32_to_bf16_bits(acc_s[2 * s + 1][2]) | (f32_to_bf16_bits(acc_s[2 * s + 1][3]) << 16);
+      const uint16_t* vl = reinterpret_cast<const uint16_t*>(lds);
+#pragma unroll
+      for (int dt = 0; dt < T::kDt; ++dt) {
+        const int col = 16 * dt + n;
+        u32x4 va;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kb = 32 * s + 16 * h + 4 * g;
+          const uint32_t v0 = vl[(kb + 0) * SV + col], v1 = vl[(kb + 1) * SV + col];
+          const uint32_t v2 = vl[(kb + 2) * SV + col], v3 = vl[(kb + 3) * SV + col];
+          va[2 * h] = v0 | (v1 << 16);
+          va[2 * h + 1] = v2 | (v3 << 16);
+        }
+        acc_o[dt] = mfma_bf16_16x16x32(va, pb, acc_o[dt]);
+      }
+    }
+  } else {
+    const float* vl = reinterpret_cast<const float*>(lds);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * t + 4 * g + i;
+#pragma unroll
+        for (int dt = 0; dt < T::kDt; ++dt)
+          acc_o[dt] = mfma_f32_16x16x4(vl[key * SV + 16 * dt + n], acc_s[t][i], acc_o[dt]);
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();      // LDS slice reused by the next tile
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
+  using T = AttnTiling<E, D>;
+  constexpr int NCH = T::kChunks, EPL = T::kEpl, NDT = T::kDt;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int last_flag;
+
+  const int nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int head = blockIdx.y, seq = blockIdx.z;
+  const int unit = seq * p.hkv + head;
+  const int G = p.group;
+  const int L = p.seq_lens[seq];
+  const int P = p.wg_slc + p.wg_win + p.wg_cmp;
+
+  int branch, local;                       // 0 = SLC, 1 = WIN, 2 = CMP
+  if ((int)blockIdx.x < p.wg_slc) { branch = 0; local = blockIdx.x; }
+  else if ((int)blockIdx.x < p.wg_slc + p.wg_win) { branch = 1; local = blockIdx.x - p.wg_slc; }
+  else { branch = 2; local = blockIdx.x - p.wg_slc - p.wg_win; }
+
+  // the group's queries as the B operand of S = K Q^T (heads >= G are zero)
+  u32x4 qf[NCH];
+  {
+    const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
+                                    ((size_t)seq * p.hkv * G + (size_t)head * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      qf[c] = ld16(Qh + (4 * c + g) * EPL);
+      if (n >= G) qf[c] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
+  const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)unit * p.max_len * D;
+  const typename E::storage* kcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.kc) + (size_t)unit * p.nc_max * D : nullptr;
+  const typename E::storage* vcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.vc) + (size_t)unit * p.nc_max * D : nullptr;
+  const int nc = (p.cmp_on && L >= 32) ? (L - 32) / 16 + 1 : 0;
+  const int win_len = min(p.window, L);
+  const int win_start = L - win_len;
+
+  typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc_o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int j = 0; j < p.tiles_per_wave; ++j) {
+    const int tile = (local * nw + wave) * p.tiles_per_wave + j;
+    const typename E::storage *Kt, *Vt;
+    int nvalid = 0;
+    if (branch == 0) {
+      if (tile < p.top_k) {
+        const int b = p.sel[(size_t)unit * p.top_k + tile];
+        if (b >= 0) {
+          nvalid = min(kBlock, L - b * kBlock);
+          Kt = Ku + (size_t)b * kBlock * D;
+          Vt = Vu + (size_t)b * kBlock * D;
+        }
+      }
+    } else if (branch == 1) {
+      const int start = win_start + tile * kBlock;
+      if (start < L) {
+        nvalid = min(kBlock, L - start);
+        Kt = Ku + (size_t)start * D;
+        Vt = Vu + (size_t)start * D;
+      }
+    } else {
+      const int start = tile * kBlock;
+      if (start < nc) {
+        nvalid = min(kBlock, nc - start);
+        Kt = kcu + (size_t)start * D;
+        Vt = vcu + (size_t)start * D;
+      }
+    }
+    if (nvalid <= 0) continue;
+    attend_tile<E, D>(Kt, Vt, nvalid, qf, p.scale_log2, lds, m_run, l_run, acc_o);
+  }
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+
+  // ---- merge the waves of this workgroup in LDS ----------------------------
+  __syncthreads();                                   // staging slices no longer needed
+  float* mo = reinterpret_cast<float*>(smem);        // [nw][16][D] then [nw][16][2]
+  float* mml = mo + (size_t)nw * 16 * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mo[((size_t)wave * 16 + n) * D + 16 * dt + 4 * g + i] = acc_o[dt][i];
+  }
+  if (g == 0) { mml[(wave * 16 + n) * 2] = m_run; mml[(wave * 16 + n) * 2 + 1] = l_run; }
+  __syncthreads();
+  const size_t pslot = (size_t)unit * P + blockIdx.x;
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += blockDim.x) {
+    const int h = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+    float M = -INFINITY;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, mml[(w * 16 + h) * 2]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float Ls = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < nw; ++w) {
+        const float mw = mml[(w * 16 + h) * 2];
+        if (mw == -INFINITY) continue;
+        const float f = fast_exp2(mw - M);
+        Ls += f * mml[(w * 16 + h) * 2 + 1];
+        const float* src = mo + ((size_t)w * 16 + h) * D + d4;
+        o[0] += f * src[0]; o[1] += f * src[1]; o[2] += f * src[2]; o[3] += f * src[3];
+      }
+    }
+    st_f32x4(p.part_o + (pslot * G + h) * D + d4, o);
+    if (d4 == 0) { p.part_ml[(pslot * 16 + h) * 2] = M; p.part_ml[(pslot * 16 + h) * 2 + 1] = Ls; }
+  }
+
+  // ---- the last workgroup of this (sequence, kv-head) combines ------------
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(p.counters + unit, 1u);
+    last_flag = (prev == (uint32_t)(P - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+
+  const int pb[4] = {0, p.wg_slc, p.wg_slc + p.wg_win, P};
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += blockDim.x) {
+    const int h = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+    const int hq = head * G + h;
+    float gt[3] = {0.f, 1.f, 0.f};                     // (cmp, slc, win)
+    if (p.gates) {
+      const float* gp = p.gates + ((size_t)seq * p.hkv * G + hq) * 3;
+      gt[0] = gp[0]; gt[1] = gp[1]; gt[2] = gp[2];
+    }
+    f32x4 res = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int br = 0; br < 3; ++br) {
+      const float gate = (br == 0) ? gt[1] : (br == 1) ? gt[2] : gt[0];
+      float M = -INFINITY, Ls = 0.f;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      for (int q = pb[br]; q < pb[br + 1]; ++q) {
+        const size_t s = (size_t)unit * P + q;
+        const float mq = p.part_ml[(s * 16 + h) * 2], lq = p.part_ml[(s * 16 + h) * 2 + 1];
+        if (mq == -INFINITY || lq == 0.f) continue;
+        const f32x4 oq = ld_f32x4(p.part_o + (s * G + h) * D + d4);
+        if (mq > M) {
+          const float f = fast_exp2(M - mq);
+          Ls = Ls * f + lq;
+          o = o * f + oq;
+          M = mq;
+        } else {
+          const float f = fast_exp2(mq - M);
+          Ls += f * lq;
+          o += f * oq;
+        }
+      }
+      if (Ls > 0.f) res += (gate / Ls) * o;
+    }
+    st_f32x4(p.out + ((size_t)seq * p.hkv * G + hq) * D + d4, res);
+  }
+  if (threadIdx.x == 0) p.counters[unit] = 0u;
+}
+
+template <typename E, int D>
+static hipError_t launch_attn_t(const AttnArgs& a, const AttnParams& ap) {
+  const int P = a.wg_slc + a.wg_win + a.wg_cmp;
+  dim3 grid(P, a.hkv, a.batch);
+  const size_t lds = attn_lds_bytes<E, D>(a.waves_per_wg);
+  hipLaunchKernelGGL((k_attn_decode<E, D>), grid, dim3(64 * a.waves_per_wg), lds, a.stream, ap);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const AttnArgs& a) {
+  AttnParams ap;
+  ap.hkv = a.hkv; ap.group = a.group; ap.max_len = a.max_len; ap.nc_max = a.nc_max;
+  ap.top_k = a.top_k; ap.window = a.window; ap.cmp_on = a.cmp_on;
+  ap.tiles_per_wave = a.tiles_per_wave; ap.wg_slc = a.wg_slc; ap.wg_win = a.wg_win; ap.wg_cmp = a.wg_cmp;
+  ap.scale_log2 = a.scale * kLog2e;
+  ap.seq_lens = a.seq_lens; ap.Q = a.Q; ap.K = a.K; ap.V = a.V; ap.kc = a.kc; ap.vc = a.vc;
+  ap.gates = a.gates; ap.sel = a.sel; ap.out = a.out; ap.counters = a.counters;
+  ap.part_ml = a.part_ml; ap.part_o = a.part_o;
+  if (a.bf16) return a.head_dim == 128 ? launch_attn_t<EltBF16, 128>(a, ap) : launch_attn_t<EltBF16, 64>(a, ap);
+  return a.head_dim == 128 ? launch_attn_t<EltF32, 128>(a, ap) : launch_attn_t<EltF32, 64>(a, ap);
+}
+
+size_t attn_decode_lds_bytes(bool bf16, int head_dim, int waves) {
+  if (bf16) return head_dim == 128 ? attn_lds_bytes<EltBF16, 128>(waves) : attn_lds_bytes<EltBF16, 64>(waves);
+  return head_dim == 128 ? attn_lds_bytes<EltF32, 128>(waves) : attn_lds_bytes<EltF32, 64>(waves);
+}
+
+}  // namespace cobs

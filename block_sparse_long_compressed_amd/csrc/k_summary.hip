@@ -1,0 +1,226 @@
+// Per-block key summaries and pooled tokens (gfx950).
+//
+// COBS (gist.science explainer, Technisches Resuemee 2.2-2.3): each block of 64
+// keys is summarised, independently of any query, by its mean key (kappa_1) and a
+// compressed form of its key covariance (kappa_2).  The diagonal form stores the
+// per-coordinate variance (1/n_b normalisation).  The compressed branch of NSA
+// (Janus issue #181, compression path) attends over mean-pooled tokens: the mean
+// of 32 consecutive keys (values) every 16 positions.
+//
+// One wavefront streams a run of consecutive blocks of one (sequence, kv-head):
+// every 16-byte load instruction reads 1 KiB of contiguous rows, the block stays
+// in registers for the two-pass variance, and row sums are reduced with lane
+// shuffles.  Pooled token j = (chunk_j + chunk_{j+1}) / 32 where chunk_c is the
+// sum of rows [16c, 16c+16); the chunk after the run (the halo) is read once.
+#include "cobs_device.h"
+#include "cobs_launch.h"
+
+namespace cobs {
+
+template <typename E, int D>
+struct RowTiling {
+  static constexpr int kLanesPerRow = D * E::kBytes / 16;     // lanes covering one row
+  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;   // rows per load instruction
+  static constexpr int kLoads = kBlock / kRowsPerLoad;        // load instructions per block
+  static constexpr int kEpl = E::kPer16;                      // elements per lane per load
+  static_assert(kLanesPerRow >= 8 && kLanesPerRow <= 32, "unsupported row width");
+  static_assert(16 % kRowsPerLoad == 0, "a 16-row chunk must be whole loads");
+};
+
+// Sum over the lanes that share a column chunk (xor over the row-group bits).
+template <int kLanesPerRow>
+__device__ __forceinline__ float reduce_rows(float v) {
+#pragma unroll
+  for (int m = kLanesPerRow; m < kWave; m <<= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+
+template <typename E, int D>
+__device__ __forceinline__ void store_pooled(typename E::storage* dst, const float* v) {
+  constexpr int kEpl = E::kPer16;
+  if constexpr (E::kBytes == 2) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = f32_to_bf16_bits(v[2 * e]) | (f32_to_bf16_bits(v[2 * e + 1]) << 16);
+    st16(dst, w);
+  } else {
+    f32x4 w;
+#pragma unroll
+    for (int e = 0; e < kEpl; ++e) w[e] = v[e];
+    st_f32x4(reinterpret_cast<float*>(dst), w);
+  }
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(64) void k_build_diag(
+    const int32_t* __restrict__ seq_lens, int max_len, int nb_max, int nc_max,
+    const typename E::storage* __restrict__ K, const typename E::storage* __restrict__ V,
+    float* __restrict__ mu, float* __restrict__ var,
+    typename E::storage* __restrict__ kc, typename E::storage* __restrict__ vc,
+    int blocks_per_wave, int want_var, int want_pool) {
+  using T = RowTiling<E, D>;
+  constexpr int LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad, NL = T::kLoads, EPL = T::kEpl;
+  const int lane = threadIdx.x;
+  const int cc = lane % LPR;          // column chunk: columns [cc*EPL, cc*EPL+EPL)
+  const int rg = lane / LPR;          // row group: rows rg, rg+RPL, ...
+  const int hkv = gridDim.y;
+  const int head = blockIdx.y, seq = blockIdx.z;
+  const int L = seq_lens[seq];
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int b_begin = blockIdx.x * blocks_per_wave;
+  const int b_end = min(b_begin + blocks_per_wave, nb);
+  if (b_begin >= b_end) return;
+  const int nc = (want_pool && L >= 32) ? (L - 32) / 16 + 1 : 0;
+
+  const size_t unit = (size_t)seq * hkv + head;
+  const typename E::storage* Ku = K + unit * (size_t)max_len * D;
+  const typename E::storage* Vu = V + unit * (size_t)max_len * D;
+  float* mu_u = mu + unit * (size_t)nb_max * D;
+  float* var_u = var ? var + unit * (size_t)nb_max * D : nullptr;
+  typename E::storage* kc_u = want_pool ? kc + unit * (size_t)nc_max * D : nullptr;
+  typename E::storage* vc_u = want_pool ? vc + unit * (size_t)nc_max * D : nullptr;
+
+  float carry_k[EPL], carry_v[EPL];   // chunk 3 of the previous block
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) carry_k[e] = carry_v[e] = 0.f;
+
+  for (int b = b_begin; b < b_end; ++b) {
+    const int row0 = b * kBlock;
+    const int nrows = min(kBlock, L - row0);
+    u32x4 xk[NL], xv[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int r = min(row0 + i * RPL + rg, L - 1);
+      xk[i] = ld16(Ku + (size_t)r * D + cc * EPL);
+      if (want_pool) xv[i] = ld16(Vu + (size_t)r * D + cc * EPL);
+    }
+    float sum[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sum[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sum[e] += ok * E::get(xk[i], e);
+    }
+    float mean[EPL];
+    const float inv_n = 1.0f / (float)nrows;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) mean[e] = reduce_rows<LPR>(sum[e]) * inv_n;
+    if (rg == 0) {
+      float* dst = mu_u + (size_t)b * D + cc * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]});
+    }
+    if (want_var) {
+      float sq[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sq[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float dlt = E::get(xk[i], e) - mean[e];
+          sq[e] += ok * dlt * dlt;
+        }
+      }
+      float v[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[e] = reduce_rows<LPR>(sq[e]) * inv_n;
+      if (rg == 1 % RPL) {
+        float* dst = var_u + (size_t)b * D + cc * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]});
+      }
+    }
+    if (want_pool) {
+      // chunk sums (rows [16q, 16q+16) of this block), masked to valid rows
+      float ck[4][EPL], cv[4][EPL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float a = 0.f, c = 0.f;
+#pragma unroll
+          for (int i = q * 16 / RPL; i < (q + 1) * 16 / RPL; ++i) {
+            const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
+            a += ok * E::get(xk[i], e);
+            c += ok * E::get(xv[i], e);
+          }
+          ck[q][e] = reduce_rows<LPR>(a);
+          cv[q][e] = reduce_rows<LPR>(c);
+        }
+      }
+      // pooled token c = 4b + q - 1 spans chunk (4b+q-1) and chunk (4b+q)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * b + q - 1;
+        if (c < 0 || c >= nc) continue;
+        if (q == 0 && b == b_begin) continue;   // emitted by the wave that owns block b-1
+        float tk[EPL], tv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float pk = (q == 0) ? carry_k[e] : ck[q - 1][e];
+          const float pv = (q == 0) ? carry_v[e] : cv[q - 1][e];
+          tk[e] = (pk + ck[q][e]) * (1.0f / 32.0f);
+          tv[e] = (pv + cv[q][e]) * (1.0f / 32.0f);
+        }
+        if (rg == 2 % RPL) store_pooled<E, D>(kc_u + (size_t)c * D + cc * EPL, tk);
+        if (rg == 3 % RPL) store_pooled<E, D>(vc_u + (size_t)c * D + cc * EPL, tv);
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) { carry_k[e] = ck[3][e]; carry_v[e] = cv[3][e]; }
+    }
+  }
+  // halo: pooled token 4*b_end - 1 needs chunk 0 of block b_end
+  if (want_pool) {
+    const int c = 4 * b_end - 1;
+    if (c < nc) {   // then rows [64*b_end, 64*b_end + 16) are all < L
+      const int row0 = b_end * kBlock;
+      float a[EPL], v[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] = v[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16 / RPL; ++i) {
+        const int r = row0 + i * RPL + rg;
+        const u32x4 xk = ld16(Ku + (size_t)r * D + cc * EPL);
+        const u32x4 xv = ld16(Vu + (size_t)r * D + cc * EPL);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) { a[e] += E::get(xk, e); v[e] += E::get(xv, e); }
+      }
+      float tk[EPL], tv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        tk[e] = (carry_k[e] + reduce_rows<LPR>(a[e])) * (1.0f / 32.0f);
+        tv[e] = (carry_v[e] + reduce_rows<LPR>(v[e])) * (1.0f / 32.0f);
+      }
+      if (rg == 2 % RPL) store_pooled<E, D>(kc_u + (size_t)c * D + cc * EPL, tk);
+      if (rg == 3 % RPL) store_pooled<E, D>(vc_u + (size_t)c * D + cc * EPL, tv);
+    }
+  }
+}
+
+template <typename E, int D>
+static hipError_t launch_diag(const BuildArgs& a) {
+  const int bpw = a.blocks_per_wave;
+  dim3 grid((a.nb_max + bpw - 1) / bpw, a.hkv, a.batch);
+  hipLaunchKernelGGL((k_build_diag<E, D>), grid, dim3(64), 0, a.stream,
+                     a.seq_lens, a.max_len, a.nb_max, a.nc_max,
+                     (const typename E::storage*)a.K, (const typename E::storage*)a.V,
+                     a.mu, a.var, (typename E::storage*)a.kc, (typename E::storage*)a.vc,
+                     bpw, a.var != nullptr ? 1 : 0, a.kc != nullptr ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_diag(const BuildArgs& a) {
+  if (a.bf16) {
+    if (a.head_dim == 128) return launch_diag<EltBF16, 128>(a);
+    return launch_diag<EltBF16, 64>(a);
+  }
+  if (a.head_dim == 128) return launch_diag<EltF32, 128>(a);
+  return launch_diag<EltF32, 64>(a);
+}
+
+}  // namespace cobs

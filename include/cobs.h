@@ -1,0 +1,183 @@
+/*
+ * cobs.h - C ABI of the MI355X (gfx950) block-sparse attention library with the
+ * COBS second-order block selector.
+ *
+ * What it computes (sources cited by page title and section):
+ *   - "COBS: Cumulant Order Block Sparse Attention" (gist.science explainer,
+ *     Technisches Resuemee): sec. 2.1 ranks KV blocks by attention mass
+ *     m_b = sum_{r in b} exp(q.k_r); sec. 2.2 expands ln m_b in cumulants,
+ *     kappa_1 = block mean of the keys, kappa_2 = within-block key covariance;
+ *     sec. 2.3 scores blocks with q.mean + 1/2 q^T Sigma q from a query-independent
+ *     summary (mean + compressed covariance, top-r scaled eigenvectors).
+ *   - "cumulant-order-block-sparse-attention" skill card, "Method" and
+ *     "Implementation steps": keep the top-k blocks of score
+ *     first-order + alpha * cumulant term.
+ *   - GitHub issue "four dimensions regarding importance and connection
+ *     strength" (Janus #181): compression, selection and sliding-window paths
+ *     with gates g_cmp, g_slc.
+ *
+ * Definitions used throughout (logits are scale * q.k, scale = 1/sqrt(d) by default):
+ *   blocks      b = 0..NB-1, keys [64b, min(64b+64, L)), n_b keys, NB = ceil(L/64)
+ *   mu_b        mean of the block's keys
+ *   diag        var_b[j] = (1/n_b) sum_r (k_r[j] - mu_b[j])^2
+ *   lowrank     v_{b,i} = sqrt(lambda_i) u_i, the `rank` largest eigenpairs of
+ *               C_b = (1/n_b) sum_r (k_r - mu_b)(k_r - mu_b)^T (v = 0 if lambda <= 0)
+ *   score       s_{h,b} = ln n_b + scale q_h.mu_b + alpha/2 scale^2 Q2,
+ *               Q2 = sum_j q_{h,j}^2 var_b[j]  or  sum_i (q_h.v_{b,i})^2
+ *   group rank  shat_b = ln sum_{h in group} exp(s_{h,b} - LSE_{b' in cand} s_{h,b'})
+ *   candidates  blocks whose keys all lie at positions <= t (decode: t = L-1, all blocks)
+ *   selection   top-k by (shat desc, block index asc), listed in ascending block
+ *               order, padded with -1 when fewer than k candidates exist
+ *   branches    SLC: exact softmax over the keys of the selected blocks
+ *               WIN: exact softmax over positions [max(0, t-W+1), t]       (W = window)
+ *               CMP: exact softmax over pooled tokens (mean of 32 keys/values at
+ *                    stride 16; token j covers [16j, 16j+32), visible iff 16j+31 <= t)
+ *   output      g_cmp o_cmp + g_slc o_slc + g_win o_win, an empty branch gives 0
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or keeps them, and keeps no per-call state on the host.
+ *   - Layouts are dense row-major, head_dim innermost, 16-byte aligned.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = default stream)
+ *     and return without synchronising.  Asynchronous faults surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated on the host before any HIP call; an invalid call
+ *     returns COBS_ERR_INVALID_ARG / COBS_ERR_UNSUPPORTED / COBS_ERR_WORKSPACE
+ *     and enqueues nothing.  A failed launch returns COBS_ERR_HIP.
+ *   - No C++ exception crosses this boundary.  Calls are reentrant; two calls
+ *     that share one workspace must not run concurrently.
+ *   - Inputs holding NaN or Inf give unspecified (but in-bounds) results.
+ */
+#ifndef COBS_H_
+#define COBS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cobs_status {
+  COBS_OK = 0,
+  COBS_ERR_INVALID_ARG = 1,  /* null pointer, size out of range, inconsistent shape */
+  COBS_ERR_UNSUPPORTED = 2,  /* valid but not built: head_dim, group size, block size */
+  COBS_ERR_WORKSPACE = 3,    /* ws_bytes smaller than cobs_workspace_bytes() */
+  COBS_ERR_HIP = 4           /* a kernel launch failed */
+} cobs_status;
+
+typedef enum cobs_dtype { COBS_BF16 = 0, COBS_F32 = 1 } cobs_dtype;
+typedef enum cobs_so_kind { COBS_SO_DIAG = 0, COBS_SO_LOWRANK = 1 } cobs_so_kind;
+
+/* Method parameters.  Shared by every call of one attention layer. */
+typedef struct cobs_params {
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t n_q_heads;    /* H_q >= 1 */
+  int32_t n_kv_heads;   /* H_kv >= 1, H_q % H_kv == 0, group G = H_q/H_kv in {1,2,4,8,16} */
+  int32_t block_size;   /* must be 64 */
+  int32_t top_k;        /* k in [1, 64] */
+  int32_t window;       /* W >= 0; 0 disables the sliding-window branch */
+  int32_t cmp_len;      /* 0 disables the compressed branch; otherwise 32 */
+  int32_t cmp_stride;   /* 16 (required when cmp_len == 32) */
+  int32_t so_kind;      /* cobs_so_kind */
+  int32_t rank;         /* r in [1, 8] for COBS_SO_LOWRANK; ignored for diag */
+  float alpha;          /* >= 0; 0 = first-order (mean-pool) selector */
+  float scale;          /* logit scale > 0; 0 selects 1/sqrt(head_dim) */
+  int32_t kv_dtype;     /* cobs_dtype of Q, K, V and the pooled tokens */
+} cobs_params;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* cobs_status_string(int32_t status);
+
+/* Checks `p` alone.  Host only. */
+cobs_status cobs_validate_params(const cobs_params* p);
+
+/* Sizes of the caller-allocated summary tensors for a [batch][H_kv][max_len][d] KV cache:
+ * mu [batch][H_kv][NB][d] f32, so (diag) [batch][H_kv][NB][d] f32 or
+ * so (lowrank) [batch][H_kv][NB][rank][d] f32, pooled tokens kc/vc
+ * [batch][H_kv][NC][d] of kv_dtype, with NB = ceil(max_len/64) and
+ * NC = (max_len-32)/16 + 1 (0 if max_len < 32 or the branch is off).
+ * Each out-pointer may be NULL.  Returns COBS_ERR_INVALID_ARG on bad input. */
+cobs_status cobs_summary_shapes(const cobs_params* p, int32_t batch, int32_t max_len,
+                                int64_t* nb_max, int64_t* nc_max,
+                                size_t* mu_bytes, size_t* so_bytes, size_t* pooled_bytes);
+
+/* Workspace bytes needed by cobs_select_topk / cobs_sparse_attn_decode /
+ * cobs_sparse_attn_prefill for these sizes (n_q_tokens = 1 for decode).
+ * The workspace must be zero-filled before its first use (its counters are left
+ * zero by every call that completes).  Returns 0 when the arguments are invalid. */
+size_t cobs_workspace_bytes(const cobs_params* p, int32_t batch, int32_t max_len, int32_t n_q_tokens);
+
+/* Summary build (COBS Technisches Resuemee 2.2-2.3; NSA compression path).
+ * Reads K once (and V for the pooled values) and writes, per (sequence, kv-head, block),
+ * mu and the second-order channel, plus the pooled tokens kc, vc.
+ *   seq_lens  [batch] int32 device, 1 <= L_b <= max_len
+ *   K, V      [batch][H_kv][max_len][d] kv_dtype; positions >= L_b are never read
+ *   mu, so    see cobs_summary_shapes; entries of blocks >= NB(L_b) are left untouched
+ *   kc, vc    see cobs_summary_shapes; may be NULL iff cmp_len == 0; tokens j with
+ *             16j+32 > L_b are left untouched.  Stored as kv_dtype (bf16: RNE of the
+ *             fp32 mean). */
+cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t max_len,
+                                 const int32_t* seq_lens, const void* K, const void* V,
+                                 float* mu, float* so, void* kc, void* vc, void* stream);
+
+/* Block scoring, group aggregation and top-k (COBS 2.1-2.3; skill card "Method").
+ * Decode when q_pos0 < 0: n_q_tokens must be 1 and each sequence's query sits at
+ * t = L_b - 1.  Chunked prefill when q_pos0 >= 0: query i of every sequence sits at
+ * t = q_pos0 + i, and the caller guarantees q_pos0 + n_q_tokens <= L_b (checked on the
+ * host only against max_len).
+ *   Q          [batch][n_q_tokens][H_q][d] kv_dtype
+ *   mu, so     from cobs_build_summaries over the same K
+ *   sel        [batch][n_q_tokens][H_kv][top_k] int32 out, ascending, -1 padded
+ *   sel_score  NULL or [batch][n_q_tokens][H_kv][NB] f32 out: shat of candidate
+ *              blocks, -inf for the others
+ *   ws         workspace of at least cobs_workspace_bytes(p, batch, max_len, n_q_tokens) */
+cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_len,
+                             const int32_t* seq_lens, int32_t n_q_tokens, int32_t q_pos0,
+                             const void* Q, const float* mu, const float* so,
+                             int32_t* sel, float* sel_score,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step for every sequence: selection (unless sel_in is given), then the
+ * SLC, WIN and CMP branches and the gated combine (NSA three paths, COBS 2.3).
+ *   Q        [batch][H_q][d] kv_dtype, query at t = L_b - 1
+ *   K, V     [batch][H_kv][max_len][d] kv_dtype
+ *   mu, so   summaries; may be NULL iff sel_in != NULL
+ *   kc, vc   pooled tokens; may be NULL iff cmp_len == 0
+ *   gates    NULL (= g_cmp 0, g_slc 1, g_win 0) or [batch][H_q][3] f32 (cmp, slc, win)
+ *   sel_in   NULL or [batch][H_kv][top_k] int32 selection to use instead of scoring
+ *            (entries must be -1 or valid block indices of that sequence)
+ *   sel_out  NULL or [batch][H_kv][top_k] int32 out (the selection used)
+ *   out      [batch][H_q][d] f32 out */
+cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t max_len,
+                                    const int32_t* seq_lens, const void* Q,
+                                    const void* K, const void* V,
+                                    const float* mu, const float* so,
+                                    const void* kc, const void* vc, const float* gates,
+                                    const int32_t* sel_in, int32_t* sel_out, float* out,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* Chunked causal prefill of one sequence: queries at t = q_pos0 .. q_pos0+n_q_tokens-1
+ * against a KV prefix of seq_len positions whose summaries were built once over
+ * all seq_len keys; per (token, kv-head group) selection over the candidate blocks
+ * of that token, then the three branches and the gated combine.
+ *   Q        [n_q_tokens][H_q][d] kv_dtype
+ *   K, V     [H_kv][seq_len][d] kv_dtype
+ *   mu, so   summaries built with batch 1, max_len = seq_len
+ *   kc, vc   pooled tokens (NULL iff cmp_len == 0)
+ *   gates    NULL or [n_q_tokens][H_q][3] f32
+ *   sel_out  NULL or [n_q_tokens][H_kv][top_k] int32 out
+ *   out      [n_q_tokens][H_q][d] f32 out
+ * Requires 0 <= q_pos0 and q_pos0 + n_q_tokens <= seq_len. */
+cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int32_t n_q_tokens,
+                                     int32_t q_pos0, const void* Q, const void* K, const void* V,
+                                     const float* mu, const float* so,
+                                     const void* kc, const void* vc, const float* gates,
+                                     int32_t* sel_out, float* out,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COBS_H_ */

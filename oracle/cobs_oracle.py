@@ -205,7 +205,7 @@ def dense_attention(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: fl
     return softmax_attend(q, keys, vals, scale)
 
 
-def _one_query(p: dict, qg: np.ndarray, keys: np.ndarray, vals: np.ndarray, L: int, t: int,
+def query_group(p: dict, qg: np.ndarray, keys: np.ndarray, vals: np.ndarray, L: int, t: int,
                summ, kc: np.ndarray, vc: np.ndarray, gates: np.ndarray | None):
     """All branches for one query position t of one GQA group.
 
@@ -287,7 +287,7 @@ def run(inputs: dict, p: dict, seqs=None, groups=None, tokens=None):
                 qg = inputs["Q"][s, i, g * G:(g + 1) * G].astype(np.float64)
                 gt = inputs["gates"][s, i, g * G:(g + 1) * G].astype(np.float64) \
                     if inputs["gates"] is not None else None
-                res[(s, g, i)] = _one_query(p, qg, keys, vals, L, t, summ, kc, vc, gt)
+                res[(s, g, i)] = query_group(p, qg, keys, vals, L, t, summ, kc, vc, gt)
     return res
 
 

@@ -1,0 +1,112 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/cobs.h, and rejects invalid calls on the host before any
+HIP call (so nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_compressed_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "cobs.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cobs_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "cobs_sparse_attn_decode" in names and len(names) >= 8
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in B._SIGNATURES, f"binding lacks {n}"
+
+
+def good():
+    return B.make_params(128, 64, 4, 16, window=512, cmp_len=32, cmp_stride=16)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, B.COBS_ERR_UNSUPPORTED),
+    ("n_kv_heads", 3, B.COBS_ERR_INVALID_ARG),
+    ("n_kv_heads", 2, B.COBS_ERR_UNSUPPORTED),       # group 32
+    ("n_q_heads", 0, B.COBS_ERR_INVALID_ARG),
+    ("top_k", 0, B.COBS_ERR_INVALID_ARG),
+    ("top_k", 65, B.COBS_ERR_INVALID_ARG),
+    ("window", -1, B.COBS_ERR_INVALID_ARG),
+    ("block_size", 128, B.COBS_ERR_UNSUPPORTED),
+    ("cmp_len", 64, B.COBS_ERR_UNSUPPORTED),
+    ("so_kind", 5, B.COBS_ERR_INVALID_ARG),
+    ("alpha", -0.5, B.COBS_ERR_INVALID_ARG),
+    ("alpha", float("nan"), B.COBS_ERR_INVALID_ARG),
+    ("scale", float("inf"), B.COBS_ERR_INVALID_ARG),
+    ("kv_dtype", 7, B.COBS_ERR_INVALID_ARG),
+])
+def test_invalid_params_rejected(field, value, status):
+    p = good()
+    setattr(p, field, value)
+    assert B.cobs_validate_params(p) == status
+    assert B.cobs_workspace_bytes(p, 1, 1024) == 0
+
+
+def test_lowrank_rank_bounds():
+    p = good()
+    p.so_kind = B.COBS_SO_LOWRANK
+    for r, st in ((0, B.COBS_ERR_INVALID_ARG), (1, B.COBS_OK), (8, B.COBS_OK), (9, B.COBS_ERR_INVALID_ARG)):
+        p.rank = r
+        assert B.cobs_validate_params(p) == st
+
+
+def test_summary_shapes():
+    p = good()
+    sh = B.cobs_summary_shapes(p, 2, 1000)
+    assert sh["nb_max"] == 16 and sh["nc_max"] == (1000 - 32) // 16 + 1
+    assert sh["mu_bytes"] == 2 * 4 * 16 * 128 * 4 == sh["so_bytes"]
+    assert sh["pooled_bytes"] == 2 * 4 * sh["nc_max"] * 128 * 2
+    p.cmp_len = 0
+    assert B.cobs_summary_shapes(p, 1, 1000)["nc_max"] == 0
+    p.cmp_len = 32
+    assert B.cobs_summary_shapes(p, 1, 20)["nc_max"] == 0
+    p.so_kind, p.rank = B.COBS_SO_LOWRANK, 4
+    assert B.cobs_summary_shapes(p, 1, 128)["so_bytes"] == 4 * 2 * 4 * 128 * 4
+
+
+def test_workspace_grows_with_problem_and_rejects_bad_sizes():
+    p = good()
+    a = B.cobs_workspace_bytes(p, 1, 32768)
+    b = B.cobs_workspace_bytes(p, 32, 32768)
+    assert 0 < a < b and a % 256 == 0
+    assert B.cobs_workspace_bytes(p, 0, 1024) == 0
+    assert B.cobs_workspace_bytes(p, 1, 0) == 0
+    assert B.cobs_workspace_bytes(p, 1, 64 * 4096 + 1) == 0
+
+
+def test_null_pointers_and_small_workspace_rejected_before_any_hip_call():
+    lib = B.lib()
+    p = good()
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
+    st = lib.cobs_sparse_attn_decode(ctypes.byref(p), 1, 1024, None, fake, fake, fake, fake, fake, fake, fake,
+                                     None, None, None, fake, fake, 1 << 30, None)
+    assert st == B.COBS_ERR_INVALID_ARG
+    st = lib.cobs_sparse_attn_decode(ctypes.byref(p), 1, 1024, fake, fake, fake, fake, fake, fake, fake, fake,
+                                     None, None, None, fake, fake, 16, None)
+    assert st == B.COBS_ERR_WORKSPACE
+    st = lib.cobs_build_summaries(ctypes.byref(p), 1, 1024, fake, fake, fake, fake, fake, None, None, None)
+    assert st == B.COBS_ERR_INVALID_ARG                   # pooled outputs missing
+    st = lib.cobs_select_topk(ctypes.byref(p), 1, 1024, fake, 2, -1, fake, fake, fake, fake, None, fake,
+                              1 << 30, None)
+    assert st == B.COBS_ERR_INVALID_ARG                   # decode takes one token
+    st = lib.cobs_sparse_attn_prefill(ctypes.byref(p), 1024, 10, 1020, fake, fake, fake, fake, fake, fake, fake,
+                                      None, None, fake, fake, 1 << 30, None)
+    assert st == B.COBS_ERR_INVALID_ARG                   # tokens run past the prefix
+
+
+def test_status_strings():
+    assert B.status_string(0) == "ok"
+    assert "workspace" in B.status_string(3)
+    assert B.status_string(99) == "unknown status"

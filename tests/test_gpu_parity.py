@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 oracle.
+
+Bars: summaries 1e-4 relative per block; pooled bf16 tokens within 1 ulp of the
+rounded oracle mean; selections exactly the oracle's except where the oracle's
+k-th / (k+1)-th score gap is below 1e-3 (then any correct top-k set passes);
+outputs max-abs 1e-2 on bf16 inputs (1e-4 on fp32 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_compressed_amd import binding as B
+from block_sparse_long_compressed_amd import synth
+from oracle import cobs_oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()          # the HIP library must be present: no fallback
+    yield
+
+
+def W(name, **kw):
+    return synth.Workload(name, **kw)
+
+
+SMALL = {
+    # several tiles and ragged tails; group 16, window not a multiple of 64
+    "g16_d128_bf16": dict(batch=3, max_len=4000, min_len=1111, n_q_heads=32, n_kv_heads=2, head_dim=128,
+                          top_k=8, window=300, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0,
+                          dtype="bf16", needles=3),
+    # fewer blocks than k for a short sequence; window longer than the sequence
+    "g4_d128_bf16_short": dict(batch=2, max_len=3000, min_len=130, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                               top_k=16, window=1000, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0,
+                               alpha=1.0, dtype="bf16", needles=2),
+    "g8_d64_bf16": dict(batch=2, max_len=2100, min_len=700, n_q_heads=16, n_kv_heads=2, head_dim=64, top_k=5,
+                        window=64, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0, dtype="bf16",
+                        needles=2),
+    "g2_d64_bf16_nocmp": dict(batch=2, max_len=900, min_len=31, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                              top_k=3, window=0, cmp_len=0, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0,
+                              dtype="bf16", needles=1),
+}
+
+
+def small(name, seed=1, lens=None):
+    w = W(name, **SMALL[name])
+    if lens is None:
+        lens = {"g16_d128_bf16": [4000, 2500, 1111], "g4_d128_bf16_short": [3000, 130],
+                "g8_d64_bf16": [2100, 700], "g2_d64_bf16_nocmp": [900, 31]}[name]
+    return w, synth.make_inputs(w, seed, lens=np.array(lens))
+
+
+def check_summaries(w, x, s):
+    p = O.params_of(w)
+    mu = s["mu"].cpu().numpy()
+    so = s["so"].cpu().numpy()
+    kc = None if s["kc"] is None else s["kc"].float().cpu().numpy()
+    vc = None if s["vc"] is None else s["vc"].float().cpu().numpy()
+    for b in range(w.batch):
+        L = int(x["lens"][b])
+        for h in range(w.n_kv_heads):
+            keys = x["K"][b, h, :L].astype(np.float64)
+            vals = x["V"][b, h, :L].astype(np.float64)
+            (rmu, rso, n), rkc, rvc = O.build_unit(p, keys, vals, L)
+            nb = len(n)
+            assert U.rel_err_rows(mu[b, h, :nb], rmu) <= 1e-4, (b, h)
+            if w.so_kind == "diag":
+                assert U.rel_err_rows(so[b, h, :nb], rso) <= 1e-4, (b, h)
+            nc = len(rkc)
+            if nc and kc is not None:
+                if w.dtype == "bf16":
+                    for got, ref in ((kc[b, h, :nc], rkc), (vc[b, h, :nc], rvc)):
+                        rr = U.bf16_round64(ref)
+                        ulp = np.maximum(np.abs(rr), 1e-38) * 2.0 ** -7
+                        assert (np.abs(got - rr) <= ulp * 1.0001).all(), (b, h)
+                else:
+                    np.testing.assert_allclose(kc[b, h, :nc], rkc, rtol=1e-5, atol=1e-6)
+                    np.testing.assert_allclose(vc[b, h, :nc], rvc, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_summaries_small(name):
+    w, x = small(name)
+    p = U.params_for(w)
+    g = U.to_device(x)
+    check_summaries(w, x, U.build(p, g))
+
+
+def test_summaries_tiny_f32():
+    w = synth.WORKLOADS["tiny_f32_L1k"]
+    x = synth.make_inputs(w, 0)
+    p = U.params_for(w)
+    check_summaries(w, x, U.build(p, U.to_device(x)))
+
+
+def run_and_check(w, x, alpha=None, out_tol=1e-2, seqs=None):
+    """Full decode on the GPU vs the oracle: selection by the gap rule, outputs
+    where the selection is unambiguous, and outputs of the attention path fed with
+    the oracle's selection everywhere."""
+    p = U.params_for(w, alpha=alpha)
+    g = U.to_device(x)
+    s = U.build(p, g)
+    out, sel = U.decode(p, g, s)
+    op = O.params_of(w, alpha=alpha)
+    seqs = range(w.batch) if seqs is None else seqs
+    ref = O.run(x, op, seqs=seqs)
+    G = w.group
+    oracle_sel = np.full_like(sel, -1)
+    for (b, h, _), (o_out, o_sel, shat, gap) in ref.items():
+        ok, msg = U.selection_ok(sel[b, h], shat, w.top_k)
+        assert ok, f"seq {b} group {h}: {msg}; gpu {sel[b, h]} oracle {o_sel} gap {gap:.3g}"
+        oracle_sel[b, h] = o_sel
+        if gap >= U.GAP:
+            np.testing.assert_array_equal(sel[b, h], o_sel)
+            err = np.abs(out[b, h * G:(h + 1) * G] - o_out).max()
+            assert err <= out_tol, f"seq {b} group {h}: max-abs {err}"
+    # attention path on the oracle's own selection (covers ambiguous-gap units too)
+    sel_in = torch.from_numpy(oracle_sel.astype(np.int32)).cuda()
+    for b in range(w.batch):
+        if b not in set(seqs):
+            sel_in[b] = torch.from_numpy(sel[b].astype(np.int32)).cuda()
+    out2, sel2 = U.decode(p, g, s, sel_in=sel_in)
+    np.testing.assert_array_equal(sel2, sel_in.cpu().numpy())
+    worst = 0.0
+    for (b, h, _), (o_out, o_sel, shat, gap) in ref.items():
+        err = np.abs(out2[b, h * G:(h + 1) * G] - o_out).max()
+        worst = max(worst, err)
+        assert err <= out_tol, f"seq {b} group {h}: max-abs {err} with the oracle's selection"
+    return worst
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0, 2.0])
+def test_decode_g16_alpha_sweep(alpha):
+    w, x = small("g16_d128_bf16")
+    run_and_check(w, x, alpha=alpha)
+
+
+@pytest.mark.parametrize("name", ["g4_d128_bf16_short", "g8_d64_bf16", "g2_d64_bf16_nocmp"])
+def test_decode_small(name):
+    w, x = small(name)
+    run_and_check(w, x)
+
+
+def test_decode_tiny_f32():
+    w = synth.WORKLOADS["tiny_f32_L1k"]
+    for seed in range(3):
+        x = synth.make_inputs(w, seed)
+        worst = run_and_check(w, x, out_tol=1e-4)
+        assert worst < 1e-4
+
+
+def test_decode_single_block_and_tiny_lengths():
+    name = "g2_d64_bf16_nocmp"
+    w = W(name, **dict(SMALL[name], window=16, max_len=70))
+    x = synth.make_inputs(w, 3, lens=np.array([1, 70]))
+    run_and_check(w, x)
+
+
+def test_exact_ties_go_to_lower_block_index():
+    name = "g2_d64_bf16_nocmp"
+    w = W(name, **dict(SMALL[name], n_q_heads=1, n_kv_heads=1, batch=1, top_k=1, max_len=640, min_len=640))
+    x = synth.make_inputs(w, 4)
+    q = x["Q"][0, 0, 0].astype(np.float64)
+    blk = x["K"][0, 0, 64 * 2: 64 * 3].copy()
+    blk[:8] = synth.round_bf16((2.5 * q / np.linalg.norm(q) * 8).astype(np.float32))  # dominant block
+    x["K"][0, 0, 64 * 2: 64 * 3] = blk
+    x["K"][0, 0, 64 * 7: 64 * 8] = blk                                                # exact duplicate
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = U.build(p, g)
+    out, sel = U.decode(p, g, s)
+    ref = O.run(x, O.params_of(w))[(0, 0, 0)]
+    assert ref[2][2] == ref[2][7] and list(ref[1]) == [2]
+    assert list(sel[0, 0]) == [2]
+
+
+def test_decode_is_deterministic():
+    w, x = small("g16_d128_bf16")
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = U.build(p, g)
+    a = U.decode(p, g, s)
+    b = U.decode(p, g, s)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_select_topk_scores_match_oracle():
+    w, x = small("g16_d128_bf16")
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = U.build(p, g)
+    nb = s["nb_max"]
+    ws = B.alloc_workspace(p, w.batch, w.max_len)
+    sel = torch.empty((w.batch, 1, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+    score = torch.empty((w.batch, 1, w.n_kv_heads, nb), dtype=torch.float32, device="cuda")
+    B.cobs_select_topk(p, g["lens"], g["Q"][:, None].contiguous(), s["mu"], s["so"], sel, ws,
+                       sel_score=score, max_len=w.max_len)
+    score = score.cpu().numpy()
+    ref = O.run(x, O.params_of(w))
+    for (b, h, _), (o_out, o_sel, shat, gap) in ref.items():
+        ncand = len(shat)
+        np.testing.assert_allclose(score[b, 0, h, :ncand], shat, rtol=0, atol=1e-4)
+        assert np.isneginf(score[b, 0, h, ncand:]).all()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the configuration the benchmark times), sampled
+# ---------------------------------------------------------------------------
+
+def test_full_size_decode_b1_L32k():
+    w = synth.WORKLOADS["decode_b1_L32k"]
+    x = synth.make_inputs(w, 1)
+    run_and_check(w, x)
+
+
+@pytest.fixture(scope="module")
+def batched_inputs():
+    w = synth.WORKLOADS["decode_b32_L16k32k"]
+    return w, synth.make_inputs(w, 2)
+
+
+@pytest.mark.parametrize("alpha", [1.0, 0.0])
+def test_full_size_batched_decode_sampled(alpha, batched_inputs):
+    w, x = batched_inputs
+    lens = x["lens"]
+    seqs = sorted({0, int(np.argmin(lens)), int(np.argmax(lens)), w.batch - 1})
+    run_and_check(w, x, alpha=alpha, seqs=seqs)
