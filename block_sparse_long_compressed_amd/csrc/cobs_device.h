@@ -79,4 +79,51 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+
+// ---------------------------------------------------------------------------
+// Hand-off between workgroups of one launch.  The XCDs of the chip have
+// separate L2 caches, so data one workgroup leaves for another is written and
+// read with the sc1 cache policy (coherent at device scope; what device-scope
+// atomic loads and stores compile to), which avoids the whole-L2 write-back and
+// invalidate of a device-scope fence.  A writer waits for its stores to be
+// acknowledged (s_waitcnt vmcnt(0)) before the workgroup bumps the counter.
+// ---------------------------------------------------------------------------
+constexpr int kCoherent = 16;   // CPol SC1
+
+struct Coherent {
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ __forceinline__ explicit Coherent(const void* base, uint32_t bytes)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000)) {}
+  __device__ __forceinline__ void st4(uint32_t byte_off, const f32x4& v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc, byte_off, 0, kCoherent);
+  }
+  __device__ __forceinline__ void st1(uint32_t byte_off, float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, byte_off, 0, kCoherent);
+  }
+  __device__ __forceinline__ f32x4 ld4(uint32_t byte_off) const {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, byte_off, 0, kCoherent));
+  }
+  __device__ __forceinline__ float ld1(uint32_t byte_off) const {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, byte_off, 0, kCoherent));
+  }
+};
+
+// All threads: wait until this thread's coherent stores are acknowledged, then
+// the workgroup synchronises and one thread increments the counter.  Returns
+// true in every thread of the workgroup that arrived last (of `expected`).
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = (prev == expected - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  return *lds_flag != 0;
+}
+
+__device__ __forceinline__ void reset_counter(uint32_t* counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace cobs

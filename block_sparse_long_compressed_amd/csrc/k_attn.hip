@@ -23,6 +23,8 @@
 #include "cobs_device.h"
 #include "cobs_launch.h"
 
+#include <algorithm>
+
 namespace cobs {
 
 struct AttnParams {
@@ -281,7 +283,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   }
   if (g == 0) { mml[(wave * 16 + n) * 2] = m_run; mml[(wave * 16 + n) * 2 + 1] = l_run; }
   __syncthreads();
-  const size_t pslot = (size_t)unit * P + blockIdx.x;
+  const Coherent po(p.part_o + (size_t)unit * P * G * D, (uint32_t)(P * G * D * 4));
+  const Coherent pm(p.part_ml + (size_t)unit * P * 32, (uint32_t)(P * 32 * 4));
   for (int idx = threadIdx.x; idx < G * (D / 4); idx += blockDim.x) {
     const int h = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
     float M = -INFINITY;
@@ -298,64 +301,60 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
         o[0] += f * src[0]; o[1] += f * src[1]; o[2] += f * src[2]; o[3] += f * src[3];
       }
     }
-    st_f32x4(p.part_o + (pslot * G + h) * D + d4, o);
-    if (d4 == 0) { p.part_ml[(pslot * 16 + h) * 2] = M; p.part_ml[(pslot * 16 + h) * 2 + 1] = Ls; }
+    po.st4((uint32_t)((((int)blockIdx.x * G + h) * D + d4) * 4), o);
+    if (d4 == 0) {
+      pm.st1((uint32_t)(((blockIdx.x * 16 + h) * 2) * 4), M);
+      pm.st1((uint32_t)(((blockIdx.x * 16 + h) * 2 + 1) * 4), Ls);
+    }
   }
 
   // ---- the last workgroup of this (sequence, kv-head) combines ------------
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t prev = atomicAdd(p.counters + unit, 1u);
-    last_flag = (prev == (uint32_t)(P - 1)) ? 1 : 0;
+  if (!arrive_last(p.counters + unit, (uint32_t)P, &last_flag)) return;
+
+  // (max, sum) of every partial into LDS with one round of loads
+  float* sm = reinterpret_cast<float*>(smem);          // [P][16][2]
+  float* fac = sm + (size_t)P * 32;                    // [P][16]: gate / L_branch * 2^(m_q - M_branch)
+  for (int i = threadIdx.x; i < P * G; i += blockDim.x) {
+    const int q = i / G, h = i % G;
+    sm[(q * 16 + h) * 2] = pm.ld1((uint32_t)(((q * 16 + h) * 2) * 4));
+    sm[(q * 16 + h) * 2 + 1] = pm.ld1((uint32_t)(((q * 16 + h) * 2 + 1) * 4));
   }
   __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-
-  const int pb[4] = {0, p.wg_slc, p.wg_slc + p.wg_win, P};
+  const int pb[4] = {0, p.wg_slc, p.wg_slc + p.wg_win, P};   // SLC, WIN, CMP partial ranges
+  for (int i = threadIdx.x; i < 3 * G; i += blockDim.x) {
+    const int br = i / G, h = i % G;
+    const int hq = head * G + h;
+    float gate = (br == 0) ? 1.f : 0.f;                 // gates absent: slc only
+    if (p.gates) gate = p.gates[((size_t)seq * p.hkv * G + hq) * 3 + (br == 0 ? 1 : br == 1 ? 2 : 0)];
+    float M = -INFINITY;
+    for (int q = pb[br]; q < pb[br + 1]; ++q)
+      if (sm[(q * 16 + h) * 2 + 1] > 0.f) M = fmaxf(M, sm[(q * 16 + h) * 2]);
+    float Ls = 0.f;
+    for (int q = pb[br]; q < pb[br + 1]; ++q) {
+      const float lq = sm[(q * 16 + h) * 2 + 1];
+      if (lq > 0.f) Ls += fast_exp2(sm[(q * 16 + h) * 2] - M) * lq;
+    }
+    for (int q = pb[br]; q < pb[br + 1]; ++q) {
+      const float lq = sm[(q * 16 + h) * 2 + 1];
+      fac[q * 16 + h] = (lq > 0.f && Ls > 0.f) ? gate * fast_exp2(sm[(q * 16 + h) * 2] - M) / Ls : 0.f;
+    }
+  }
+  __syncthreads();
   for (int idx = threadIdx.x; idx < G * (D / 4); idx += blockDim.x) {
     const int h = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    const int hq = head * G + h;
-    float gt[3] = {0.f, 1.f, 0.f};                     // (cmp, slc, win)
-    if (p.gates) {
-      const float* gp = p.gates + ((size_t)seq * p.hkv * G + hq) * 3;
-      gt[0] = gp[0]; gt[1] = gp[1]; gt[2] = gp[2];
-    }
     f32x4 res = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int br = 0; br < 3; ++br) {
-      const float gate = (br == 0) ? gt[1] : (br == 1) ? gt[2] : gt[0];
-      float M = -INFINITY, Ls = 0.f;
-      f32x4 o = {0.f, 0.f, 0.f, 0.f};
-      for (int q = pb[br]; q < pb[br + 1]; ++q) {
-        const size_t s = (size_t)unit * P + q;
-        const float mq = p.part_ml[(s * 16 + h) * 2], lq = p.part_ml[(s * 16 + h) * 2 + 1];
-        if (mq == -INFINITY || lq == 0.f) continue;
-        const f32x4 oq = ld_f32x4(p.part_o + (s * G + h) * D + d4);
-        if (mq > M) {
-          const float f = fast_exp2(M - mq);
-          Ls = Ls * f + lq;
-          o = o * f + oq;
-          M = mq;
-        } else {
-          const float f = fast_exp2(mq - M);
-          Ls += f * lq;
-          o += f * oq;
-        }
-      }
-      if (Ls > 0.f) res += (gate / Ls) * o;
-    }
-    st_f32x4(p.out + ((size_t)seq * p.hkv * G + hq) * D + d4, res);
+#pragma unroll 8
+    for (int q = 0; q < P; ++q) res += fac[q * 16 + h] * po.ld4((uint32_t)(((q * G + h) * D + d4) * 4));
+    st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h) * D + d4, res);
   }
-  if (threadIdx.x == 0) p.counters[unit] = 0u;
+  if (threadIdx.x == 0) reset_counter(p.counters + unit);
 }
 
 template <typename E, int D>
 static hipError_t launch_attn_t(const AttnArgs& a, const AttnParams& ap) {
   const int P = a.wg_slc + a.wg_win + a.wg_cmp;
   dim3 grid(P, a.hkv, a.batch);
-  const size_t lds = attn_lds_bytes<E, D>(a.waves_per_wg);
+  const size_t lds = std::max(attn_lds_bytes<E, D>(a.waves_per_wg), (size_t)P * 48 * sizeof(float));
   hipLaunchKernelGGL((k_attn_decode<E, D>), grid, dim3(64 * a.waves_per_wg), lds, a.stream, ap);
   return hipGetLastError();
 }

@@ -23,6 +23,7 @@ namespace cobs {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelMaxPerThread = 16;           // up to 4096 blocks per sequence
+constexpr int kSelMaxSplits = 64;              // scoring workgroups per (sequence, kv-head)
 
 struct SelParams {
   int tokens, hkv, group, max_len, nb_max, nb_pad, top_k, rank, q_pos0, splits, tiles_per_wave;
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   __shared__ int scan_w[4];
   __shared__ int bcast[4];
   __shared__ float lse_sh[16];
+  __shared__ float red_part[kSelMaxSplits * 32];
 
   // ---- phase 1: scores of this workgroup's tiles -------------------------
   // B operand (weights): lane (head n, k-group g) holds, for slice u and
@@ -121,6 +123,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   }
   const bool use_quad = p.alpha != 0.f;
   float run_m = -INFINITY, run_s = 0.f;      // LSE partial of head n over this lane's blocks
+  const Coherent sc(p.scores + (size_t)unit * 16 * p.nb_pad, (uint32_t)(16 * p.nb_pad * 4));
+  const Coherent lp(p.lse_part + (size_t)unit * p.splits * 32, (uint32_t)(p.splits * 32 * 4));
   const size_t sum_base = (size_t)(seq * p.hkv + head) * p.nb_max;
   const int tiles_total = (ncand + 15) / 16;
   for (int j = 0; j < p.tiles_per_wave; ++j) {
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
         run_m = mx;
       }
     }
-    if (n < G) st_f32x4(p.scores + ((size_t)unit * 16 + n) * p.nb_pad + tile * 16 + 4 * g, s);
+    if (n < G) sc.st4((uint32_t)((n * p.nb_pad + tile * 16 + 4 * g) * 4), s);
   }
   // combine the LSE partial over the four lane groups, then over the waves
 #pragma unroll
@@ -205,28 +209,25 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
       const float mx = fmaxf(M, om);
       if (mx != -INFINITY) { S = S * __expf(M - mx) + os * __expf(om - mx); M = mx; }
     }
-    float* dst = p.lse_part + (((size_t)unit * p.splits + blockIdx.x) * 16 + threadIdx.x) * 2;
-    dst[0] = M;
-    dst[1] = S;
+    const uint32_t o = (uint32_t)(((blockIdx.x * 16) + threadIdx.x) * 2 * 4);
+    lp.st1(o, M);
+    lp.st1(o + 4, S);
   }
 
   // ---- hand-off: the last workgroup of this unit selects -----------------
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const uint32_t prev = atomicAdd(p.counters + unit, 1u);
-    bcast[0] = (prev == (uint32_t)(p.splits - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!bcast[0]) return;
-  __threadfence();
+  if (!arrive_last(p.counters + unit, (uint32_t)p.splits, &bcast[0])) return;
 
   // ---- phase 2: LSE per head, group scores, radix select ------------------
+  // every partial (max, sum) is fetched at once, then reduced from LDS
+  for (int i = threadIdx.x; i < p.splits * 16; i += kSelThreads) {
+    red_part[2 * i] = lp.ld1((uint32_t)(i * 8));
+    red_part[2 * i + 1] = lp.ld1((uint32_t)(i * 8 + 4));
+  }
+  __syncthreads();
   if (threadIdx.x < 16) {
     float M = -INFINITY, S = 0.f;
     for (int x = 0; x < p.splits; ++x) {
-      const float* src = p.lse_part + (((size_t)unit * p.splits + x) * 16 + threadIdx.x) * 2;
-      const float om = src[0], os = src[1];
+      const float om = red_part[2 * (x * 16 + threadIdx.x)], os = red_part[2 * (x * 16 + threadIdx.x) + 1];
       const float mx = fmaxf(M, om);
       if (mx != -INFINITY) { S = S * __expf(M - mx) + os * __expf(om - mx); M = mx; }
     }
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
       float M = -INFINITY;
 #pragma unroll
       for (int h = 0; h < 16; ++h) {
-        v[h] = (h < G) ? p.scores[((size_t)unit * 16 + h) * p.nb_pad + b] - lse_sh[h] : -INFINITY;
+        v[h] = (h < G) ? sc.ld1((uint32_t)((h * p.nb_pad + b) * 4)) - lse_sh[h] : -INFINITY;
         M = fmaxf(M, v[h]);
       }
       float S = 0.f;
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
       if (e < per && b < p.nb_max) ss[b] = shat[e];
     }
   }
-  if (threadIdx.x == 0) p.counters[unit] = 0u;     // leave the counter zero for the next call
+  if (threadIdx.x == 0) reset_counter(p.counters + unit);   // zero for the next call
 }
 
 template <typename E, int D>
