@@ -80,6 +80,18 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 }
 
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Hand-off between workgroups of one launch.  The XCDs of the chip have
 // separate L2 caches, so data one workgroup leaves for another is written and

@@ -321,31 +321,66 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {
   }
   __syncthreads();
   const int pb[4] = {0, p.wg_slc, p.wg_slc + p.wg_win, P};   // SLC, WIN, CMP partial ranges
+  // merge factor of partial q for head h: gate / L_branch * 2^(m_q - M_branch)
   for (int i = threadIdx.x; i < 3 * G; i += blockDim.x) {
     const int br = i / G, h = i % G;
     const int hq = head * G + h;
     float gate = (br == 0) ? 1.f : 0.f;                 // gates absent: slc only
     if (p.gates) gate = p.gates[((size_t)seq * p.hkv * G + hq) * 3 + (br == 0 ? 1 : br == 1 ? 2 : 0)];
-    float M = -INFINITY;
-    for (int q = pb[br]; q < pb[br + 1]; ++q)
-      if (sm[(q * 16 + h) * 2 + 1] > 0.f) M = fmaxf(M, sm[(q * 16 + h) * 2]);
-    float Ls = 0.f;
-    for (int q = pb[br]; q < pb[br + 1]; ++q) {
-      const float lq = sm[(q * 16 + h) * 2 + 1];
-      if (lq > 0.f) Ls += fast_exp2(sm[(q * 16 + h) * 2] - M) * lq;
+    const int q0 = pb[br], q1 = pb[br + 1];
+    float M = -INFINITY, Ls = 0.f;
+    for (int c0 = q0; c0 < q1; c0 += 16) {            // all reads of a chunk in flight together
+      float mv[16], lv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool ok = c0 + j < q1;
+        mv[j] = ok ? sm[((c0 + j) * 16 + h) * 2] : -INFINITY;
+        lv[j] = ok ? sm[((c0 + j) * 16 + h) * 2 + 1] : 0.f;
+      }
+      float Mc = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) if (lv[j] > 0.f) Mc = fmaxf(Mc, mv[j]);
+      if (Mc == -INFINITY) continue;
+      const float Mn = fmaxf(M, Mc);
+      Ls = (M == -INFINITY) ? 0.f : Ls * fast_exp2(M - Mn);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) if (lv[j] > 0.f) Ls += fast_exp2(mv[j] - Mn) * lv[j];
+      M = Mn;
     }
-    for (int q = pb[br]; q < pb[br + 1]; ++q) {
+    const float inv = (Ls > 0.f) ? gate / Ls : 0.f;
+    for (int q = q0; q < q1; ++q) {
       const float lq = sm[(q * 16 + h) * 2 + 1];
-      fac[q * 16 + h] = (lq > 0.f && Ls > 0.f) ? gate * fast_exp2(sm[(q * 16 + h) * 2] - M) / Ls : 0.f;
+      fac[q * 16 + h] = (lq > 0.f) ? inv * fast_exp2(sm[(q * 16 + h) * 2] - M) : 0.f;
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += blockDim.x) {
-    const int h = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    f32x4 res = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int q = 0; q < P; ++q) res += fac[q * 16 + h] * po.ld4((uint32_t)(((q * G + h) * D + d4) * 4));
-    st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h) * D + d4, res);
+  // out[h][d] = sum_q fac[q][h] O_q[h][d]; two output float4 per thread, partials in
+  // chunks of 16 so that up to 32 coherent loads are in flight at once
+  const int items = G * (D / 4);
+  for (int i0 = threadIdx.x; i0 < items; i0 += 2 * blockDim.x) {
+    const int i1 = i0 + blockDim.x;
+    const bool has1 = i1 < items;
+    const int h0 = i0 / (D / 4), d0 = (i0 % (D / 4)) * 4;
+    const int h1 = has1 ? i1 / (D / 4) : h0, d1 = has1 ? (i1 % (D / 4)) * 4 : d0;
+    f32x4 r0 = {0.f, 0.f, 0.f, 0.f}, r1 = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < P; c0 += 16) {
+      f32x4 o0[16], o1[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int q = min(c0 + j, P - 1);
+        o0[j] = po.ld4((uint32_t)(((q * G + h0) * D + d0) * 4));
+        o1[j] = po.ld4((uint32_t)(((q * G + h1) * D + d1) * 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (c0 + j < P) {
+          r0 += fac[(c0 + j) * 16 + h0] * o0[j];
+          r1 += fac[(c0 + j) * 16 + h1] * o1[j];
+        }
+      }
+    }
+    st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h0) * D + d0, r0);
+    if (has1) st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h1) * D + d1, r1);
   }
   if (threadIdx.x == 0) reset_counter(p.counters + unit);
 }

@@ -16,6 +16,7 @@
 // Phase 2 (the last workgroup of a (sequence, kv-head), found with an atomic
 // counter): per-head LSE, group scores, an MSB-first 8-bit radix select of the
 // k-th largest key in LDS, and an ordered compaction into ascending block order.
+// Phase 2 is latency-bound, so each of its global reads is a single round.
 #include "cobs_device.h"
 #include "cobs_launch.h"
 
@@ -34,7 +35,7 @@ struct SelParams {
   int32_t* sel;
   float* sel_score;
   uint32_t* counters;
-  float* scores;
+  float* scores;                               // [unit][nb_pad][16] block-major
   float* lse_part;
 };
 
@@ -47,12 +48,7 @@ __device__ __forceinline__ int candidate_blocks(int L, int t) {
 // Exclusive prefix sum over the 256 threads of a workgroup, in thread order.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_inclusive_sum(v);
   if (lane == 63) lds_w[w] = x;
   __syncthreads();
   int base = 0, tot = 0;
@@ -65,6 +61,23 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int* tota
   __syncthreads();
   *total = tot;
   return base + x - v;
+}
+
+// Adds 1 to hist[digit] for every active lane; lanes of the wave that share a
+// digit are combined first (a few rounds), the rest use plain LDS atomics.
+__device__ __forceinline__ void wave_histogram_add(uint32_t* hist, bool active, uint32_t digit) {
+  uint64_t todo = __ballot(active);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    if (!todo) break;
+    const int leader = __builtin_ctzll(todo);
+    const uint32_t dl = __shfl(digit, leader, 64);
+    const uint64_t same = __ballot(active && digit == dl) & todo;
+    if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(same));
+    todo &= ~same;
+  }
+  if ((todo >> lane) & 1ull) atomicAdd(&hist[digit], 1u);
 }
 
 template <typename E>
@@ -81,8 +94,9 @@ __device__ __forceinline__ void load_q4(const void* Q, size_t off, float* out4) 
   }
 }
 
-// KIND 0: diagonal channel; KIND 1: rank-R scaled eigenvectors.
-template <typename E, int D, int KIND, int R>
+// KIND 0: diagonal channel; KIND 1: rank-r scaled eigenvectors.
+// HV = number of float4 holding the group's heads (G <= 4HV).
+template <typename E, int D, int KIND, int HV>
 __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   constexpr int NU = D / 16;                    // 16-column slices of a summary row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,11 +110,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   const int G = p.group;
 
   __shared__ float red_m[4][16], red_s[4][16];
-  __shared__ uint32_t hist[256];
+  __shared__ __align__(16) uint32_t hist2[2][4][256];
   __shared__ int scan_w[4];
   __shared__ int bcast[4];
   __shared__ float lse_sh[16];
   __shared__ float red_part[kSelMaxSplits * 32];
+  extern __shared__ uint32_t s_dyn[];              // [nb_pad] keys, then [nb_pad] group scores
+  uint32_t* s_key = s_dyn;
+  float* s_shat = reinterpret_cast<float*>(s_dyn + p.nb_pad);
+
+  const Coherent sc(p.scores + (size_t)unit * 16 * p.nb_pad, (uint32_t)(16 * p.nb_pad * 4));
+  const Coherent lp(p.lse_part + (size_t)unit * p.splits * 32, (uint32_t)(p.splits * 32 * 4));
 
   // ---- phase 1: scores of this workgroup's tiles -------------------------
   // B operand (weights): lane (head n, k-group g) holds, for slice u and
@@ -123,8 +143,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   }
   const bool use_quad = p.alpha != 0.f;
   float run_m = -INFINITY, run_s = 0.f;      // LSE partial of head n over this lane's blocks
-  const Coherent sc(p.scores + (size_t)unit * 16 * p.nb_pad, (uint32_t)(16 * p.nb_pad * 4));
-  const Coherent lp(p.lse_part + (size_t)unit * p.splits * 32, (uint32_t)(p.splits * 32 * 4));
   const size_t sum_base = (size_t)(seq * p.hkv + head) * p.nb_max;
   const int tiles_total = (ncand + 15) / 16;
   for (int j = 0; j < p.tiles_per_wave; ++j) {
@@ -132,63 +150,69 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
     if (tile >= tiles_total) break;
     const int brow = min(tile * 16 + n, ncand - 1);     // A-operand row (block) of this lane
     const float* mrow = p.mu + (sum_base + brow) * D;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 m4[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) m4[u] = ld_f32x4(mrow + 16 * u + 4 * g);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KIND == 0) {
-      const float* vrow = p.so + (sum_base + brow) * D;
+      f32x4 v4[NU];
+      if (use_quad) {
+        const float* vrow = p.so + (sum_base + brow) * D;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) v4[u] = ld_f32x4(vrow + 16 * u + 4 * g);
+      }
+      // two independent accumulation chains (linear and quadratic terms)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const f32x4 m4 = ld_f32x4(mrow + 16 * u + 4 * g);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(m4[c], wlin[u][c], acc);
-      }
-      if (use_quad) {
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const f32x4 v4 = ld_f32x4(vrow + 16 * u + 4 * g);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(v4[c], wquad[u][c], acc);
+        for (int c = 0; c < 4; ++c) {
+          acc = mfma_f32_16x16x4(m4[u][c], wlin[u][c], acc);
+          if (use_quad) acc2 = mfma_f32_16x16x4(v4[u][c], wquad[u][c], acc2);
         }
       }
     } else {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const f32x4 m4 = ld_f32x4(mrow + 16 * u + 4 * g);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(m4[c], wlin[u][c], acc);
+        for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(m4[u][c], wlin[u][c], acc);
       }
       if (use_quad) {
-        const float* vbase = p.so + (sum_base + brow) * (size_t)(R * D);
-        f32x4 quad = {0.f, 0.f, 0.f, 0.f};
+        const float* vbase = p.so + (sum_base + brow) * (size_t)(p.rank * D);
+#pragma unroll 1
+        for (int r = 0; r < p.rank; ++r) {
+          f32x4 v4[NU];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+          for (int u = 0; u < NU; ++u) v4[u] = ld_f32x4(vbase + r * D + 16 * u + 4 * g);
+          f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            const f32x4 v4 = ld_f32x4(vbase + r * D + 16 * u + 4 * g);
+          for (int u = 0; u < NU; u += 2) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) pr = mfma_f32_16x16x4(v4[c], wlin[u][c], pr);
+            for (int c = 0; c < 4; ++c) {
+              pr = mfma_f32_16x16x4(v4[u][c], wlin[u][c], pr);
+              pr2 = mfma_f32_16x16x4(v4[u + 1][c], wlin[u + 1][c], pr2);
+            }
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) quad[i] += pr[i] * pr[i];
+          for (int i = 0; i < 4; ++i) {
+            const float dd = pr[i] + pr2[i];
+            acc2[i] += 0.5f * p.alpha * dd * dd;
+          }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += 0.5f * p.alpha * quad[i];
       }
     }
-    // acc[i]: score partial of block tile*16 + 4g + i for head n
-    f32x4 s;
+    // acc[i] + acc2[i]: score of block tile*16 + 4g + i for head n
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = tile * 16 + 4 * g + i;
       const int nbk = min(kBlock, L - b * kBlock);
-      s[i] = (b < ncand) ? acc[i] + __logf((float)nbk) : -INFINITY;
-      const float mx = fmaxf(run_m, s[i]);
+      const float s = (b < ncand) ? acc[i] + acc2[i] + __logf((float)nbk) : -INFINITY;
+      const float mx = fmaxf(run_m, s);
       if (mx != -INFINITY) {
-        run_s = run_s * __expf(run_m - mx) + __expf(s[i] - mx);
+        run_s = run_s * __expf(run_m - mx) + __expf(s - mx);
         run_m = mx;
       }
+      if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), s);
     }
-    if (n < G) sc.st4((uint32_t)((n * p.nb_pad + tile * 16 + 4 * g) * 4), s);
   }
   // combine the LSE partial over the four lane groups, then over the waves
 #pragma unroll
@@ -217,8 +241,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   // ---- hand-off: the last workgroup of this unit selects -----------------
   if (!arrive_last(p.counters + unit, (uint32_t)p.splits, &bcast[0])) return;
 
-  // ---- phase 2: LSE per head, group scores, radix select ------------------
-  // every partial (max, sum) is fetched at once, then reduced from LDS
+  // ---- phase 2: LSE per head ------------------------------------------------
   for (int i = threadIdx.x; i < p.splits * 16; i += kSelThreads) {
     red_part[2 * i] = lp.ld1((uint32_t)(i * 8));
     red_part[2 * i + 1] = lp.ld1((uint32_t)(i * 8 + 4));
@@ -235,122 +258,144 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   }
   __syncthreads();
 
+  // ---- group scores: thread owns blocks [tid*per, tid*per + per) ------------
+  // Keys and scores live in LDS (s_key, s_shat) so the loops below stay compact.
   const int per = (p.nb_max + kSelThreads - 1) / kSelThreads;   // <= kSelMaxPerThread
-  uint32_t key[kSelMaxPerThread];
-  float shat[kSelMaxPerThread];
+  const int b0 = threadIdx.x * per;
+  constexpr int kRound = 8 / HV;                                 // blocks per load round (8 float4)
+  float lse_r[4 * HV];
 #pragma unroll
-  for (int e = 0; e < kSelMaxPerThread; ++e) {
-    key[e] = 0u;
-    shat[e] = -INFINITY;
-    const int b = threadIdx.x * per + e;
-    if (e < per && b < ncand) {
-      float v[16];
-      float M = -INFINITY;
+  for (int h = 0; h < 4 * HV; ++h) lse_r[h] = (h < G) ? lse_sh[h] : 0.f;
+#pragma unroll 1
+  for (int e0 = 0; e0 < per; e0 += kRound) {
+    f32x4 raw[kRound][HV];
 #pragma unroll
-      for (int h = 0; h < 16; ++h) {
-        v[h] = (h < G) ? sc.ld1((uint32_t)((h * p.nb_pad + b) * 4)) - lse_sh[h] : -INFINITY;
-        M = fmaxf(M, v[h]);
+    for (int e = 0; e < kRound; ++e) {
+      const int b = b0 + e0 + e;
+      const bool ok = e0 + e < per && b < ncand;
+#pragma unroll
+      for (int v = 0; v < HV; ++v)
+        raw[e][v] = ok ? sc.ld4((uint32_t)((b * 16 + 4 * v) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int e = 0; e < kRound; ++e) {
+      const int b = b0 + e0 + e;
+      if (e0 + e < per && b < ncand) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 4 * HV; ++h)
+          if (h < G) M = fmaxf(M, raw[e][h >> 2][h & 3] - lse_r[h]);
+        float S = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4 * HV; ++h)
+          if (h < G) S += __expf(raw[e][h >> 2][h & 3] - lse_r[h] - M);
+        const float sh = M + __logf(S);
+        s_shat[b] = sh;
+        s_key[b] = orderable(sh);
       }
-      float S = 0.f;
-#pragma unroll
-      for (int h = 0; h < 16; ++h) S += (h < G) ? __expf(v[h] - M) : 0.f;
-      shat[e] = M + __logf(S);
-      key[e] = orderable(shat[e]);
     }
   }
+
+  __syncthreads();                                 // s_key / s_shat complete
+  if (p.sel_score) {
+    float* ss = p.sel_score + (size_t)unit * p.nb_max;
+    for (int b = threadIdx.x; b < p.nb_max; b += kSelThreads) ss[b] = (b < ncand) ? s_shat[b] : -INFINITY;
+  }
+
+  // ---- radix select of the k-th largest key --------------------------------
+  // Each wave fills a private 256-bin histogram (double-buffered across passes);
+  // after one barrier every wave sums the four and finds the digit itself.
+  const int e_end = max(0, min(per, ncand - b0));   // this thread's candidates [b0, b0 + e_end)
   const int kk = min(p.top_k, ncand);
   uint32_t prefix = 0u, hi_mask = 0u;
   int need = kk;                                  // how many still to take at or below the prefix
+  int eq_bin = 0;                                 // keys equal to the k-th largest
+#pragma unroll 1
   for (int pass = 0; pass < 4 && kk > 0; ++pass) {
     const int shift = 24 - 8 * pass;
-    hist[threadIdx.x] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kSelMaxPerThread; ++e) {
-      const int b = threadIdx.x * per + e;
-      if (e < per && b < ncand && (key[e] & hi_mask) == prefix)
-        atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+    uint32_t* mine = hist2[pass & 1][wave];
+    *reinterpret_cast<u32x4*>(&mine[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll 1
+    for (int e = 0; e < per; ++e) {               // uniform trip count: wave-wide ballots inside
+      const uint32_t key = (e < e_end) ? s_key[b0 + e] : 0u;
+      wave_histogram_add(mine, e < e_end && (key & hi_mask) == prefix, (key >> shift) & 255u);
     }
     __syncthreads();
-    if (wave == 0) {
-      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-      const int tot = (int)(h0 + h1 + h2 + h3);
-      int incl = tot;                             // sum over lanes >= this lane
+    u32x4 hb = *reinterpret_cast<const u32x4*>(&hist2[pass & 1][0][4 * lane]);
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(incl, off, 64);
-        if (lane + off < 64) incl += y;
-      }
-      int above = incl - tot;                     // elements in higher bins than this lane's
-      const uint32_t hs[4] = {h0, h1, h2, h3};
+    for (int w = 1; w < 4; ++w) hb += *reinterpret_cast<const u32x4*>(&hist2[pass & 1][w][4 * lane]);
+    const int tot = (int)(hb[0] + hb[1] + hb[2] + hb[3]);
+    const int incl = wave_inclusive_sum(tot);
+    const int all = __builtin_amdgcn_readlane(incl, 63);
+    int above = all - incl;                        // keys in bins above this lane's four
+    int dig = 0, nn = 0, eb = 0;
+    bool found = false;
 #pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < need && need <= above + (int)hs[j]) {
-          bcast[1] = 4 * lane + j;
-          bcast[2] = need - above;
-        }
-        above += (int)hs[j];
-      }
+    for (int j = 3; j >= 0; --j) {
+      const int h = (int)hb[j];
+      if (!found && above < need && need <= above + h) { found = true; dig = 4 * lane + j; nn = need - above; eb = h; }
+      above += h;
     }
-    __syncthreads();
-    prefix |= (uint32_t)bcast[1] << shift;
+    const int src = __builtin_ctzll(__ballot(found));
+    prefix |= (uint32_t)__builtin_amdgcn_readlane(dig, src) << shift;
+    need = __builtin_amdgcn_readlane(nn, src);
+    eq_bin = __builtin_amdgcn_readlane(eb, src);
     hi_mask |= 255u << shift;
-    need = bcast[2];
-    __syncthreads();
   }
-  // `prefix` is the k-th largest key; `need` keys equal to it are taken, lowest index first
-  int eq_count = 0;
-#pragma unroll
-  for (int e = 0; e < kSelMaxPerThread; ++e) {
-    const int b = threadIdx.x * per + e;
-    eq_count += (e < per && b < ncand && kk > 0 && key[e] == prefix) ? 1 : 0;
+  // `prefix` is the k-th largest key; `need` of the `eq_bin` keys equal to it are
+  // taken, lowest block index first
+  int eq_rank = 0;
+  if (kk > 0 && need < eq_bin) {                  // a tie straddles the cut: rank the equal keys
+    int eq_count = 0;
+#pragma unroll 1
+    for (int e = 0; e < e_end; ++e) eq_count += (s_key[b0 + e] == prefix) ? 1 : 0;
+    int eq_total;
+    eq_rank = block_exclusive_scan(eq_count, scan_w, &eq_total);
   }
-  int eq_total;
-  int eq_rank = block_exclusive_scan(eq_count, scan_w, &eq_total);
-  bool take[kSelMaxPerThread];
   int take_count = 0;
-#pragma unroll
-  for (int e = 0; e < kSelMaxPerThread; ++e) {
-    const int b = threadIdx.x * per + e;
-    const bool valid = e < per && b < ncand && kk > 0;
-    bool tk = valid && key[e] > prefix;
-    if (valid && key[e] == prefix) { tk = eq_rank < need; ++eq_rank; }
-    take[e] = tk;
-    take_count += tk ? 1 : 0;
+  if (kk > 0) {
+    int r = eq_rank;
+#pragma unroll 1
+    for (int e = 0; e < e_end; ++e) {
+      const uint32_t key = s_key[b0 + e];
+      if (key > prefix) ++take_count;
+      else if (key == prefix) { take_count += (r < need) ? 1 : 0; ++r; }
+    }
   }
   int sel_total;
   int pos = block_exclusive_scan(take_count, scan_w, &sel_total);
   int32_t* sel_u = p.sel + (size_t)unit * p.top_k;
-#pragma unroll
-  for (int e = 0; e < kSelMaxPerThread; ++e) {
-    if (take[e]) sel_u[pos++] = threadIdx.x * per + e;
-  }
-  for (int i = sel_total + (int)threadIdx.x; i < p.top_k; i += kSelThreads) sel_u[i] = -1;
-  if (p.sel_score) {
-    float* ss = p.sel_score + (size_t)unit * p.nb_max;
-#pragma unroll
-    for (int e = 0; e < kSelMaxPerThread; ++e) {
-      const int b = threadIdx.x * per + e;
-      if (e < per && b < p.nb_max) ss[b] = shat[e];
+  if (kk > 0) {
+    int r = eq_rank;
+#pragma unroll 1
+    for (int e = 0; e < e_end; ++e) {
+      const uint32_t key = s_key[b0 + e];
+      bool tk = key > prefix;
+      if (key == prefix) { tk = r < need; ++r; }
+      if (tk) sel_u[pos++] = b0 + e;
     }
   }
+  for (int i = sel_total + (int)threadIdx.x; i < p.top_k; i += kSelThreads) sel_u[i] = -1;
   if (threadIdx.x == 0) reset_counter(p.counters + unit);   // zero for the next call
+}
+
+template <typename E, int D, int KIND>
+static hipError_t launch_sel_hv(const SelectArgs& a, const SelParams& sp, dim3 grid) {
+  const size_t lds = (size_t)sp.nb_pad * 8;
+  if (a.group <= 4) {
+    hipLaunchKernelGGL((k_select<E, D, KIND, 1>), grid, dim3(kSelThreads), lds, a.stream, sp);
+  } else if (a.group <= 8) {
+    hipLaunchKernelGGL((k_select<E, D, KIND, 2>), grid, dim3(kSelThreads), lds, a.stream, sp);
+  } else {
+    hipLaunchKernelGGL((k_select<E, D, KIND, 4>), grid, dim3(kSelThreads), lds, a.stream, sp);
+  }
+  return hipGetLastError();
 }
 
 template <typename E, int D>
 static hipError_t launch_sel_t(const SelectArgs& a, const SelParams& sp) {
   dim3 grid(a.splits, a.hkv, a.batch * a.tokens);
-  if (a.so_kind == 0) {
-    hipLaunchKernelGGL((k_select<E, D, 0, 1>), grid, dim3(kSelThreads), 0, a.stream, sp);
-  } else {
-    switch (a.rank) {
-#define COBS_R(r) case r: hipLaunchKernelGGL((k_select<E, D, 1, r>), grid, dim3(kSelThreads), 0, a.stream, sp); break;
-      COBS_R(1) COBS_R(2) COBS_R(3) COBS_R(4) COBS_R(5) COBS_R(6) COBS_R(7) COBS_R(8)
-#undef COBS_R
-      default: return hipErrorInvalidValue;
-    }
-  }
-  return hipGetLastError();
+  return a.so_kind == 0 ? launch_sel_hv<E, D, 0>(a, sp, grid) : launch_sel_hv<E, D, 1>(a, sp, grid);
 }
 
 hipError_t launch_select(const SelectArgs& a) {
