@@ -85,14 +85,16 @@ Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
   pl.wg_cmp = cdiv(t_cmp, per_wg);
   pl.attn_P = pl.wg_slc + pl.wg_win + pl.wg_cmp;
 
+  // with several query tokens only the selection buffer is used (prefill path)
+  const bool decode = tokens == 1;
   size_t off = 0;
   pl.off_cnt_sel = off;  off = align_up(off + sizeof(uint32_t) * pl.units_sel);
   pl.off_cnt_attn = off; off = align_up(off + sizeof(uint32_t) * pl.units_attn);
-  pl.off_scores = off;   off = align_up(off + sizeof(float) * (size_t)pl.units_sel * 16 * nb_pad);
-  pl.off_lse = off;      off = align_up(off + sizeof(float) * (size_t)pl.units_sel * pl.sel_splits * 32);
+  pl.off_scores = off;   off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_sel * 16 * nb_pad : 0));
+  pl.off_lse = off;      off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_sel * pl.sel_splits * 32 : 0));
   pl.off_sel = off;      off = align_up(off + sizeof(int32_t) * (size_t)pl.units_sel * p->top_k);
-  pl.off_ml = off;       off = align_up(off + sizeof(float) * (size_t)pl.units_attn * pl.attn_P * 32);
-  pl.off_o = off;        off = align_up(off + sizeof(float) * (size_t)pl.units_attn * pl.attn_P * G * d);
+  pl.off_ml = off;       off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_attn * pl.attn_P * 32 : 0));
+  pl.off_o = off;        off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_attn * pl.attn_P * G * d : 0));
   pl.total = off;
   return pl;
 }
@@ -166,6 +168,18 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
   return st;
 }
 
+static PrefillArgs prefill_args(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
+                                int32_t tokens, int32_t q_pos0, hipStream_t stream) {
+  PrefillArgs a;
+  a.batch = batch; a.tokens = tokens; a.hkv = p->n_kv_heads; a.group = group_of(p); a.head_dim = p->head_dim;
+  a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len); a.top_k = p->top_k;
+  a.window = p->window; a.cmp_on = (p->cmp_len > 0 && nc_of(p, max_len) > 0) ? 1 : 0; a.rank = p->rank;
+  a.so_kind = p->so_kind; a.q_pos0 = q_pos0; a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha;
+  a.scale = scale_of(p); a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr;
+  a.mu = a.so = a.gates = nullptr; a.sel = nullptr; a.sel_score = nullptr; a.out = nullptr; a.stream = stream;
+  return a;
+}
+
 static cobs_status select_impl(const cobs_params* p, const Plan& pl, int32_t batch, int32_t max_len,
                                const int32_t* seq_lens, int32_t tokens, int32_t q_pos0, const void* Q,
                                const float* mu, const float* so, int32_t* sel, float* sel_score, void* ws,
@@ -194,6 +208,11 @@ cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_le
   if (!seq_lens || !Q || !mu || !so || !sel || !ws) return COBS_ERR_INVALID_ARG;
   const Plan pl = make_plan(p, batch, max_len, n_q_tokens);
   if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
+  if (q_pos0 >= 0) {           // queries at explicit positions: one wave per (token, group)
+    PrefillArgs a = prefill_args(p, batch, max_len, seq_lens, n_q_tokens, q_pos0, (hipStream_t)stream);
+    a.Q = Q; a.mu = mu; a.so = so; a.sel = sel; a.sel_score = sel_score;
+    return hip_status(launch_prefill_select(a));
+  }
   return select_impl(p, pl, batch, max_len, seq_lens, n_q_tokens, q_pos0, Q, mu, so, sel, sel_score, ws,
                      (hipStream_t)stream);
 }
@@ -247,8 +266,16 @@ cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int3
   if ((st = check_sizes(1, seq_len, n_q_tokens)) != COBS_OK) return st;
   if (q_pos0 < 0 || (int64_t)q_pos0 + n_q_tokens > seq_len) return COBS_ERR_INVALID_ARG;
   if (!Q || !K || !V || !mu || !so || !out || !ws) return COBS_ERR_INVALID_ARG;
-  (void)kc; (void)vc; (void)gates; (void)sel_out; (void)ws_bytes; (void)stream;
-  return COBS_ERR_UNSUPPORTED;
+  const bool cmp_on = p->cmp_len > 0 && nc_of(p, seq_len) > 0;
+  if (cmp_on && (!kc || !vc)) return COBS_ERR_INVALID_ARG;
+  const Plan pl = make_plan(p, 1, seq_len, n_q_tokens);
+  if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
+  PrefillArgs a = prefill_args(p, 1, seq_len, nullptr, n_q_tokens, q_pos0, (hipStream_t)stream);
+  a.Q = Q; a.K = K; a.V = V; a.kc = kc; a.vc = vc; a.mu = mu; a.so = so; a.gates = gates; a.out = out;
+  a.sel = sel_out ? sel_out : at<int32_t>(ws, pl.off_sel);
+  cobs_status st2 = hip_status(launch_prefill_select(a));
+  if (st2 != COBS_OK) return st2;
+  return hip_status(launch_prefill_attn(a));
 }
 
 }  // extern "C"

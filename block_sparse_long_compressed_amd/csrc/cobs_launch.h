@@ -56,10 +56,27 @@ struct AttnArgs {
   hipStream_t stream;
 };
 
+// Chunked prefill (and selection for queries at explicit positions).
+struct PrefillArgs {
+  int batch, tokens, hkv, group, head_dim, max_len, nb_max, nc_max, top_k, window, cmp_on, rank, so_kind;
+  int q_pos0;                  // query i at t = q_pos0 + i
+  bool bf16;
+  float alpha, scale;
+  const int32_t* seq_lens;     // device [batch] or null (then every length is max_len)
+  const void *Q, *K, *V, *kc, *vc;
+  const float *mu, *so, *gates;
+  int32_t* sel;
+  float* sel_score;
+  float* out;
+  hipStream_t stream;
+};
+
 hipError_t launch_build_diag(const BuildArgs& a);
 hipError_t launch_build_lowrank(const BuildArgs& a);
 hipError_t launch_select(const SelectArgs& a);
 hipError_t launch_attn_decode(const AttnArgs& a);
 size_t attn_decode_lds_bytes(bool bf16, int head_dim, int waves);
+hipError_t launch_prefill_select(const PrefillArgs& a);
+hipError_t launch_prefill_attn(const PrefillArgs& a);
 
 }  // namespace cobs

@@ -22,6 +22,7 @@
 // the partials of each branch by log-sum-exp rescaling and applies the gates.
 #include "cobs_device.h"
 #include "cobs_launch.h"
+#include "attn_tile.h"
 
 #include <algorithm>
 
@@ -40,156 +41,6 @@ struct AttnParams {
   float* part_ml;
   float* part_o;
 };
-
-template <typename E, int D>
-struct AttnTiling {
-  static constexpr int kEpl = E::kPer16;                  // elements per 16-byte chunk
-  static constexpr int kChunks = D * E::kBytes / 64;      // 16-byte chunks per lane per key row
-  static constexpr int kLanesPerRow = D * E::kBytes / 16;
-  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
-  static constexpr int kLoads = kBlock / kRowsPerLoad;    // V staging loads per lane
-  static constexpr int kRowStride = D + 4;                // LDS row stride (elements), see reads
-  static constexpr int kDt = D / 16;                      // 16-wide output column tiles
-};
-
-template <typename E, int D>
-constexpr size_t attn_lds_bytes(int waves) {
-  using T = AttnTiling<E, D>;
-  const size_t stage = (size_t)waves * kBlock * T::kRowStride * E::kBytes;
-  const size_t merge = (size_t)waves * 16 * (D + 2) * sizeof(float);
-  return stage > merge ? stage : merge;
-}
-
-// One 64-key tile: rows [0, nvalid) of Kt / Vt (row stride D elements).
-template <typename E, int D>
-__device__ __forceinline__ void attend_tile(const typename E::storage* __restrict__ Kt,
-                                            const typename E::storage* __restrict__ Vt, int nvalid,
-                                            const u32x4 (&qf)[AttnTiling<E, D>::kChunks],
-                                            float scale_log2, typename E::storage* lds,
-                                            float& m_run, float& l_run,
-                                            f32x4 (&acc_o)[AttnTiling<E, D>::kDt]) {
-  using T = AttnTiling<E, D>;
-  constexpr int NCH = T::kChunks, EPL = T::kEpl, LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad;
-  constexpr int SV = T::kRowStride;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
-
-  // issue all loads of the tile: K in MFMA layout, V rows for LDS staging
-  u32x4 kf[4][NCH];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r = min(16 * t + n, nvalid - 1);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) kf[t][c] = ld16(Kt + (size_t)r * D + (4 * c + g) * EPL);
-  }
-  u32x4 vf[T::kLoads];
-  const int vc_col = (lane % LPR) * EPL, vr0 = lane / LPR;
-#pragma unroll
-  for (int i = 0; i < T::kLoads; ++i) {
-    const int r = min(RPL * i + vr0, nvalid - 1);
-    vf[i] = ld16(Vt + (size_t)r * D + vc_col);
-  }
-
-  // S = K Q^T : acc_s[t][i] = q_n . k_{16t + 4g + i}
-  f32x4 acc_s[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if constexpr (E::kBytes == 2) {
-        a = mfma_bf16_16x16x32(kf[t][c], qf[c], a);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a = mfma_f32_16x16x4(__uint_as_float(kf[t][c][e]), __uint_as_float(qf[c][e]), a);
-      }
-    }
-    acc_s[t] = a;
-  }
-
-  // stage V (row-major, padded) in this wave's LDS slice
-#pragma unroll
-  for (int i = 0; i < T::kLoads; ++i) {
-    typename E::storage* dst = lds + (RPL * i + vr0) * SV + vc_col;
-    uint2* d2 = reinterpret_cast<uint2*>(dst);
-    d2[0] = make_uint2(vf[i][0], vf[i][1]);
-    d2[1] = make_uint2(vf[i][2], vf[i][3]);
-  }
-
-  // online softmax in the log2 domain; lane owns head n
-  float mt = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 16 * t + 4 * g + i;
-      const float x = (key < nvalid) ? acc_s[t][i] * scale_log2 : -INFINITY;
-      acc_s[t][i] = x;
-      mt = fmaxf(mt, x);
-    }
-  }
-  mt = fmaxf(mt, shfl_xor_f(mt, 16));
-  mt = fmaxf(mt, shfl_xor_f(mt, 32));
-  const float m_new = fmaxf(m_run, mt);
-  const float corr = fast_exp2(m_run - m_new);     // 0 when m_run = -inf
-  float psum = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = fast_exp2(acc_s[t][i] - m_new);
-      acc_s[t][i] = pv;
-      psum += pv;
-    }
-  }
-  l_run = l_run * corr + psum;
-  m_run = m_new;
-#pragma unroll
-  for (int dt = 0; dt < T::kDt; ++dt) acc_o[dt] *= corr;
-
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): V stores visible to this wave
-  __builtin_amdgcn_wave_barrier();
-
-  // O^T += V^T P^T
-  if constexpr (E::kBytes == 2) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 pb;
-      pb[0] = f32_to_bf16_bits(acc_s[2 * s][0]) | (f32_to_bf16_bits(acc_s[2 * s][1]) << 16);
-      pb[1] = f32_to_bf16_bits(acc_s[2 * s][2]) | (f32_to_bf16_bits(acc_s[2 * s][3]) << 16);
-      pb[2] = f32_to_bf16_bits(acc_s[2 * s + 1][0]) | (f32_to_bf16_bits(acc_s[2 * s + 1][1]) << 16);
-      pb[3] = f32_to_bf16_bits(acc_s[2 * s + 1][2]) | (f32_to_bf16_bits(acc_s[2 * s + 1][3]) << 16);
-      const uint16_t* vl = reinterpret_cast<const uint16_t*>(lds);
-#pragma unroll
-      for (int dt = 0; dt < T::kDt; ++dt) {
-        const int col = 16 * dt + n;
-        u32x4 va;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kb = 32 * s + 16 * h + 4 * g;
-          const uint32_t v0 = vl[(kb + 0) * SV + col], v1 = vl[(kb + 1) * SV + col];
-          const uint32_t v2 = vl[(kb + 2) * SV + col], v3 = vl[(kb + 3) * SV + col];
-          va[2 * h] = v0 | (v1 << 16);
-          va[2 * h + 1] = v2 | (v3 << 16);
-        }
-        acc_o[dt] = mfma_bf16_16x16x32(va, pb, acc_o[dt]);
-      }
-    }
-  } else {
-    const float* vl = reinterpret_cast<const float*>(lds);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * t + 4 * g + i;
-#pragma unroll
-        for (int dt = 0; dt < T::kDt; ++dt)
-          acc_o[dt] = mfma_f32_16x16x4(vl[key * SV + 16 * dt + n], acc_s[t][i], acc_o[dt]);
-      }
-    }
-  }
-  __builtin_amdgcn_wave_barrier();      // LDS slice reused by the next tile
-}
 
 template <typename E, int D>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnParams p) {

@@ -1,0 +1,314 @@
+// Chunked causal prefill (gfx950): per-token block selection and per-token
+// three-branch attention for queries at positions t = q_pos0 .. q_pos0+T-1 of a
+// sequence whose block summaries were built once over the whole prefix.
+//
+// Selection (COBS explainer, Technisches Resuemee 2.1-2.3; skill card "Method")
+// is the decode rule applied to each token's causal candidate set (blocks whose
+// keys all lie at positions <= t).  One wave owns one (token, kv-head group):
+// pass 1 runs the fp32-MFMA block scores over the candidates and keeps an online
+// per-head log-sum-exp; pass 2 recomputes the scores, normalises each head by its
+// LSE and reduces over the group's 16 heads with lane shuffles into an LDS key per
+// block; a single-wave MSB-first radix select (DPP scans, ballots, no barriers)
+// then keeps the top-k, ties to the lower block index.
+//
+// Attention (NSA branches, Janus issue #181): one workgroup per (token, group);
+// wave 0 runs the selected blocks, wave 1 the window [t-W+1, t], waves 2-3 the
+// two halves of the visible pooled tokens, each with the shared 64-key tile
+// routine; the waves' (max, sum, O) are merged in LDS and the gated sum is
+// written directly (no workspace, no second pass).
+#include "attn_tile.h"
+#include "cobs_device.h"
+#include "cobs_launch.h"
+#include "score_common.h"
+
+#include <algorithm>
+
+namespace cobs {
+
+struct PsParams {
+  int tokens, hkv, group, max_len, nb_max, nb_pad, top_k, rank, q_pos0, L_fixed;
+  float alpha, scale;
+  const int32_t* seq_lens;          // null: every sequence has length L_fixed
+  const void* Q;
+  const float *mu, *so;
+  int32_t* sel;
+  float* sel_score;
+};
+
+template <typename E, int D, int KIND>
+__global__ __launch_bounds__(256) void k_prefill_select(PsParams p) {
+  constexpr int NU = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int tok = blockIdx.x * 4 + wave;
+  const int head = blockIdx.y, seq = blockIdx.z;
+  __shared__ __align__(16) uint32_t hist[4][256];
+  extern __shared__ uint32_t s_keys_all[];        // [4][nb_pad]
+  if (tok >= p.tokens) return;                    // waves are independent: no barriers below
+  uint32_t* s_key = s_keys_all + (size_t)wave * p.nb_pad;
+  uint32_t* h = hist[wave];
+
+  const int L = p.seq_lens ? p.seq_lens[seq] : p.L_fixed;
+  const int t = p.q_pos0 + tok;
+  const int ncand = candidate_blocks(L, t);
+  const int G = p.group;
+  const size_t unit = ((size_t)seq * p.tokens + tok) * p.hkv + head;
+  const size_t sum_base = ((size_t)seq * p.hkv + head) * p.nb_max;
+  const int tiles = (ncand + 15) / 16;
+
+  float wlin[NU][4], wquad[NU][4];
+  score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
+                            n, g, G, p.scale, p.alpha, wlin, wquad);
+  const bool use_quad = p.alpha != 0.f;
+  auto scores = [&](int tile) -> f32x4 {
+    const int brow = min(tile * 16 + n, ncand - 1);
+    f32x4 s = score_tile<D, KIND>(p.mu + (sum_base + brow) * D,
+                                  KIND == 0 ? p.so + (sum_base + brow) * D
+                                            : p.so + (sum_base + brow) * (size_t)(p.rank * D),
+                                  p.rank, g, use_quad, p.alpha, wlin, wquad);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tile * 16 + 4 * g + i;
+      s[i] = (b < ncand && n < G) ? s[i] + __logf((float)min(kBlock, L - b * kBlock)) : -INFINITY;
+    }
+    return s;
+  };
+
+  // pass 1: per-head log-sum-exp over the candidates
+  float run_m = -INFINITY, run_s = 0.f;
+#pragma unroll 1
+  for (int tile = 0; tile < tiles; ++tile) {
+    const f32x4 s = scores(tile);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mx = fmaxf(run_m, s[i]);
+      if (mx != -INFINITY) { run_s = run_s * __expf(run_m - mx) + __expf(s[i] - mx); run_m = mx; }
+    }
+  }
+#pragma unroll
+  for (int m = 16; m < 64; m <<= 1) {
+    const float om = shfl_xor_f(run_m, m), os = shfl_xor_f(run_s, m);
+    const float mx = fmaxf(run_m, om);
+    if (mx != -INFINITY) { run_s = run_s * __expf(run_m - mx) + os * __expf(om - mx); run_m = mx; }
+  }
+  const float lse = (run_m == -INFINITY) ? 0.f : run_m + __logf(run_s);
+
+  // pass 2: group score shat_b = ln sum_h exp(s_hb - LSE_h), reduced over the 16 lanes of a row
+#pragma unroll 1
+  for (int tile = 0; tile < tiles; ++tile) {
+    const f32x4 s = scores(tile);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = s[i] - lse;                 // -inf for heads >= G and non-candidates
+      float M = v;
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) M = fmaxf(M, shfl_xor_f(M, m));
+      float S = (M == -INFINITY) ? 0.f : __expf(v - M);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) S += shfl_xor_f(S, m);
+      const int b = tile * 16 + 4 * g + i;
+      if (n == 0 && b < ncand) s_key[b] = orderable(M + __logf(S));
+      if (n == 0 && b < ncand && p.sel_score) p.sel_score[unit * p.nb_max + b] = M + __logf(S);
+    }
+  }
+  if (p.sel_score) {
+    for (int b = ncand + lane; b < p.nb_max; b += 64) p.sel_score[unit * p.nb_max + b] = -INFINITY;
+  }
+
+  // single-wave radix select over s_key[0, ncand); lane owns [lb0, lb1)
+  const int per_l = (ncand + 63) / 64;
+  const int lb0 = min(lane * per_l, ncand), lb1 = min(lb0 + per_l, ncand);
+  const int kk = min(p.top_k, ncand);
+  uint32_t prefix = 0u, hi_mask = 0u;
+  int need = kk, eq_bin = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 4 && kk > 0; ++pass) {
+    const int shift = 24 - 8 * pass;
+    *reinterpret_cast<u32x4*>(&h[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll 1
+    for (int e = 0; e < per_l; ++e) {
+      const int b = lb0 + e;
+      const uint32_t key = (b < lb1) ? s_key[b] : 0u;
+      wave_histogram_add(h, b < lb1 && (key & hi_mask) == prefix, (key >> shift) & 255u);
+    }
+    const u32x4 hb = *reinterpret_cast<const u32x4*>(&h[4 * lane]);
+    prefix |= radix_digit(hb, need, eq_bin) << shift;
+    hi_mask |= 255u << shift;
+  }
+  int eq_rank = 0;
+  if (kk > 0 && need < eq_bin) {
+    int c = 0;
+#pragma unroll 1
+    for (int b = lb0; b < lb1; ++b) c += (s_key[b] == prefix) ? 1 : 0;
+    eq_rank = wave_inclusive_sum(c) - c;
+  }
+  int take = 0;
+  if (kk > 0) {
+    int r = eq_rank;
+#pragma unroll 1
+    for (int b = lb0; b < lb1; ++b) {
+      const uint32_t key = s_key[b];
+      if (key > prefix) ++take;
+      else if (key == prefix) { take += (r < need) ? 1 : 0; ++r; }
+    }
+  }
+  const int tincl = wave_inclusive_sum(take);
+  const int total = __builtin_amdgcn_readlane(tincl, 63);
+  int pos = tincl - take;
+  int32_t* sel_u = p.sel + unit * p.top_k;
+  if (kk > 0) {
+    int r = eq_rank;
+#pragma unroll 1
+    for (int b = lb0; b < lb1; ++b) {
+      const uint32_t key = s_key[b];
+      bool tk = key > prefix;
+      if (key == prefix) { tk = r < need; ++r; }
+      if (tk) sel_u[pos++] = b;
+    }
+  }
+  for (int i = total + lane; i < p.top_k; i += 64) sel_u[i] = -1;
+}
+
+struct AuParams {
+  int tokens, hkv, group, seq_len, nc_max, top_k, window, cmp_on, q_pos0;
+  float scale_log2;
+  const void *Q, *K, *V, *kc, *vc;
+  const float* gates;
+  const int32_t* sel;
+  float* out;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_attn_unit(AuParams p) {
+  using T = AttnTiling<E, D>;
+  constexpr int NCH = T::kChunks, EPL = T::kEpl, NDT = T::kDt;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int tok = blockIdx.x, head = blockIdx.y;
+  const int G = p.group, L = p.seq_len;
+  const int t = p.q_pos0 + tok;
+  const size_t unit = (size_t)tok * p.hkv + head;
+
+  u32x4 qf[NCH];
+  {
+    const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
+                                    ((size_t)tok * p.hkv * G + (size_t)head * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      qf[c] = ld16(Qh + (4 * c + g) * EPL);
+      if (n >= G) qf[c] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)head * L * D;
+  const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)head * L * D;
+  const int nc = (p.cmp_on && t >= 31) ? (t - 31) / 16 + 1 : 0;          // pooled tokens with 16j+31 <= t
+  const int win_len = p.window > 0 ? min(p.window, t + 1) : 0;
+  const int win_start = t + 1 - win_len;
+  const int ntc = (nc + kBlock - 1) / kBlock, half = (ntc + 1) / 2;
+
+  typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc_o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int count = wave == 0 ? p.top_k : wave == 1 ? (win_len + kBlock - 1) / kBlock : wave == 2 ? half : ntc - half;
+  for (int j = 0; j < count; ++j) {
+    const typename E::storage *Kt = nullptr, *Vt = nullptr;
+    int nvalid = 0;
+    if (wave == 0) {
+      const int b = p.sel[unit * p.top_k + j];
+      if (b >= 0) { nvalid = min(kBlock, L - b * kBlock); Kt = Ku + (size_t)b * kBlock * D; Vt = Vu + (size_t)b * kBlock * D; }
+    } else if (wave == 1) {
+      const int start = win_start + j * kBlock;
+      nvalid = min(kBlock, t + 1 - start);
+      Kt = Ku + (size_t)start * D; Vt = Vu + (size_t)start * D;
+    } else {
+      const int start = (j + (wave == 3 ? half : 0)) * kBlock;
+      nvalid = min(kBlock, nc - start);
+      const size_t cu = (size_t)head * p.nc_max;
+      Kt = reinterpret_cast<const typename E::storage*>(p.kc) + (cu + start) * D;
+      Vt = reinterpret_cast<const typename E::storage*>(p.vc) + (cu + start) * D;
+    }
+    if (nvalid <= 0) continue;
+    attend_tile<E, D>(Kt, Vt, nvalid, qf, p.scale_log2, lds, m_run, l_run, acc_o);
+  }
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(smem);        // [4][16][D]
+  float* mml = mo + 4 * 16 * D;                      // [4][16][2]
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mo[((size_t)wave * 16 + n) * D + 16 * dt + 4 * g + i] = acc_o[dt][i];
+  }
+  if (g == 0) { mml[(wave * 16 + n) * 2] = m_run; mml[(wave * 16 + n) * 2 + 1] = l_run; }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += blockDim.x) {
+    const int hh = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
+    const int hq = head * G + hh;
+    float gt[3] = {0.f, 1.f, 0.f};                   // (cmp, slc, win)
+    if (p.gates) {
+      const float* gp = p.gates + ((size_t)tok * p.hkv * G + hq) * 3;
+      gt[0] = gp[0]; gt[1] = gp[1]; gt[2] = gp[2];
+    }
+    auto wave_o = [&](int w) -> f32x4 { return ld_f32x4(mo + ((size_t)w * 16 + hh) * D + d4); };
+    auto wm = [&](int w) { return mml[(w * 16 + hh) * 2]; };
+    auto wl = [&](int w) { return mml[(w * 16 + hh) * 2 + 1]; };
+    f32x4 res = {0.f, 0.f, 0.f, 0.f};
+    if (wl(0) > 0.f) res += (gt[1] / wl(0)) * wave_o(0);
+    if (wl(1) > 0.f) res += (gt[2] / wl(1)) * wave_o(1);
+    const float M = fmaxf(wl(2) > 0.f ? wm(2) : -INFINITY, wl(3) > 0.f ? wm(3) : -INFINITY);
+    if (M != -INFINITY) {
+      const float f2 = wl(2) > 0.f ? fast_exp2(wm(2) - M) : 0.f, f3 = wl(3) > 0.f ? fast_exp2(wm(3) - M) : 0.f;
+      const float Ls = f2 * wl(2) + f3 * wl(3);
+      res += (gt[0] / Ls) * (f2 * wave_o(2) + f3 * wave_o(3));
+    }
+    st_f32x4(p.out + ((size_t)tok * p.hkv * G + hq) * D + d4, res);
+  }
+}
+
+template <typename E, int D, int KIND>
+static hipError_t launch_ps(const PrefillArgs& a, const PsParams& sp) {
+  dim3 grid((a.tokens + 3) / 4, a.hkv, a.batch);
+  const size_t lds = (size_t)4 * sp.nb_pad * sizeof(uint32_t);
+  hipLaunchKernelGGL((k_prefill_select<E, D, KIND>), grid, dim3(256), lds, a.stream, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_select(const PrefillArgs& a) {
+  PsParams sp;
+  sp.tokens = a.tokens; sp.hkv = a.hkv; sp.group = a.group; sp.max_len = a.max_len; sp.nb_max = a.nb_max;
+  sp.nb_pad = (a.nb_max + 15) / 16 * 16; sp.top_k = a.top_k; sp.rank = a.rank; sp.q_pos0 = a.q_pos0;
+  sp.L_fixed = a.max_len; sp.alpha = a.alpha; sp.scale = a.scale; sp.seq_lens = a.seq_lens; sp.Q = a.Q;
+  sp.mu = a.mu; sp.so = a.so; sp.sel = a.sel; sp.sel_score = a.sel_score;
+  if (a.bf16) {
+    if (a.head_dim == 128) return a.so_kind == 0 ? launch_ps<EltBF16, 128, 0>(a, sp) : launch_ps<EltBF16, 128, 1>(a, sp);
+    return a.so_kind == 0 ? launch_ps<EltBF16, 64, 0>(a, sp) : launch_ps<EltBF16, 64, 1>(a, sp);
+  }
+  if (a.head_dim == 128) return a.so_kind == 0 ? launch_ps<EltF32, 128, 0>(a, sp) : launch_ps<EltF32, 128, 1>(a, sp);
+  return a.so_kind == 0 ? launch_ps<EltF32, 64, 0>(a, sp) : launch_ps<EltF32, 64, 1>(a, sp);
+}
+
+template <typename E, int D>
+static hipError_t launch_au(const PrefillArgs& a, const AuParams& ap) {
+  dim3 grid(a.tokens, a.hkv, 1);
+  const size_t lds = std::max(attn_lds_bytes<E, D>(4), (size_t)4 * 16 * (D + 2) * sizeof(float));
+  hipLaunchKernelGGL((k_attn_unit<E, D>), grid, dim3(256), lds, a.stream, ap);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const PrefillArgs& a) {
+  AuParams ap;
+  ap.tokens = a.tokens; ap.hkv = a.hkv; ap.group = a.group; ap.seq_len = a.max_len; ap.nc_max = a.nc_max;
+  ap.top_k = a.top_k; ap.window = a.window; ap.cmp_on = a.cmp_on; ap.q_pos0 = a.q_pos0;
+  ap.scale_log2 = a.scale * kLog2e; ap.Q = a.Q; ap.K = a.K; ap.V = a.V; ap.kc = a.kc; ap.vc = a.vc;
+  ap.gates = a.gates; ap.sel = a.sel; ap.out = a.out;
+  if (a.bf16) return a.head_dim == 128 ? launch_au<EltBF16, 128>(a, ap) : launch_au<EltBF16, 64>(a, ap);
+  return a.head_dim == 128 ? launch_au<EltF32, 128>(a, ap) : launch_au<EltF32, 64>(a, ap);
+}
+
+}  // namespace cobs

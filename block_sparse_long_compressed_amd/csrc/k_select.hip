@@ -19,6 +19,7 @@
 // Phase 2 is latency-bound, so each of its global reads is a single round.
 #include "cobs_device.h"
 #include "cobs_launch.h"
+#include "score_common.h"
 
 namespace cobs {
 
@@ -39,11 +40,6 @@ struct SelParams {
   float* lse_part;
 };
 
-// Number of candidate blocks (a prefix [0, n)) for a query at position t of a
-// sequence of length L: blocks whose keys all lie at positions <= t.
-__device__ __forceinline__ int candidate_blocks(int L, int t) {
-  return (t >= L - 1) ? (L + kBlock - 1) / kBlock : (t + 1) / kBlock;
-}
 
 // Exclusive prefix sum over the 256 threads of a workgroup, in thread order.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int* total) {
@@ -63,36 +59,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int* tota
   return base + x - v;
 }
 
-// Adds 1 to hist[digit] for every active lane; lanes of the wave that share a
-// digit are combined first (a few rounds), the rest use plain LDS atomics.
-__device__ __forceinline__ void wave_histogram_add(uint32_t* hist, bool active, uint32_t digit) {
-  uint64_t todo = __ballot(active);
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    if (!todo) break;
-    const int leader = __builtin_ctzll(todo);
-    const uint32_t dl = __shfl(digit, leader, 64);
-    const uint64_t same = __ballot(active && digit == dl) & todo;
-    if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(same));
-    todo &= ~same;
-  }
-  if ((todo >> lane) & 1ull) atomicAdd(&hist[digit], 1u);
-}
-
-template <typename E>
-__device__ __forceinline__ void load_q4(const void* Q, size_t off, float* out4) {
-  if constexpr (E::kBytes == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Q) + off);
-    out4[0] = __uint_as_float(w.x << 16);
-    out4[1] = __uint_as_float(w.x & 0xFFFF0000u);
-    out4[2] = __uint_as_float(w.y << 16);
-    out4[3] = __uint_as_float(w.y & 0xFFFF0000u);
-  } else {
-    const f32x4 v = ld_f32x4(reinterpret_cast<const float*>(Q) + off);
-    out4[0] = v[0]; out4[1] = v[1]; out4[2] = v[2]; out4[3] = v[3];
-  }
-}
 
 // KIND 0: diagonal channel; KIND 1: rank-r scaled eigenvectors.
 // HV = number of float4 holding the group's heads (G <= 4HV).
@@ -126,21 +92,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
   // B operand (weights): lane (head n, k-group g) holds, for slice u and
   // component c, the weight of summary column 16u + 4g + c.
   float wlin[NU][4], wquad[NU][4];
-  {
-    const bool hv = n < G;
-    const size_t qoff = ((size_t)blockIdx.z * (size_t)(p.hkv * G) + (size_t)head * G + (hv ? n : 0)) * D;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      float q4[4];
-      load_q4<E>(p.Q, qoff + 16 * u + 4 * g, q4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float qv = hv ? q4[c] : 0.f;
-        wlin[u][c] = p.scale * qv;
-        wquad[u][c] = (KIND == 0) ? 0.5f * p.alpha * p.scale * p.scale * qv * qv : 0.f;
-      }
-    }
-  }
+  score_weights<E, D, KIND>(p.Q, ((size_t)blockIdx.z * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G,
+                            p.scale, p.alpha, wlin, wquad);
   const bool use_quad = p.alpha != 0.f;
   float run_m = -INFINITY, run_s = 0.f;      // LSE partial of head n over this lane's blocks
   const size_t sum_base = (size_t)(seq * p.hkv + head) * p.nb_max;
@@ -149,63 +102,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
     const int tile = (blockIdx.x * 4 + wave) * p.tiles_per_wave + j;
     if (tile >= tiles_total) break;
     const int brow = min(tile * 16 + n, ncand - 1);     // A-operand row (block) of this lane
-    const float* mrow = p.mu + (sum_base + brow) * D;
-    f32x4 m4[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) m4[u] = ld_f32x4(mrow + 16 * u + 4 * g);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (KIND == 0) {
-      f32x4 v4[NU];
-      if (use_quad) {
-        const float* vrow = p.so + (sum_base + brow) * D;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) v4[u] = ld_f32x4(vrow + 16 * u + 4 * g);
-      }
-      // two independent accumulation chains (linear and quadratic terms)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc = mfma_f32_16x16x4(m4[u][c], wlin[u][c], acc);
-          if (use_quad) acc2 = mfma_f32_16x16x4(v4[u][c], wquad[u][c], acc2);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(m4[u][c], wlin[u][c], acc);
-      }
-      if (use_quad) {
-        const float* vbase = p.so + (sum_base + brow) * (size_t)(p.rank * D);
-#pragma unroll 1
-        for (int r = 0; r < p.rank; ++r) {
-          f32x4 v4[NU];
-#pragma unroll
-          for (int u = 0; u < NU; ++u) v4[u] = ld_f32x4(vbase + r * D + 16 * u + 4 * g);
-          f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int u = 0; u < NU; u += 2) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              pr = mfma_f32_16x16x4(v4[u][c], wlin[u][c], pr);
-              pr2 = mfma_f32_16x16x4(v4[u + 1][c], wlin[u + 1][c], pr2);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float dd = pr[i] + pr2[i];
-            acc2[i] += 0.5f * p.alpha * dd * dd;
-          }
-        }
-      }
-    }
-    // acc[i] + acc2[i]: score of block tile*16 + 4g + i for head n
+    const f32x4 sc2 = score_tile<D, KIND>(p.mu + (sum_base + brow) * D,
+                                          KIND == 0 ? p.so + (sum_base + brow) * D
+                                                    : p.so + (sum_base + brow) * (size_t)(p.rank * D),
+                                          p.rank, g, use_quad, p.alpha, wlin, wquad);
+    // sc2[i]: score (without ln n_b) of block tile*16 + 4g + i for head n
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = tile * 16 + 4 * g + i;
       const int nbk = min(kBlock, L - b * kBlock);
-      const float s = (b < ncand) ? acc[i] + acc2[i] + __logf((float)nbk) : -INFINITY;
+      const float s = (b < ncand) ? sc2[i] + __logf((float)nbk) : -INFINITY;
       const float mx = fmaxf(run_m, s);
       if (mx != -INFINITY) {
         run_s = run_s * __expf(run_m - mx) + __expf(s - mx);
@@ -324,22 +230,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelParams p) {
     u32x4 hb = *reinterpret_cast<const u32x4*>(&hist2[pass & 1][0][4 * lane]);
 #pragma unroll
     for (int w = 1; w < 4; ++w) hb += *reinterpret_cast<const u32x4*>(&hist2[pass & 1][w][4 * lane]);
-    const int tot = (int)(hb[0] + hb[1] + hb[2] + hb[3]);
-    const int incl = wave_inclusive_sum(tot);
-    const int all = __builtin_amdgcn_readlane(incl, 63);
-    int above = all - incl;                        // keys in bins above this lane's four
-    int dig = 0, nn = 0, eb = 0;
-    bool found = false;
-#pragma unroll
-    for (int j = 3; j >= 0; --j) {
-      const int h = (int)hb[j];
-      if (!found && above < need && need <= above + h) { found = true; dig = 4 * lane + j; nn = need - above; eb = h; }
-      above += h;
-    }
-    const int src = __builtin_ctzll(__ballot(found));
-    prefix |= (uint32_t)__builtin_amdgcn_readlane(dig, src) << shift;
-    need = __builtin_amdgcn_readlane(nn, src);
-    eq_bin = __builtin_amdgcn_readlane(eb, src);
+    prefix |= radix_digit(hb, need, eq_bin) << shift;
     hi_mask |= 255u << shift;
   }
   // `prefix` is the k-th largest key; `need` of the `eq_bin` keys equal to it are

@@ -26,8 +26,12 @@ def to_device(x: dict, dev="cuda") -> dict:
          "V": torch.from_numpy(x["V"]).to(dev).to(dt).contiguous(),
          "lens": torch.from_numpy(x["lens"]).to(dev).contiguous()}
     q = torch.from_numpy(x["Q"]).to(dev).to(dt)
-    g["Q"] = q[:, 0].contiguous() if not w.prefill else q.contiguous()
-    g["gates"] = None if x["gates"] is None else torch.from_numpy(x["gates"][:, 0]).to(dev).contiguous()
+    if w.prefill:                      # one sequence: Q [T][Hq][d], gates [T][Hq][3]
+        g["Q"] = q[0].contiguous()
+        g["gates"] = None if x["gates"] is None else torch.from_numpy(x["gates"][0]).to(dev).contiguous()
+    else:                              # decode: Q [B][Hq][d], gates [B][Hq][3]
+        g["Q"] = q[:, 0].contiguous()
+        g["gates"] = None if x["gates"] is None else torch.from_numpy(x["gates"][:, 0]).to(dev).contiguous()
     return g
 
 
@@ -45,6 +49,20 @@ def decode(p, g, s, sel_in=None):
     sel = torch.full((batch, p.n_kv_heads, p.top_k), -7, dtype=torch.int32, device="cuda")
     B.cobs_sparse_attn_decode(p, g["lens"], g["Q"], g["K"], g["V"], s["mu"], s["so"], s["kc"], s["vc"],
                               g["gates"], out, ws, sel_in=sel_in, sel_out=sel)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), sel.cpu().numpy()
+
+
+def prefill(p, g, s, q_pos0):
+    T = g["Q"].shape[0]
+    K0, V0 = g["K"][0].contiguous(), g["V"][0].contiguous()
+    kc = None if s["kc"] is None else s["kc"][0].contiguous()
+    vc = None if s["vc"] is None else s["vc"][0].contiguous()
+    ws = B.alloc_workspace(p, 1, K0.shape[1], T)
+    out = torch.empty((T, p.n_q_heads, p.head_dim), dtype=torch.float32, device="cuda")
+    sel = torch.full((T, p.n_kv_heads, p.top_k), -7, dtype=torch.int32, device="cuda")
+    B.cobs_sparse_attn_prefill(p, q_pos0, g["Q"], K0, V0, s["mu"], s["so"], kc, vc, g["gates"], out, ws,
+                               sel_out=sel)
     torch.cuda.synchronize()
     return out.cpu().numpy(), sel.cpu().numpy()
 
