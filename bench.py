@@ -63,6 +63,27 @@ def algorithmic_bytes(w, lens, sel, alpha):
     return attn, sel_b
 
 
+def counter_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when there is no
+    summary for this workload or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_attn_decode_{workload.split('_', 1)[1]}_hbm_bytes.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        data = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in data.get("source_files", []):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != data.get("source_sha256"):
+        return None
+    return data.get("traffic_bytes_per_launch")
+
+
 def cpu_baseline(w, x, seconds):
     """The fp64 oracle timed on the host for a bounded sample of decode queries."""
     from threadpoolctl import threadpool_limits
@@ -108,6 +129,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--eager", action="store_true", help="launch steps directly instead of graph replays")
+    ap.add_argument("--mode", choices=["decode", "prefill", "build", "copy"], default="decode",
+                    help="decode (the metric), prefill (MFMA utilisation), build (summary GB/s), "
+                         "copy (plain copy of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
@@ -119,9 +144,15 @@ def main():
     from block_sparse_long_compressed_amd import synth
     from tests import gpu_util as U
 
+    if args.mode == "copy":
+        return bench_copy(args)
+    if args.mode == "prefill":
+        return bench_prefill(args)
+    if args.mode == "build":
+        return bench_build(args)
     w = synth.WORKLOADS[args.workload]
     if w.prefill:
-        raise SystemExit("bench.py times decode workloads")
+        raise SystemExit("use --mode prefill for prefill workloads")
     alpha = w.alpha if args.alpha is None else args.alpha
     log(f"[bench] workload {w.name} alpha {alpha}: generating inputs")
     x = synth.make_inputs(w, args.seed)
@@ -178,6 +209,10 @@ def main():
     attn_only = capture([lambda i=i: step(i, with_sel_in=True) for i in range(R)])
 
     def run_steps(n):
+        if args.eager:
+            for i in range(n):
+                step(i)
+            return
         for _ in range(n // R):
             full.replay()
         for i in range(n % R):
@@ -204,8 +239,12 @@ def main():
         attn_only.replay()
     torch.cuda.synchronize()
     ev0.record()
-    for _ in range(n_attn // R):
-        attn_only.replay()
+    for r in range(n_attn // R):
+        if args.eager:
+            for i in range(R):
+                step(i, with_sel_in=True)
+        else:
+            attn_only.replay()
     ev1.record()
     torch.cuda.synchronize()
     attn_us = ev0.elapsed_time(ev1) * 1e3 / n_attn
@@ -233,15 +272,106 @@ def main():
                    "seq_len_min": w.min_len, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "block": 64, "top_k": w.top_k, "window": w.window,
                    "cmp": [w.cmp_len, w.cmp_stride], "second_order": w.so_kind, "rank": w.rank,
-                   "alpha": alpha, "step_bytes": step_bytes, "replicas": R, "graph_replay": True},
+                   "alpha": alpha, "step_bytes": step_bytes, "replicas": R, "graph_replay": not args.eager},
         "roofline": {"bound": "hbm", "kernel": "k_attn_decode", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_launch": attn_bytes, "avg_launch_us": attn_us},
+                     "traffic": counter_traffic(w.name), "bytes_per_launch": attn_bytes,
+                     "avg_launch_us": attn_us},
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def timed(fn, n, warm=2):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3          # seconds per call
+
+
+def bench_copy(args):
+    """A plain device-to-device copy of a known size: FETCH_SIZE / WRITE_SIZE of
+    this kernel against its 2 x 256 MiB gives the counters' byte scale."""
+    import torch
+    n = 256 * 2 ** 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), max(args.steps, 5))
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "us": t * 1e6,
+                      "GBps": 2 * n / t / 1e9}), flush=True)
+
+
+def bench_build(args):
+    """Summary build (mean + second-order channel + pooled tokens): K and V are
+    streamed once; reported as GB/s of K+V read."""
+    import torch
+    from block_sparse_long_compressed_amd import binding as B
+    from block_sparse_long_compressed_amd import synth
+    from tests import gpu_util as U
+    w = synth.WORKLOADS[args.workload]
+    x = synth.make_inputs(w, args.seed)
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = B.alloc_summaries(p, w.batch, w.max_len)
+    fn = lambda: B.cobs_build_summaries(p, g["lens"], g["K"], g["V"], s["mu"], s["so"], s["kc"], s["vc"])
+    t = timed(fn, max(1, min(args.steps, 20)))
+    es = 2 if w.dtype == "bf16" else 4
+    kv = int(np.asarray(x["lens"], dtype=np.int64).sum()) * w.n_kv_heads * w.head_dim * es * 2
+    print(json.dumps({"mode": "build", "workload": w.name, "second_order": w.so_kind, "rank": w.rank,
+                      "ms": t * 1e3, "kv_bytes": kv, "GBps_streamed": kv / t / 1e9,
+                      "pct_of_hbm_peak": 100 * kv / t / 1e9 / HBM_PEAK_GBPS}), flush=True)
+
+
+def prefill_flops(w, lens, sel):
+    """Algorithmic FLOPs of a prefill chunk: 4d per (query head, key) of the union
+    of the three branches' key sets counted per branch (QK^T and PV), plus the
+    scoring contraction 2 x (d + d) per (query head, candidate block)."""
+    d, G = w.head_dim, w.group
+    L = int(lens[0])
+    total = 0
+    for i in range(w.n_q_tokens):
+        t = w.q_pos0 + i
+        ncand = L // 64 if t >= L - 1 else (t + 1) // 64
+        nwin = min(w.window, t + 1)
+        nc = (t - 31) // 16 + 1 if t >= 31 else 0
+        for h in range(w.n_kv_heads):
+            nslc = sum(min(64, L - 64 * b) for b in sel[i, h] if b >= 0)
+            total += G * 4 * d * (nslc + nwin + nc) + G * 2 * 2 * d * ncand
+    return total
+
+
+def bench_prefill(args):
+    import torch
+    from block_sparse_long_compressed_amd import binding as B
+    from block_sparse_long_compressed_amd import synth
+    from tests import gpu_util as U
+    w = synth.WORKLOADS[args.workload if args.workload.startswith("prefill") else "prefill_T8k_L32k"]
+    x = synth.make_inputs(w, args.seed)
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = U.build(p, g)
+    out, sel = U.prefill(p, g, s, w.q_pos0)
+    flops = prefill_flops(w, x["lens"], sel)
+    K0, V0 = g["K"][0].contiguous(), g["V"][0].contiguous()
+    kc, vc = s["kc"][0].contiguous(), s["vc"][0].contiguous()
+    ws = B.alloc_workspace(p, 1, w.max_len, w.n_q_tokens)
+    o = torch.empty((w.n_q_tokens, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    fn = lambda: B.cobs_sparse_attn_prefill(p, w.q_pos0, g["Q"], K0, V0, s["mu"], s["so"], kc, vc, g["gates"],
+                                            o, ws)
+    t = timed(fn, max(1, min(args.steps, 20)))
+    tflops = flops / t / 1e12
+    print(json.dumps({"mode": "prefill", "workload": w.name, "ms": t * 1e3, "tokens_per_s": w.n_q_tokens / t,
+                      "algorithmic_flop": flops, "TFLOPs": tflops,
+                      "mfma_utilisation_vs_bf16_dense": tflops / 2500.0}), flush=True)
 
 
 if __name__ == "__main__":

@@ -314,3 +314,37 @@ def test_full_size_long_decode_rank4_sampled(long_inputs):
         assert ok, f"seq {b} group {h}: {msg}"
         if gap >= U.GAP:
             assert np.abs(out[b, h * G:(h + 1) * G] - o_out).max() <= 1e-2
+
+
+def test_decode_graph_replays_match_eager():
+    """The benchmark replays captured decode steps; every replay, with eager work and
+    synchronisations in between, must reproduce the eager result exactly."""
+    w, x = small("g16_d128_bf16")
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = U.build(p, g)
+    eager_out, eager_sel = U.decode(p, g, s)
+    ws = B.alloc_workspace(p, w.batch, w.max_len)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+    step = lambda: B.cobs_sparse_attn_decode(p, g["lens"], g["Q"], g["K"], g["V"], s["mu"], s["so"], s["kc"],
+                                             s["vc"], g["gates"], out, ws, sel_out=sel)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-9)
+        scratch = torch.randn(1 << 20, device="cuda").sum()          # unrelated eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sel.cpu().numpy(), eager_sel)
+        np.testing.assert_array_equal(out.cpu().numpy(), eager_out)
+        assert torch.isfinite(scratch)
