@@ -78,7 +78,10 @@ def counter_traffic(workload):
         return None
     h = hashlib.sha256()
     for f in data.get("source_files", []):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        path_f = os.path.join(ROOT, f)
+        if not os.path.exists(path_f):
+            return None
+        h.update(open(path_f, "rb").read())
     if h.hexdigest() != data.get("source_sha256"):
         return None
     return data.get("traffic_bytes_per_launch")

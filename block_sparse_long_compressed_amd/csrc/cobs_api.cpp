@@ -59,7 +59,7 @@ struct Plan {
   int units_sel, units_attn;
   int sel_tpw, sel_splits;
   int attn_waves, attn_tpw, wg_slc, wg_win, wg_cmp, attn_P;
-  size_t off_cnt_sel, off_cnt_attn, off_scores, off_lse, off_sel, off_ml, off_o, total;
+  size_t off_cnt_sel, off_cnt_attn, off_ready, off_scores, off_lse, off_sel, off_ml, off_o, total;
 };
 
 Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
@@ -90,6 +90,7 @@ Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
   size_t off = 0;
   pl.off_cnt_sel = off;  off = align_up(off + sizeof(uint32_t) * pl.units_sel);
   pl.off_cnt_attn = off; off = align_up(off + sizeof(uint32_t) * pl.units_attn);
+  pl.off_ready = off;    off = align_up(off + sizeof(uint32_t) * (size_t)pl.units_attn * p->top_k);
   pl.off_scores = off;   off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_sel * 16 * nb_pad : 0));
   pl.off_lse = off;      off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_sel * pl.sel_splits * 32 : 0));
   pl.off_sel = off;      off = align_up(off + sizeof(int32_t) * (size_t)pl.units_sel * p->top_k);
@@ -180,21 +181,27 @@ static PrefillArgs prefill_args(const cobs_params* p, int32_t batch, int32_t max
   return a;
 }
 
-static cobs_status select_impl(const cobs_params* p, const Plan& pl, int32_t batch, int32_t max_len,
-                               const int32_t* seq_lens, int32_t tokens, int32_t q_pos0, const void* Q,
-                               const float* mu, const float* so, int32_t* sel, float* sel_score, void* ws,
-                               hipStream_t stream) {
-  SelectArgs a;
-  a.batch = batch; a.tokens = tokens; a.hkv = p->n_kv_heads; a.group = group_of(p);
-  a.head_dim = p->head_dim; a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.top_k = p->top_k;
-  a.rank = p->rank; a.so_kind = p->so_kind; a.q_pos0 = q_pos0; a.bf16 = p->kv_dtype == COBS_BF16;
-  a.alpha = p->alpha; a.scale = scale_of(p); a.splits = pl.sel_splits; a.tiles_per_wave = pl.sel_tpw;
-  a.seq_lens = seq_lens; a.Q = Q; a.mu = mu; a.so = so; a.sel = sel; a.sel_score = sel_score;
-  a.counters = at<uint32_t>(ws, pl.off_cnt_sel);
+static DecodeArgs decode_args(const cobs_params* p, const Plan& pl, int32_t batch, int32_t max_len,
+                              const int32_t* seq_lens, void* ws, hipStream_t stream) {
+  DecodeArgs a;
+  a.batch = batch; a.hkv = p->n_kv_heads; a.group = group_of(p); a.head_dim = p->head_dim;
+  a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len); a.top_k = p->top_k;
+  a.window = p->window; a.cmp_on = (p->cmp_len > 0 && nc_of(p, max_len) > 0) ? 1 : 0; a.rank = p->rank;
+  a.so_kind = p->so_kind; a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha; a.scale = scale_of(p);
+  a.do_select = a.do_attn = false;
+  a.splits = pl.sel_splits; a.sel_tpw = pl.sel_tpw;
+  a.tpw = pl.attn_tpw; a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
+  a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr; a.mu = a.so = a.gates = nullptr;
+  a.sel = nullptr; a.sel_in = nullptr; a.sel_score = nullptr; a.out = nullptr;
+  a.sel_counters = at<uint32_t>(ws, pl.off_cnt_sel);
+  a.attn_counters = at<uint32_t>(ws, pl.off_cnt_attn);
+  a.ready = at<uint32_t>(ws, pl.off_ready);
   a.scores = at<float>(ws, pl.off_scores);
   a.lse_part = at<float>(ws, pl.off_lse);
+  a.part_ml = at<float>(ws, pl.off_ml);
+  a.part_o = at<float>(ws, pl.off_o);
   a.stream = stream;
-  return hip_status(launch_select(a));
+  return a;
 }
 
 cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
@@ -213,8 +220,10 @@ cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_le
     a.Q = Q; a.mu = mu; a.so = so; a.sel = sel; a.sel_score = sel_score;
     return hip_status(launch_prefill_select(a));
   }
-  return select_impl(p, pl, batch, max_len, seq_lens, n_q_tokens, q_pos0, Q, mu, so, sel, sel_score, ws,
-                     (hipStream_t)stream);
+  DecodeArgs a = decode_args(p, pl, batch, max_len, seq_lens, ws, (hipStream_t)stream);
+  a.do_select = true;
+  a.Q = Q; a.mu = mu; a.so = so; a.sel = sel; a.sel_score = sel_score;
+  return hip_status(launch_decode(a));
 }
 
 cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
@@ -231,30 +240,18 @@ cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t
   const Plan pl = make_plan(p, batch, max_len, 1);
   if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  const int32_t* sel = sel_in;
-  if (!sel) {
-    int32_t* dst = sel_out ? sel_out : at<int32_t>(ws, pl.off_sel);
-    if ((st = select_impl(p, pl, batch, max_len, seq_lens, 1, -1, Q, mu, so, dst, nullptr, ws, s)) != COBS_OK)
-      return st;
-    sel = dst;
-  } else if (sel_out && sel_out != sel_in) {
+  if (sel_in && sel_out && sel_out != sel_in) {
     if (hipMemcpyAsync(sel_out, sel_in, sizeof(int32_t) * (size_t)batch * p->n_kv_heads * p->top_k,
                        hipMemcpyDeviceToDevice, s) != hipSuccess)
       return COBS_ERR_HIP;
   }
-  AttnArgs a;
-  a.batch = batch; a.hkv = p->n_kv_heads; a.group = group_of(p); a.head_dim = p->head_dim;
-  a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len);
-  a.top_k = p->top_k; a.window = p->window; a.cmp_on = cmp_on ? 1 : 0; a.bf16 = p->kv_dtype == COBS_BF16;
-  a.scale = scale_of(p); a.waves_per_wg = pl.attn_waves; a.tiles_per_wave = pl.attn_tpw;
-  a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
-  a.seq_lens = seq_lens; a.Q = Q; a.K = K; a.V = V; a.kc = kc; a.vc = vc; a.gates = gates; a.sel = sel;
-  a.out = out;
-  a.counters = at<uint32_t>(ws, pl.off_cnt_attn);
-  a.part_ml = at<float>(ws, pl.off_ml);
-  a.part_o = at<float>(ws, pl.off_o);
-  a.stream = s;
-  return hip_status(launch_attn_decode(a));
+  DecodeArgs a = decode_args(p, pl, batch, max_len, seq_lens, ws, s);
+  a.do_select = sel_in == nullptr;
+  a.do_attn = true;
+  a.Q = Q; a.K = K; a.V = V; a.kc = kc; a.vc = vc; a.mu = mu; a.so = so; a.gates = gates; a.out = out;
+  a.sel = sel_out ? sel_out : at<int32_t>(ws, pl.off_sel);
+  a.sel_in = sel_in;
+  return hip_status(launch_decode(a));
 }
 
 cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int32_t n_q_tokens, int32_t q_pos0,
