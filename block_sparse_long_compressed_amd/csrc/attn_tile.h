@@ -8,7 +8,9 @@
 // staged in LDS row-major (padded so the transposed reads are conflict-free) and
 // read as the A operand.  K is loaded straight into the MFMA layout.  fp32
 // inputs use v_mfma_f32_16x16x4_f32 with the same lane layout.  The softmax is
-// online, in the log2 domain.
+// online, in the log2 domain.  The steps are separate so that a caller walking
+// several tiles can issue the next tile's K loads once the scores are formed and
+// its V loads once V is staged, overlapping memory with the softmax and P V.
 #pragma once
 #include "cobs_device.h"
 
@@ -33,63 +35,89 @@ constexpr size_t attn_lds_bytes(int waves) {
   return stage > merge ? stage : merge;
 }
 
-// One 64-key tile: rows [0, nvalid) of Kt / Vt (row stride D elements).
+// Registers of one 64-key tile in flight: K in the MFMA A layout, V rows as
+// loaded (for LDS staging).
 template <typename E, int D>
-__device__ __forceinline__ void attend_tile(const typename E::storage* __restrict__ Kt,
-                                            const typename E::storage* __restrict__ Vt, int nvalid,
-                                            const u32x4 (&qf)[AttnTiling<E, D>::kChunks],
-                                            float scale_log2, typename E::storage* lds,
-                                            float& m_run, float& l_run,
-                                            f32x4 (&acc_o)[AttnTiling<E, D>::kDt]) {
+struct TileRegs {
+  u32x4 kf[4][AttnTiling<E, D>::kChunks];
+  u32x4 vf[AttnTiling<E, D>::kLoads];
+};
+
+// Issue the K loads of rows [0, nvalid) of Kt (row stride D elements; rows past
+// nvalid repeat the last valid row and are masked in the softmax).
+template <typename E, int D>
+__device__ __forceinline__ void tile_load_k(const typename E::storage* __restrict__ Kt, int nvalid,
+                                            TileRegs<E, D>& r) {
   using T = AttnTiling<E, D>;
-  constexpr int NCH = T::kChunks, EPL = T::kEpl, LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad;
-  constexpr int SV = T::kRowStride;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
-
-  // issue all loads of the tile: K in MFMA layout, V rows for LDS staging
-  u32x4 kf[4][NCH];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int r = min(16 * t + n, nvalid - 1);
+    const int row = min(16 * t + n, nvalid - 1);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kf[t][c] = ld16(Kt + (size_t)r * D + (4 * c + g) * EPL);
+    for (int c = 0; c < T::kChunks; ++c) r.kf[t][c] = ld16(Kt + (size_t)row * D + (4 * c + g) * T::kEpl);
   }
-  u32x4 vf[T::kLoads];
-  const int vc_col = (lane % LPR) * EPL, vr0 = lane / LPR;
+}
+
+template <typename E, int D>
+__device__ __forceinline__ void tile_load_v(const typename E::storage* __restrict__ Vt, int nvalid,
+                                            TileRegs<E, D>& r) {
+  using T = AttnTiling<E, D>;
+  const int lane = threadIdx.x & 63;
+  const int col = (lane % T::kLanesPerRow) * T::kEpl, r0 = lane / T::kLanesPerRow;
 #pragma unroll
   for (int i = 0; i < T::kLoads; ++i) {
-    const int r = min(RPL * i + vr0, nvalid - 1);
-    vf[i] = ld16(Vt + (size_t)r * D + vc_col);
+    const int row = min(T::kRowsPerLoad * i + r0, nvalid - 1);
+    r.vf[i] = ld16(Vt + (size_t)row * D + col);
   }
+}
 
-  // S = K Q^T : acc_s[t][i] = q_n . k_{16t + 4g + i}
-  f32x4 acc_s[4];
+// S = K Q^T : s[t][i] = q_n . k_{16t + 4g + i}
+template <typename E, int D>
+__device__ __forceinline__ void tile_scores(const TileRegs<E, D>& r, const u32x4 (&qf)[AttnTiling<E, D>::kChunks],
+                                            f32x4 (&s)[4]) {
+  constexpr int NCH = AttnTiling<E, D>::kChunks;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if constexpr (E::kBytes == 2) {
-        a = mfma_bf16_16x16x32(kf[t][c], qf[c], a);
+        a = mfma_bf16_16x16x32(r.kf[t][c], qf[c], a);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a = mfma_f32_16x16x4(__uint_as_float(kf[t][c][e]), __uint_as_float(qf[c][e]), a);
+        for (int e = 0; e < 4; ++e) a = mfma_f32_16x16x4(__uint_as_float(r.kf[t][c][e]), __uint_as_float(qf[c][e]), a);
       }
     }
-    acc_s[t] = a;
+    s[t] = a;
   }
+}
 
-  // stage V (row-major, padded) in this wave's LDS slice
+// V rows into this wave's LDS slice (row-major, padded).
+template <typename E, int D>
+__device__ __forceinline__ void tile_stage_v(const TileRegs<E, D>& r, typename E::storage* lds) {
+  using T = AttnTiling<E, D>;
+  const int lane = threadIdx.x & 63;
+  const int col = (lane % T::kLanesPerRow) * T::kEpl, r0 = lane / T::kLanesPerRow;
 #pragma unroll
   for (int i = 0; i < T::kLoads; ++i) {
-    typename E::storage* dst = lds + (RPL * i + vr0) * SV + vc_col;
+    typename E::storage* dst = lds + (T::kRowsPerLoad * i + r0) * T::kRowStride + col;
     uint2* d2 = reinterpret_cast<uint2*>(dst);
-    d2[0] = make_uint2(vf[i][0], vf[i][1]);
-    d2[1] = make_uint2(vf[i][2], vf[i][3]);
+    d2[0] = make_uint2(r.vf[i][0], r.vf[i][1]);
+    d2[1] = make_uint2(r.vf[i][2], r.vf[i][3]);
   }
+}
 
-  // online softmax in the log2 domain; lane owns head n
+// Online softmax of the tile's scores (log2 domain; lane owns head n) and
+// O^T += V^T P^T from the staged V.
+template <typename E, int D>
+__device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, float scale_log2,
+                                                const typename E::storage* lds, float& m_run, float& l_run,
+                                                f32x4 (&acc_o)[AttnTiling<E, D>::kDt]) {
+  using T = AttnTiling<E, D>;
+  constexpr int SV = T::kRowStride;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
   float mt = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -123,7 +151,6 @@ __device__ __forceinline__ void attend_tile(const typename E::storage* __restric
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): V stores visible to this wave
   __builtin_amdgcn_wave_barrier();
 
-  // O^T += V^T P^T
   if constexpr (E::kBytes == 2) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -162,6 +189,23 @@ __device__ __forceinline__ void attend_tile(const typename E::storage* __restric
     }
   }
   __builtin_amdgcn_wave_barrier();      // LDS slice reused by the next tile
+}
+
+// One whole 64-key tile: rows [0, nvalid) of Kt / Vt (row stride D elements).
+template <typename E, int D>
+__device__ __forceinline__ void attend_tile(const typename E::storage* __restrict__ Kt,
+                                            const typename E::storage* __restrict__ Vt, int nvalid,
+                                            const u32x4 (&qf)[AttnTiling<E, D>::kChunks],
+                                            float scale_log2, typename E::storage* lds,
+                                            float& m_run, float& l_run,
+                                            f32x4 (&acc_o)[AttnTiling<E, D>::kDt]) {
+  TileRegs<E, D> r;
+  tile_load_k<E, D>(Kt, nvalid, r);
+  tile_load_v<E, D>(Vt, nvalid, r);
+  f32x4 s[4];
+  tile_scores<E, D>(r, qf, s);
+  tile_stage_v<E, D>(r, lds);
+  tile_softmax_pv<E, D>(s, nvalid, scale_log2, lds, m_run, l_run, acc_o);
 }
 
 }  // namespace cobs

@@ -1,7 +1,7 @@
 // C ABI of the library: argument validation, workspace planning and launches.
 // Every check happens on the host before the first HIP call, so an invalid call
 // enqueues nothing (see include/cobs.h for the contract).
-#include "../../include/cobs.h"
+#include "cobs.h"
 
 #include <math.h>
 #include <string.h>
@@ -14,7 +14,8 @@ namespace {
 
 using namespace cobs;
 
-constexpr int kTargetWaves = 4096;      // wave-tiles that keep 256 CUs busy
+constexpr int kTargetWaves = 4096;      // attention wave-tiles that keep 256 CUs busy
+constexpr int kSelWaves = 2048;         // scoring waves (each keeps two summary tiles in flight)
 constexpr size_t kAlign = 256;
 constexpr int kMaxBlocks = 4096;        // per sequence (selection keeps <= 16 keys per thread)
 
@@ -71,7 +72,7 @@ Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
   pl.units_attn = batch * hkv;
   // scoring: 16-block tiles, 4 waves per workgroup
   const int tiles = cdiv(nb, 16);
-  pl.sel_tpw = std::min(8, std::max(1, cdiv(pl.units_sel * tiles, kTargetWaves)));
+  pl.sel_tpw = std::min(8, std::max(1, cdiv(pl.units_sel * tiles, kSelWaves)));
   pl.sel_splits = cdiv(tiles, 4 * pl.sel_tpw);
   // attention: 64-key tiles of the three branches
   const int t_slc = p->top_k;

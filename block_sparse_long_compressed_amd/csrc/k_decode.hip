@@ -41,7 +41,6 @@ namespace cobs {
 constexpr int kThreads = 256;
 constexpr int kSelMaxSplits = 64;              // scoring workgroups per (sequence, kv-head)
 constexpr uint32_t kSpinCap = 1u << 21;        // ~0.1 s of polling before a waiter gives up
-constexpr int kMaxTpw = 8;                     // tiles per wave (the host never plans more)
 
 struct DecodeParams {
   int hkv, group, max_len, nb_max, nb_pad, top_k;
@@ -115,32 +114,60 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
   const Coherent lp(p.lse_part + (size_t)unit * p.splits * 32, (uint32_t)(p.splits * 32 * 4));
 
   // ---- phase 1: scores of this workgroup's tiles -------------------------
+  // Summary rows are requested before the query so that both arrive in one
+  // round trip, and the wave keeps RING tiles in flight: each tile's slot is
+  // refilled with the tile RING ahead as soon as it is scored.  (A rank-r tile
+  // is already several times larger than a diagonal one.)
+  constexpr int RING = KIND == 0 ? 2 : 1;
+  const bool use_quad = p.alpha != 0.f;
+  const size_t sum_base = (size_t)unit * p.nb_max;
+  const size_t so_row = KIND == 0 ? (size_t)D : (size_t)p.rank * D;
+  const int tiles_total = (ncand + 15) / 16;
+  const int tile0 = (split * 4 + wave) * p.sel_tpw;
+  auto rows_of = [&](int tile, const float*& mr, const float*& vr) {
+    const int brow = min(tile * 16 + n, ncand - 1);      // A-operand row (block) of this lane
+    mr = p.mu + (sum_base + brow) * D;
+    vr = p.so + (sum_base + brow) * so_row;
+  };
+  SumTile<D, KIND> st[RING];
+  const float* vrow[RING];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) {
+    vrow[r] = nullptr;
+    if (r < p.sel_tpw && tile0 + r < tiles_total) {
+      const float* mrow;
+      rows_of(tile0 + r, mrow, vrow[r]);
+      sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+    }
+  }
   float wlin[NU][4], wquad[NU][4];
   score_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
                             p.alpha, wlin, wquad);
-  const bool use_quad = p.alpha != 0.f;
   float run_m = -INFINITY, run_s = 0.f;        // LSE partial of head n over this lane's blocks
-  const size_t sum_base = (size_t)unit * p.nb_max;
-  const int tiles_total = (ncand + 15) / 16;
-  for (int j = 0; j < p.sel_tpw; ++j) {
-    const int tile = (split * 4 + wave) * p.sel_tpw + j;
-    if (tile >= tiles_total) break;
-    const int brow = min(tile * 16 + n, ncand - 1);     // A-operand row (block) of this lane
-    const f32x4 s4 = score_tile<D, KIND>(p.mu + (sum_base + brow) * D,
-                                         KIND == 0 ? p.so + (sum_base + brow) * D
-                                                   : p.so + (sum_base + brow) * (size_t)(p.rank * D),
-                                         p.rank, g, use_quad, p.alpha, wlin, wquad);
+  for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = tile * 16 + 4 * g + i;
-      const int nbk = min(kBlock, L - b * kBlock);
-      const float s = (b < ncand) ? s4[i] + __logf((float)nbk) : -INFINITY;
-      const float mx = fmaxf(run_m, s);
-      if (mx != -INFINITY) {
-        run_s = run_s * __expf(run_m - mx) + __expf(s - mx);
-        run_m = mx;
+    for (int r = 0; r < RING; ++r) {
+      const int j = j0 + r, tile = tile0 + j0 + r;
+      if (j < p.sel_tpw && tile < tiles_total) {
+        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin, wquad);
+        if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
+          const float* mrow;
+          rows_of(tile + RING, mrow, vrow[r]);
+          sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = tile * 16 + 4 * g + i;
+          const int nbk = min(kBlock, L - b * kBlock);
+          const float s = (b < ncand) ? s4[i] + __logf((float)nbk) : -INFINITY;
+          const float mx = fmaxf(run_m, s);
+          if (mx != -INFINITY) {
+            run_s = run_s * __expf(run_m - mx) + __expf(s - mx);
+            run_m = mx;
+          }
+          if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), s);
+        }
       }
-      if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), s);
     }
   }
 #pragma unroll
@@ -319,27 +346,23 @@ __device__ void attn_role(const DecodeParams& p, int unit, int branch, int local
   const int L = p.seq_lens[seq];
   const int P = p.wg_slc + p.wg_win + p.wg_cmp;
 
-  // the group's queries as the B operand of S = K Q^T (heads >= G are zero)
-  u32x4 qf[NCH];
-  {
-    const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
-                                    ((size_t)seq * p.hkv * G + (size_t)head * G + (n < G ? n : 0)) * D;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      qf[c] = ld16(Qh + (4 * c + g) * EPL);
-      if (n >= G) qf[c] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // selected blocks: from the published codes (polled, bounded) or the caller's selection
-  int slc_blocks[kMaxTpw];
-#pragma unroll
-  for (int j = 0; j < kMaxTpw; ++j) slc_blocks[j] = -1;
-  if (branch == 0) {
-#pragma unroll
-    for (int j = 0; j < kMaxTpw; ++j) {
-      if (j >= p.tpw) break;
-      const int tile = (local * nw + wave) * p.tpw + j;
-      if (tile >= p.top_k) break;
+  const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
+  const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)unit * p.max_len * D;
+  const typename E::storage* kcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.kc) + (size_t)unit * p.nc_max * D : nullptr;
+  const typename E::storage* vcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.vc) + (size_t)unit * p.nc_max * D : nullptr;
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int nc = (p.cmp_on && L >= 32) ? (L - 32) / 16 + 1 : 0;
+  const int win_len = min(p.window, L);
+  const int win_start = L - win_len;
+
+  // Source rows of this wave's j-th tile; returns the number of valid keys (0:
+  // none).  Selected blocks come from the published codes (polled, bounded) or
+  // the caller's selection; every block index is bounds-checked.
+  auto tile_src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
+    if (j >= p.tpw) return 0;
+    const int tile = (local * nw + wave) * p.tpw + j;
+    if (branch == 0) {
+      if (tile >= p.top_k) return 0;
       int b = -1;
       if (p.wait_ready) {
         const Coherent pc(p.pub + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
@@ -354,18 +377,24 @@ __device__ void attn_role(const DecodeParams& p, int unit, int branch, int local
         const Coherent si(p.sel_attn + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
         b = __float_as_int(si.ld1((uint32_t)(tile * 4)));
       }
-      slc_blocks[j] = b;
+      if (b < 0 || b >= nb) return 0;
+      Kt = Ku + (size_t)b * kBlock * D;
+      Vt = Vu + (size_t)b * kBlock * D;
+      return min(kBlock, L - b * kBlock);
     }
-  }
-
-  const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
-  const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)unit * p.max_len * D;
-  const typename E::storage* kcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.kc) + (size_t)unit * p.nc_max * D : nullptr;
-  const typename E::storage* vcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.vc) + (size_t)unit * p.nc_max * D : nullptr;
-  const int nb = (L + kBlock - 1) / kBlock;
-  const int nc = (p.cmp_on && L >= 32) ? (L - 32) / 16 + 1 : 0;
-  const int win_len = min(p.window, L);
-  const int win_start = L - win_len;
+    if (branch == 1) {
+      const int start = win_start + tile * kBlock;
+      if (start >= L) return 0;
+      Kt = Ku + (size_t)start * D;
+      Vt = Vu + (size_t)start * D;
+      return min(kBlock, L - start);
+    }
+    const int start = tile * kBlock;
+    if (start >= nc) return 0;
+    Kt = kcu + (size_t)start * D;
+    Vt = vcu + (size_t)start * D;
+    return min(kBlock, nc - start);
+  };
 
   typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
   float m_run = -INFINITY, l_run = 0.f;
@@ -373,36 +402,37 @@ __device__ void attn_role(const DecodeParams& p, int unit, int branch, int local
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int j = 0; j < p.tpw && j < kMaxTpw; ++j) {
-    const int tile = (local * nw + wave) * p.tpw + j;
-    const typename E::storage *Kt = nullptr, *Vt = nullptr;
-    int nvalid = 0;
-    if (branch == 0) {
-      int b = -1;
+  // Software pipeline over the wave's tiles (valid tiles form a prefix): the next
+  // tile's K loads go out once this tile's scores are formed (overlapping the
+  // softmax and P V), its V loads after P V (overlapping the next scores).
+  TileRegs<E, D> tr;
+  const typename E::storage *Kt = nullptr, *Vt = nullptr;
+  int nv = tile_src(0, Kt, Vt);
+  if (nv > 0) {
+    tile_load_k<E, D>(Kt, nv, tr);
+    tile_load_v<E, D>(Vt, nv, tr);
+  }
+  // The group's queries as the B operand of S = K Q^T, requested after the first
+  // tile so that no round trip precedes the tile loads.  Columns n >= G repeat
+  // head G-1: their scores and outputs stay in their own columns and are never
+  // merged or written.
+  u32x4 qf[NCH];
+  {
+    const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
+                                    ((size_t)seq * p.hkv * G + (size_t)head * G + min(n, G - 1)) * D;
 #pragma unroll
-      for (int jj = 0; jj < kMaxTpw; ++jj) b = (jj == j) ? slc_blocks[jj] : b;
-      if (b >= 0 && b < nb) {
-        nvalid = min(kBlock, L - b * kBlock);
-        Kt = Ku + (size_t)b * kBlock * D;
-        Vt = Vu + (size_t)b * kBlock * D;
-      }
-    } else if (branch == 1) {
-      const int start = win_start + tile * kBlock;
-      if (start < L) {
-        nvalid = min(kBlock, L - start);
-        Kt = Ku + (size_t)start * D;
-        Vt = Vu + (size_t)start * D;
-      }
-    } else {
-      const int start = tile * kBlock;
-      if (start < nc) {
-        nvalid = min(kBlock, nc - start);
-        Kt = kcu + (size_t)start * D;
-        Vt = vcu + (size_t)start * D;
-      }
-    }
-    if (nvalid <= 0) continue;
-    attend_tile<E, D>(Kt, Vt, nvalid, qf, p.scale_log2, lds, m_run, l_run, acc_o);
+    for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
+  }
+  for (int j = 0; nv > 0; ++j) {
+    f32x4 sc4[4];
+    tile_scores<E, D>(tr, qf, sc4);
+    const typename E::storage *Kn = nullptr, *Vn = nullptr;
+    const int nv_next = tile_src(j + 1, Kn, Vn);
+    if (nv_next > 0) tile_load_k<E, D>(Kn, nv_next, tr);
+    tile_stage_v<E, D>(tr, lds);
+    tile_softmax_pv<E, D>(sc4, nv, p.scale_log2, lds, m_run, l_run, acc_o);
+    if (nv_next > 0) tile_load_v<E, D>(Vn, nv_next, tr);
+    nv = nv_next;
   }
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
@@ -527,7 +557,7 @@ __device__ void attn_role(const DecodeParams& p, int unit, int branch, int local
 }
 
 template <typename E, int D, int KIND, int HV>
-__global__ __launch_bounds__(kThreads) void k_decode(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, E::kBytes * D <= 256 ? 2 : 1) void k_decode(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int flag;
   const int i = blockIdx.x;

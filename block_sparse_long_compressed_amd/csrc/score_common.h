@@ -47,61 +47,102 @@ __device__ __forceinline__ void score_weights(const void* Q, size_t q_base, int 
   }
 }
 
-// Scores (without ln n_b) of the 16 blocks whose summary rows this lane's row
-// pointers address.  Two independent MFMA chains (linear / quadratic terms).
+// Summary rows of one 16-block tile held in registers: this lane's mean columns
+// and its second-order columns (the diagonal, or the first kRankGroup scaled
+// eigenvectors; further groups are fetched while scoring).
+constexpr int kRankGroup = 4;
+
 template <int D, int KIND>
-__device__ __forceinline__ f32x4 score_tile(const float* mrow, const float* vrow, int rank, int g, bool use_quad,
-                                            float alpha, const float (&wlin)[D / 16][4],
-                                            const float (&wquad)[D / 16][4]) {
-  constexpr int NU = D / 16;
-  f32x4 m4[NU];
+struct SumTile {
+  f32x4 m4[D / 16];
+  f32x4 v4[KIND == 0 ? 1 : kRankGroup][D / 16];
+};
+
+template <int D, int KIND>
+__device__ __forceinline__ void sum_tile_load_group(const float* vrow, int r0, int rank, int g, SumTile<D, KIND>& t) {
 #pragma unroll
-  for (int u = 0; u < NU; ++u) m4[u] = ld_f32x4(mrow + 16 * u + 4 * g);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (KIND == 0) {
-    f32x4 v4[NU];
-    if (use_quad) {
+  for (int rr = 0; rr < kRankGroup; ++rr) {
+    if (r0 + rr < rank) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) v4[u] = ld_f32x4(vrow + 16 * u + 4 * g);
+      for (int u = 0; u < D / 16; ++u) t.v4[rr][u] = ld_f32x4(vrow + (r0 + rr) * D + 16 * u + 4 * g);
     }
+  }
+}
+
+// Issue the loads of one tile (mrow / vrow: this lane's block row).
+template <int D, int KIND>
+__device__ __forceinline__ void sum_tile_load(const float* mrow, const float* vrow, int rank, int g, bool use_quad,
+                                              SumTile<D, KIND>& t) {
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) t.m4[u] = ld_f32x4(mrow + 16 * u + 4 * g);
+  if (use_quad) {
+    if constexpr (KIND == 0) {
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) t.v4[0][u] = ld_f32x4(vrow + 16 * u + 4 * g);
+    } else {
+      sum_tile_load_group<D, KIND>(vrow, 0, rank, g, t);
+    }
+  }
+}
+
+// Scores (without ln n_b) of the tile's 16 blocks for the group's heads from the
+// loaded rows.  Linear and quadratic terms are independent MFMA chains.
+template <int D, int KIND>
+__device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const float* vrow, int rank, int g, bool use_quad,
+                                                float alpha, const float (&wlin)[D / 16][4],
+                                                const float (&wquad)[D / 16][4]) {
+  constexpr int NU = D / 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(t.m4[u][c], wlin[u][c], acc);
+  }
+  if (!use_quad) return acc;
+  if constexpr (KIND == 0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc = mfma_f32_16x16x4(m4[u][c], wlin[u][c], acc);
-        if (use_quad) acc2 = mfma_f32_16x16x4(v4[u][c], wquad[u][c], acc2);
-      }
+      for (int c = 0; c < 4; ++c) acc2 = mfma_f32_16x16x4(t.v4[0][u][c], wquad[u][c], acc2);
     }
   } else {
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(m4[u][c], wlin[u][c], acc);
-    }
-    if (use_quad) {
+    // (v_i . q)^2 for each scaled eigenvector v_i: the projection is a linear MFMA
+    // chain with the linear weights, squared on the VALU
 #pragma unroll 1
-      for (int r = 0; r < rank; ++r) {
-        f32x4 v4[NU];
+    for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
+      if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, g, t);
 #pragma unroll
-        for (int u = 0; u < NU; ++u) v4[u] = ld_f32x4(vrow + r * D + 16 * u + 4 * g);
-        f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < kRankGroup; ++rr) {
+        if (r0 + rr < rank) {
+          f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < NU; u += 2) {
+          for (int u = 0; u < NU; u += 2) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            pr = mfma_f32_16x16x4(v4[u][c], wlin[u][c], pr);
-            pr2 = mfma_f32_16x16x4(v4[u + 1][c], wlin[u + 1][c], pr2);
+            for (int c = 0; c < 4; ++c) {
+              pr = mfma_f32_16x16x4(t.v4[rr][u][c], wlin[u][c], pr);
+              pr2 = mfma_f32_16x16x4(t.v4[rr][u + 1][c], wlin[u + 1][c], pr2);
+            }
           }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float dd = pr[i] + pr2[i];
-          acc2[i] += 0.5f * alpha * dd * dd;
+          for (int i = 0; i < 4; ++i) {
+            const float dd = pr[i] + pr2[i];
+            acc2[i] += 0.5f * alpha * dd * dd;
+          }
         }
       }
     }
   }
   return acc + acc2;
+}
+
+// Load and score one tile in one step.
+template <int D, int KIND>
+__device__ __forceinline__ f32x4 score_tile(const float* mrow, const float* vrow, int rank, int g, bool use_quad,
+                                            float alpha, const float (&wlin)[D / 16][4],
+                                            const float (&wquad)[D / 16][4]) {
+  SumTile<D, KIND> t;
+  sum_tile_load<D, KIND>(mrow, vrow, rank, g, use_quad, t);
+  return sum_tile_score<D, KIND>(t, vrow, rank, g, use_quad, alpha, wlin, wquad);
 }
 
 // Number of candidate blocks (a prefix [0, n)) for a query at position t of a
