@@ -58,5 +58,6 @@ hipError_t launch_build_lowrank(const BuildArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill_select(const PrefillArgs& a);
 hipError_t launch_prefill_attn(const PrefillArgs& a);
+hipError_t launch_prefill_attn_bf16(const PrefillArgs& a);   // token-blocked, bf16 K/V
 
 }  // namespace cobs

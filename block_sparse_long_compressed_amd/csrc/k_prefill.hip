@@ -302,12 +302,12 @@ static hipError_t launch_au(const PrefillArgs& a, const AuParams& ap) {
 }
 
 hipError_t launch_prefill_attn(const PrefillArgs& a) {
+  if (a.bf16) return launch_prefill_attn_bf16(a);      // token-blocked kernel (k_prefill_attn.hip)
   AuParams ap;
   ap.tokens = a.tokens; ap.hkv = a.hkv; ap.group = a.group; ap.seq_len = a.max_len; ap.nc_max = a.nc_max;
   ap.top_k = a.top_k; ap.window = a.window; ap.cmp_on = a.cmp_on; ap.q_pos0 = a.q_pos0;
   ap.scale_log2 = a.scale * kLog2e; ap.Q = a.Q; ap.K = a.K; ap.V = a.V; ap.kc = a.kc; ap.vc = a.vc;
   ap.gates = a.gates; ap.sel = a.sel; ap.out = a.out;
-  if (a.bf16) return a.head_dim == 128 ? launch_au<EltBF16, 128>(a, ap) : launch_au<EltBF16, 64>(a, ap);
   return a.head_dim == 128 ? launch_au<EltF32, 128>(a, ap) : launch_au<EltF32, 64>(a, ap);
 }
 

@@ -1,0 +1,368 @@
+// Token-blocked chunked-prefill attention (gfx950, bf16 K/V).
+//
+// NSA branches (Janus issue #181) for each query token t of a chunk, with the
+// readings of the decode path: selected blocks (the token's own top-k), the
+// window [t-W+1, t] and the pooled tokens j with 16j + 31 <= t, each an exact
+// softmax, combined as g_cmp o_cmp + g_slc o_slc + g_win o_win.
+//
+// A workgroup owns 8 consecutive tokens of one kv-head group (two per wave, so a
+// wave's B operand covers 2 x 16 query heads).  The window and pooled-token keys
+// of consecutive tokens nearly coincide, so those 64-key tiles are staged once in
+// LDS for all 8 tokens (double buffered, the next tile's global loads in flight
+// while the current one is consumed) and every token masks its own key range:
+//   K rows padded to d+8 elements, read as the A operand of S = K Q^T with
+//   16-byte reads;
+//   V rows padded to d+4 elements, its transpose (the A operand of O^T = V^T P^T)
+//   gathered with 16-bit reads, shared by both tokens of a wave.
+// Selected blocks differ per token: a second launch gives each (token, group)
+// one wave that gathers its blocks straight into registers with the shared
+// 64-key tile steps (software pipelined) and adds its gated output.  Keeping the
+// two phases in separate launches lets each run two waves per SIMD.
+#include "attn_tile.h"
+#include "cobs_device.h"
+#include "cobs_launch.h"
+
+#include <algorithm>
+
+namespace cobs {
+
+constexpr int kPfTokens = 8;          // query tokens per workgroup (two per wave)
+
+template <int D>
+struct PfShape {
+  static constexpr int kNch = D / 32;                    // 32-wide contraction slices of head_dim
+  static constexpr int kDt = D / 16;                     // 16-row output tiles of O^T
+  static constexpr int kKs = D + 8;                      // LDS row stride of staged K (elements)
+  static constexpr int kRowChunks = D / 8;               // 16-byte chunks per K/V row
+  static constexpr int kLoads = kBlock * kRowChunks / 256;   // 16-byte loads per thread per tile (K or V)
+  static constexpr int kVs = D + 4;                      // LDS row stride of staged V (elements)
+  static constexpr int kKElems = kBlock * kKs;
+  static constexpr int kBufElems = kKElems + kBlock * kVs;   // one staged tile: K then V
+};
+
+struct PaParams {
+  int tokens, hkv, group, seq_len, nc_max, top_k, window, cmp_on, q_pos0;
+  float scale_log2;
+  const uint16_t *Q, *K, *V, *kc, *vc;
+  const float* gates;
+  const int32_t* sel;
+  float* out;
+};
+
+template <int D>
+struct StageRegs {
+  u32x4 k[PfShape<D>::kLoads], v[PfShape<D>::kLoads];
+};
+
+// Global loads of one 64-row K/V tile (rows past nvalid repeat the last valid row).
+template <int D>
+__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
+                                           int nvalid, StageRegs<D>& r) {
+  using S = PfShape<D>;
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i) {
+    const int id = threadIdx.x + 256 * i;
+    const int row = min(id / S::kRowChunks, nvalid - 1), cc = id % S::kRowChunks;
+    r.k[i] = ld16(Ks + (size_t)row * D + cc * 8);
+    r.v[i] = ld16(Vs + (size_t)row * D + cc * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_store(const StageRegs<D>& r, uint16_t* buf) {
+  using S = PfShape<D>;
+  uint16_t* vs = buf + S::kKElems;
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i) {
+    const int id = threadIdx.x + 256 * i;
+    const int row = id / S::kRowChunks, cc = id % S::kRowChunks;
+    st16(buf + row * S::kKs + cc * 8, r.k[i]);
+    uint2* d2 = reinterpret_cast<uint2*>(vs + row * S::kVs + cc * 8);    // 8-byte aligned rows
+    d2[0] = make_uint2(r.v[i][0], r.v[i][1]);
+    d2[1] = make_uint2(r.v[i][2], r.v[i][3]);
+  }
+}
+
+// One staged tile for the wave's two tokens: keys at positions tile_start + 0..63,
+// token u sees positions [lo[u], hi[u]].
+template <int D>
+__device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start, const int (&lo)[2], const int (&hi)[2],
+                                            const u32x4 (&qf)[2][PfShape<D>::kNch], float scale_log2,
+                                            float (&m)[2], float (&l)[2], f32x4 (&acc)[2][PfShape<D>::kDt]) {
+  using S = PfShape<D>;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  f32x4 s[2][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < S::kNch; ++c) {
+      const u32x4 kop = *reinterpret_cast<const u32x4*>(buf + (16 * t + n) * S::kKs + (4 * c + g) * 8);
+      a0 = mfma_bf16_16x16x32(kop, qf[0][c], a0);
+      a1 = mfma_bf16_16x16x32(kop, qf[1][c], a1);
+    }
+    s[0][t] = a0;
+    s[1][t] = a1;
+  }
+  u32x4 pb[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = tile_start + 16 * t + 4 * g + i;
+        const float x = (pos >= lo[u] && pos <= hi[u]) ? s[u][t][i] * scale_log2 : -INFINITY;
+        s[u][t][i] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, shfl_xor_f(mt, 16));
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    const float m_new = fmaxf(m[u], mt);
+    // a token with no visible key yet keeps (m, l, acc) = (-inf, 0, 0); its P is all zero
+    const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m[u] - m_new);
+    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = fast_exp2(s[u][t][i] - mref);
+        s[u][t][i] = pv;
+        psum += pv;
+      }
+    }
+    l[u] = l[u] * corr + psum;
+    m[u] = m_new;
+#pragma unroll
+    for (int dt = 0; dt < S::kDt; ++dt) acc[u][dt] *= corr;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pb[u][h][0] = f32_to_bf16_bits(s[u][2 * h][0]) | (f32_to_bf16_bits(s[u][2 * h][1]) << 16);
+      pb[u][h][1] = f32_to_bf16_bits(s[u][2 * h][2]) | (f32_to_bf16_bits(s[u][2 * h][3]) << 16);
+      pb[u][h][2] = f32_to_bf16_bits(s[u][2 * h + 1][0]) | (f32_to_bf16_bits(s[u][2 * h + 1][1]) << 16);
+      pb[u][h][3] = f32_to_bf16_bits(s[u][2 * h + 1][2]) | (f32_to_bf16_bits(s[u][2 * h + 1][3]) << 16);
+    }
+  }
+  // O^T += V^T P^T: the A operand (V^T rows d, keys of lane group g) is gathered
+  // from the row-major V with 16-bit reads (padded stride: conflict-free)
+  const uint16_t* vs = buf + S::kKElems;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int dt = 0; dt < S::kDt; ++dt) {
+      const int col = 16 * dt + n;
+      u32x4 vop;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kb = 32 * h + 16 * e + 4 * g;
+        const uint32_t v0 = vs[(kb + 0) * S::kVs + col], v1 = vs[(kb + 1) * S::kVs + col];
+        const uint32_t v2 = vs[(kb + 2) * S::kVs + col], v3 = vs[(kb + 3) * S::kVs + col];
+        vop[2 * e] = v0 | (v1 << 16);
+        vop[2 * e + 1] = v2 | (v3 << 16);
+      }
+      acc[0][dt] = mfma_bf16_16x16x32(vop, pb[0][h], acc[0][dt]);
+      acc[1][dt] = mfma_bf16_16x16x32(vop, pb[1][h], acc[1][dt]);
+    }
+  }
+}
+
+// Window and pooled-token branches for the workgroup's 8 tokens; writes
+// out = g_win o_win + g_cmp o_cmp (zero where a token has no such keys).
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
+  using S = PfShape<D>;
+  constexpr int NCH = S::kNch, NDT = S::kDt;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* bufs = reinterpret_cast<uint16_t*>(smem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int head = blockIdx.y, G = p.group, L = p.seq_len;
+  const int tok0 = blockIdx.x * kPfTokens;
+  const int last_tok = min(tok0 + kPfTokens, p.tokens) - 1;
+  const int hcol = min(n, G - 1);           // columns n >= G repeat head G-1 and are never written
+
+  // this wave's two tokens (a token past the chunk sees nothing and writes nothing)
+  int tok[2], t[2];
+  bool live[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int k = tok0 + 2 * wave + u;
+    live[u] = k < p.tokens;
+    tok[u] = live[u] ? k : last_tok;
+    t[u] = p.q_pos0 + tok[u];
+  }
+  u32x4 qf[2][NCH];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint16_t* Qh = p.Q + ((size_t)tok[u] * p.hkv * G + (size_t)head * G + hcol) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qf[u][c] = ld16(Qh + (4 * c + g) * 8);
+  }
+
+  const int t_first = p.q_pos0 + tok0, t_last = p.q_pos0 + last_tok;
+  bool have_out = false;                     // uniform: the window branch already wrote the outputs
+#pragma unroll 1
+  for (int br = 0; br < 2; ++br) {             // 0 = window, 1 = pooled tokens
+    int lo[2], hi[2], base = 0, count = 0;
+    const uint16_t *Ksrc, *Vsrc;
+    if (br == 0) {
+      if (p.window > 0) {
+        base = max(0, t_first - p.window + 1);
+        count = t_last + 1 - base;
+      }
+      Ksrc = p.K + (size_t)head * L * D;
+      Vsrc = p.V + (size_t)head * L * D;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        lo[u] = max(0, t[u] - p.window + 1);
+        hi[u] = live[u] ? t[u] : -1;
+      }
+    } else {
+      if (p.cmp_on) count = t_last >= 31 ? (t_last - 31) / 16 + 1 : 0;
+      Ksrc = p.kc + (size_t)head * p.nc_max * D;
+      Vsrc = p.vc + (size_t)head * p.nc_max * D;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        lo[u] = 0;
+        hi[u] = (live[u] && t[u] >= 31) ? (t[u] - 31) / 16 : -1;
+      }
+    }
+    const int ntiles = (count + kBlock - 1) / kBlock;
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    f32x4 acc[2][NDT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (ntiles > 0) {
+      StageRegs<D> sr;
+      stage_load<D>(Ksrc + (size_t)base * D, Vsrc + (size_t)base * D, min(kBlock, count), sr);
+      __syncthreads();                         // the previous branch is done with the buffers
+      stage_store<D>(sr, bufs);
+#pragma unroll 1
+      for (int j = 0; j < ntiles; ++j) {
+        uint16_t* cur = bufs + (j & 1) * S::kBufElems;
+        const int nstart = base + (j + 1) * kBlock;
+        if (j + 1 < ntiles) stage_load<D>(Ksrc + (size_t)nstart * D, Vsrc + (size_t)nstart * D, min(kBlock, base + count - nstart), sr);
+        __syncthreads();                       // tile j staged by every thread
+        shared_tile<D>(cur, base + j * kBlock, lo, hi, qf, p.scale_log2, m, l, acc);
+        if (j + 1 < ntiles) stage_store<D>(sr, bufs + ((j + 1) & 1) * S::kBufElems);
+      }
+    }
+    // this branch's gated, normalised output goes straight to (or onto) the outputs
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float lt = l[u];
+      lt += shfl_xor_f(lt, 16);
+      lt += shfl_xor_f(lt, 32);
+      if (live[u] && n < G) {
+        const size_t row = (size_t)tok[u] * p.hkv * G + (size_t)head * G + n;
+        const float gate = p.gates ? p.gates[row * 3 + (br == 0 ? 2 : 0)] : 0.f;    // (cmp, slc, win)
+        const float f = lt > 0.f ? gate / lt : 0.f;
+        float* op = p.out + row * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const f32x4 prev = have_out ? ld_f32x4(op + 16 * dt) : f32x4{0.f, 0.f, 0.f, 0.f};
+          st_f32x4(op + 16 * dt, prev + f * acc[u][dt]);   // loads see this lane's own stores
+        }
+      }
+    }
+    have_out = true;
+  }
+}
+
+// Selected blocks: one wave per (token, kv-head group), gathered straight into
+// registers (software pipelined); adds g_slc o_slc to the outputs.
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_prefill_slc(PaParams p) {
+  using T = AttnTiling<EltBF16, D>;
+  constexpr int NCH = T::kChunks, NDT = T::kDt;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int head = blockIdx.y, G = p.group, L = p.seq_len;
+  const int tok = blockIdx.x * 4 + wave;
+  if (tok >= p.tokens) return;                 // waves are independent: no barriers below
+  const int hcol = min(n, G - 1);
+  const uint16_t* Kh = p.K + (size_t)head * L * D;
+  const uint16_t* Vh = p.V + (size_t)head * L * D;
+  const int32_t* selu = p.sel + ((size_t)tok * p.hkv + head) * p.top_k;
+  const int nb = (L + kBlock - 1) / kBlock;
+  auto src = [&](int j, const uint16_t*& Kt, const uint16_t*& Vt) -> int {
+    if (j >= p.top_k) return 0;
+    const int b = selu[j];
+    if (b < 0 || b >= nb) return 0;            // bounds-checked block index
+    Kt = Kh + (size_t)b * kBlock * D;
+    Vt = Vh + (size_t)b * kBlock * D;
+    return min(kBlock, L - b * kBlock);
+  };
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem) + (size_t)wave * kBlock * T::kRowStride;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileRegs<EltBF16, D> tr;
+  const uint16_t *Kt = nullptr, *Vt = nullptr;
+  int nv = src(0, Kt, Vt);
+  if (nv > 0) {
+    tile_load_k<EltBF16, D>(Kt, nv, tr);
+    tile_load_v<EltBF16, D>(Vt, nv, tr);
+  }
+  u32x4 qf[NCH];
+  {
+    const uint16_t* Qh = p.Q + ((size_t)tok * p.hkv * G + (size_t)head * G + hcol) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * 8);
+  }
+  for (int j = 0; nv > 0; ++j) {
+    f32x4 sc4[4];
+    tile_scores<EltBF16, D>(tr, qf, sc4);
+    const uint16_t *Kn = nullptr, *Vn = nullptr;
+    const int nv_next = src(j + 1, Kn, Vn);
+    if (nv_next > 0) tile_load_k<EltBF16, D>(Kn, nv_next, tr);
+    tile_stage_v<EltBF16, D>(tr, lds);
+    tile_softmax_pv<EltBF16, D>(sc4, nv, p.scale_log2, lds, m_run, l_run, acc);
+    if (nv_next > 0) tile_load_v<EltBF16, D>(Vn, nv_next, tr);
+    nv = nv_next;
+  }
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  if (n < G) {
+    const size_t row = (size_t)tok * p.hkv * G + (size_t)head * G + n;
+    const float gate = p.gates ? p.gates[row * 3 + 1] : 1.f;    // slc only without gates
+    const float f = l_run > 0.f ? gate / l_run : 0.f;
+    float* op = p.out + row * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) st_f32x4(op + 16 * dt, ld_f32x4(op + 16 * dt) + f * acc[dt]);
+  }
+}
+
+template <int D>
+static hipError_t launch_pa(const PrefillArgs& a) {
+  PaParams p;
+  p.tokens = a.tokens; p.hkv = a.hkv; p.group = a.group; p.seq_len = a.max_len; p.nc_max = a.nc_max;
+  p.top_k = a.top_k; p.window = a.window; p.cmp_on = a.cmp_on; p.q_pos0 = a.q_pos0;
+  p.scale_log2 = a.scale * kLog2e;
+  p.Q = static_cast<const uint16_t*>(a.Q); p.K = static_cast<const uint16_t*>(a.K);
+  p.V = static_cast<const uint16_t*>(a.V); p.kc = static_cast<const uint16_t*>(a.kc);
+  p.vc = static_cast<const uint16_t*>(a.vc); p.gates = a.gates; p.sel = a.sel; p.out = a.out;
+  dim3 g1((a.tokens + kPfTokens - 1) / kPfTokens, a.hkv, 1);
+  hipLaunchKernelGGL((k_prefill_shared<D>), g1, dim3(256), (size_t)2 * PfShape<D>::kBufElems * 2, a.stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2((a.tokens + 3) / 4, a.hkv, 1);
+  const size_t lds2 = attn_lds_bytes<EltBF16, D>(4);
+  hipLaunchKernelGGL((k_prefill_slc<D>), g2, dim3(256), lds2, a.stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn_bf16(const PrefillArgs& a) {
+  return a.head_dim == 128 ? launch_pa<128>(a) : launch_pa<64>(a);
+}
+
+}  // namespace cobs
