@@ -69,24 +69,6 @@ struct DecodeParams {
   float* part_o;                // [unit][P][G][d]
 };
 
-// Exclusive prefix sum over the 256 threads of a workgroup, in thread order.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int x = wave_inclusive_sum(v);
-  if (lane == 63) lds_w[w] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) {
-    const int c = lds_w[i];
-    base += (i < w) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
-
 // LDS of the scoring role (inside the launch's dynamic buffer).
 struct SelLds {
   float red_m[4][16], red_s[4][16];
@@ -260,71 +242,16 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
     for (int b = threadIdx.x; b < p.nb_max; b += kThreads) ss[b] = (b < ncand) ? s_shat[b] : -INFINITY;
   }
 
-  // ---- radix select of the k-th largest key --------------------------------
-  // Each wave fills a private 256-bin histogram (double-buffered across passes);
-  // after one barrier every wave sums the four and finds the digit itself.  The
-  // passes stop as soon as the bin holding the k-th key is taken whole.
-  const int e_end = max(0, min(per, ncand - b0));
-  const int kk = min(p.top_k, ncand);
-  uint32_t prefix = 0u, hi_mask = 0u;
-  int need = kk, eq_bin = 0;
-#pragma unroll 1
-  for (int pass = 0; pass < 4 && kk > 0; ++pass) {
-    const int shift = 24 - 8 * pass;
-    uint32_t* mine = sl.hist2[pass & 1][wave];
-    *reinterpret_cast<u32x4*>(&mine[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll 1
-    for (int e = 0; e < per; ++e) {               // uniform trip count: wave-wide ballots inside
-      const uint32_t key = (e < e_end) ? s_key[b0 + e] : 0u;
-      wave_histogram_add(mine, e < e_end && (key & hi_mask) == prefix, (key >> shift) & 255u);
-    }
-    __syncthreads();
-    u32x4 hb = *reinterpret_cast<const u32x4*>(&sl.hist2[pass & 1][0][4 * lane]);
-#pragma unroll
-    for (int w = 1; w < 4; ++w) hb += *reinterpret_cast<const u32x4*>(&sl.hist2[pass & 1][w][4 * lane]);
-    prefix |= radix_digit(hb, need, eq_bin) << shift;
-    hi_mask |= 255u << shift;
-    if (need == eq_bin) break;                    // every key with this prefix is taken
-  }
-  // taken: (key & hi_mask) > prefix, or == prefix among the first `need` by block index
-  int eq_rank = 0;
-  if (kk > 0 && need < eq_bin) {                  // a tie straddles the cut: rank the equal keys
-    int eq_count = 0;
-#pragma unroll 1
-    for (int e = 0; e < e_end; ++e) eq_count += ((s_key[b0 + e] & hi_mask) == prefix) ? 1 : 0;
-    int eq_total;
-    eq_rank = block_exclusive_scan(eq_count, sl.scan_w, &eq_total);
-  }
-  int take_count = 0;
-  if (kk > 0) {
-    int r = eq_rank;
-#pragma unroll 1
-    for (int e = 0; e < e_end; ++e) {
-      const uint32_t km = s_key[b0 + e] & hi_mask;
-      if (km > prefix) ++take_count;
-      else if (km == prefix) { take_count += (r < need) ? 1 : 0; ++r; }
-    }
-  }
-  int sel_total;
-  const int pos0 = block_exclusive_scan(take_count, sl.scan_w, &sel_total);
-  // the selection (ascending, -1 padded) and, for waiting attention waves, its codes
+  // ---- radix select; the selection (ascending, -1 padded) and, for waiting
+  // attention waves, its codes
   const Coherent so(p.sel + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
   const Coherent pc(p.pub ? static_cast<const void*>(p.pub + (size_t)unit * p.top_k) : static_cast<const void*>(p.sel),
                     (uint32_t)(p.top_k * 4));
-  if (kk > 0) {
-    int r = eq_rank, pos = pos0;
-#pragma unroll 1
-    for (int e = 0; e < e_end; ++e) {
-      const uint32_t km = s_key[b0 + e] & hi_mask;
-      bool tk = km > prefix;
-      if (km == prefix) { tk = r < need; ++r; }
-      if (tk) {
-        so.st1((uint32_t)(pos * 4), __int_as_float(b0 + e));
-        if (p.pub) pc.st1((uint32_t)(pos * 4), __uint_as_float((uint32_t)(b0 + e + 2)));
-        ++pos;
-      }
-    }
-  }
+  const int sel_total = wg_select_topk(s_key, ncand, per, p.top_k, &sl.hist2[0][0][0], sl.scan_w,
+                                       [&](int pos, int b) {
+                                         so.st1((uint32_t)(pos * 4), __int_as_float(b));
+                                         if (p.pub) pc.st1((uint32_t)(pos * 4), __uint_as_float((uint32_t)(b + 2)));
+                                       });
   for (int i = sel_total + (int)threadIdx.x; i < p.top_k; i += kThreads) {
     so.st1((uint32_t)(i * 4), __int_as_float(-1));
     if (p.pub) pc.st1((uint32_t)(i * 4), __uint_as_float(1u));

@@ -169,6 +169,146 @@ __global__ __launch_bounds__(256) void k_prefill_select(PsParams p) {
   for (int i = total + lane; i < p.top_k; i += 64) sel_u[i] = -1;
 }
 
+// One workgroup per (token, kv-head group) for contexts up to kPsWgMaxBlocks
+// blocks: the four waves score interleaved 16-block tiles once (two tiles in
+// flight per wave), keep the per-head scores block-major in LDS, combine their
+// per-head log-sum-exp partials, form the group scores from LDS and run the
+// workgroup radix select.  Longer contexts use the one-wave kernel above, which
+// scores twice instead of storing.
+constexpr int kPsWgMaxBlocks = 2048;
+
+struct PsWgLds {
+  float red_m[4][16], red_s[4][16];
+  uint32_t hist2[2][4][256];
+  int scan_w[4];
+  float lse_sh[16];
+  // followed by [nb_pad][16] scores and [nb_pad] keys
+};
+
+template <typename E, int D, int KIND>
+__global__ __launch_bounds__(256, 2) void k_prefill_select_wg(PsParams p) {
+  constexpr int NU = D / 16;
+  constexpr int RING = KIND == 0 ? 2 : 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  PsWgLds& sl = *reinterpret_cast<PsWgLds*>(smem);
+  float* s_sc = reinterpret_cast<float*>(smem + sizeof(PsWgLds));
+  uint32_t* s_key = reinterpret_cast<uint32_t*>(s_sc + (size_t)p.nb_pad * 16);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int tok = blockIdx.x, head = blockIdx.y, seq = blockIdx.z;
+  const int L = p.seq_lens ? p.seq_lens[seq] : p.L_fixed;
+  const int t = p.q_pos0 + tok;
+  const int ncand = candidate_blocks(L, t);
+  const int G = p.group;
+  const size_t unit = ((size_t)seq * p.tokens + tok) * p.hkv + head;
+  const size_t sum_base = ((size_t)seq * p.hkv + head) * p.nb_max;
+  const size_t so_row = KIND == 0 ? (size_t)D : (size_t)p.rank * D;
+  const int tiles = (ncand + 15) / 16;
+  const bool use_quad = p.alpha != 0.f;
+  auto rows_of = [&](int tile, const float*& mr, const float*& vr) {
+    const int brow = min(tile * 16 + n, ncand - 1);
+    mr = p.mu + (sum_base + brow) * D;
+    vr = p.so + (sum_base + brow) * so_row;
+  };
+
+  // ---- scores of tiles wave, wave+4, ... (summary rows requested before the query)
+  SumTile<D, KIND> st[RING];
+  const float* vrow[RING];
+#pragma unroll
+  for (int r = 0; r < RING; ++r) {
+    vrow[r] = nullptr;
+    const int tile = wave + 4 * r;
+    if (tile < tiles) {
+      const float* mrow;
+      rows_of(tile, mrow, vrow[r]);
+      sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+    }
+  }
+  float wlin[NU][4], wquad[NU][4];
+  score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
+                            n, g, G, p.scale, p.alpha, wlin, wquad);
+  float run_m = -INFINITY, run_s = 0.f;
+#pragma unroll 1
+  for (int j0 = 0; wave + 4 * j0 < tiles; j0 += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const int tile = wave + 4 * (j0 + r);
+      if (tile < tiles) {
+        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin, wquad);
+        if (tile + 4 * RING < tiles) {
+          const float* mrow;
+          rows_of(tile + 4 * RING, mrow, vrow[r]);
+          sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = tile * 16 + 4 * g + i;
+          const float sv = (b < ncand) ? s4[i] + __logf((float)min(kBlock, L - b * kBlock)) : -INFINITY;
+          const float mx = fmaxf(run_m, sv);
+          if (mx != -INFINITY) {
+            run_s = run_s * __expf(run_m - mx) + __expf(sv - mx);
+            run_m = mx;
+          }
+          s_sc[b * 16 + n] = sv;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 16; m < 64; m <<= 1) {
+    const float om = shfl_xor_f(run_m, m), os = shfl_xor_f(run_s, m);
+    const float mx = fmaxf(run_m, om);
+    if (mx != -INFINITY) { run_s = run_s * __expf(run_m - mx) + os * __expf(om - mx); run_m = mx; }
+  }
+  if (g == 0) { sl.red_m[wave][n] = run_m; sl.red_s[wave][n] = run_s; }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float M = -INFINITY, S = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float om = sl.red_m[w][threadIdx.x], os = sl.red_s[w][threadIdx.x];
+      const float mx = fmaxf(M, om);
+      if (mx != -INFINITY) { S = S * __expf(M - mx) + os * __expf(om - mx); M = mx; }
+    }
+    sl.lse_sh[threadIdx.x] = (M == -INFINITY) ? -INFINITY : M + __logf(S);
+  }
+  __syncthreads();
+
+  // ---- group scores shat_b = ln sum_h exp(s_hb - LSE_h); thread owns [tid*per, +per)
+  const int per = (ncand + 255) / 256;
+  float lse_r[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) lse_r[h] = sl.lse_sh[h];
+  const int b0 = threadIdx.x * per;
+#pragma unroll 1
+  for (int e = 0; e < per; ++e) {
+    const int b = b0 + e;
+    if (b >= ncand) break;
+    f32x4 raw[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) raw[v] = *reinterpret_cast<const f32x4*>(&s_sc[b * 16 + 4 * v]);
+    float M = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < G) M = fmaxf(M, raw[h >> 2][h & 3] - lse_r[h]);
+    float S = 0.f;
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < G) S += __expf(raw[h >> 2][h & 3] - lse_r[h] - M);
+    const float sh = M + __logf(S);
+    s_key[b] = orderable(sh);
+    if (p.sel_score) p.sel_score[unit * p.nb_max + b] = sh;
+  }
+  if (p.sel_score) {
+    for (int b = ncand + threadIdx.x; b < p.nb_max; b += 256) p.sel_score[unit * p.nb_max + b] = -INFINITY;
+  }
+  __syncthreads();
+
+  int32_t* sel_u = p.sel + unit * p.top_k;
+  const int total = wg_select_topk(s_key, ncand, per, p.top_k, &sl.hist2[0][0][0], sl.scan_w,
+                                   [&](int pos, int b) { sel_u[pos] = b; });
+  for (int i = total + (int)threadIdx.x; i < p.top_k; i += 256) sel_u[i] = -1;
+}
+
 struct AuParams {
   int tokens, hkv, group, seq_len, nc_max, top_k, window, cmp_on, q_pos0;
   float scale_log2;
@@ -273,6 +413,12 @@ __global__ __launch_bounds__(256) void k_attn_unit(AuParams p) {
 
 template <typename E, int D, int KIND>
 static hipError_t launch_ps(const PrefillArgs& a, const PsParams& sp) {
+  if (sp.nb_pad <= kPsWgMaxBlocks) {
+    dim3 grid(a.tokens, a.hkv, a.batch);
+    const size_t lds = sizeof(PsWgLds) + (size_t)sp.nb_pad * 17 * sizeof(float);
+    hipLaunchKernelGGL((k_prefill_select_wg<E, D, KIND>), grid, dim3(256), lds, a.stream, sp);
+    return hipGetLastError();
+  }
   dim3 grid((a.tokens + 3) / 4, a.hkv, a.batch);
   const size_t lds = (size_t)4 * sp.nb_pad * sizeof(uint32_t);
   hipLaunchKernelGGL((k_prefill_select<E, D, KIND>), grid, dim3(256), lds, a.stream, sp);

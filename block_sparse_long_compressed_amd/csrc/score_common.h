@@ -191,4 +191,92 @@ __device__ __forceinline__ uint32_t radix_digit(const u32x4& hb, int& need, int&
   return (uint32_t)__builtin_amdgcn_readlane(dig, src);
 }
 
+// Exclusive prefix sum over the 256 threads of a workgroup, in thread order.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_w, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x = wave_inclusive_sum(v);
+  if (lane == 63) lds_w[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lds_w[i];
+    base += (i < w) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// Top-k of the orderable keys[0, ncand) by a 256-thread workgroup, ties to the
+// lower block index (MSB-first 8-bit radix select).  Thread tid owns blocks
+// [tid * per, tid * per + per).  Each wave fills a private 256-bin histogram
+// (double-buffered across passes, `hist` is [2][4][256]); after one barrier every
+// wave sums the four and finds the digit itself; the passes stop as soon as the
+// bin holding the k-th key is taken whole.  Calls emit(pos, b) for every selected
+// block b with its position in ascending block order and returns how many were
+// selected (min(top_k, ncand)).
+template <typename Emit>
+__device__ __forceinline__ int wg_select_topk(const uint32_t* keys, int ncand, int per, int top_k,
+                                              uint32_t* hist, int* scan_w, Emit&& emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b0 = threadIdx.x * per;
+  const int e_end = max(0, min(per, ncand - b0));
+  const int kk = min(top_k, ncand);
+  uint32_t prefix = 0u, hi_mask = 0u;
+  int need = kk, eq_bin = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 4 && kk > 0; ++pass) {
+    const int shift = 24 - 8 * pass;
+    uint32_t* hp = hist + (pass & 1) * 1024;
+    uint32_t* mine = hp + wave * 256;
+    *reinterpret_cast<u32x4*>(&mine[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll 1
+    for (int e = 0; e < per; ++e) {               // uniform trip count: wave-wide ballots inside
+      const uint32_t key = (e < e_end) ? keys[b0 + e] : 0u;
+      wave_histogram_add(mine, e < e_end && (key & hi_mask) == prefix, (key >> shift) & 255u);
+    }
+    __syncthreads();
+    u32x4 hb = *reinterpret_cast<const u32x4*>(&hp[4 * lane]);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) hb += *reinterpret_cast<const u32x4*>(&hp[w * 256 + 4 * lane]);
+    prefix |= radix_digit(hb, need, eq_bin) << shift;
+    hi_mask |= 255u << shift;
+    if (need == eq_bin) break;                    // every key with this prefix is taken
+  }
+  // taken: (key & hi_mask) > prefix, or == prefix among the first `need` by block index
+  int eq_rank = 0;
+  if (kk > 0 && need < eq_bin) {                  // a tie straddles the cut: rank the equal keys
+    int eq_count = 0;
+#pragma unroll 1
+    for (int e = 0; e < e_end; ++e) eq_count += ((keys[b0 + e] & hi_mask) == prefix) ? 1 : 0;
+    int eq_total;
+    eq_rank = block_exclusive_scan(eq_count, scan_w, &eq_total);
+  }
+  int take_count = 0;
+  if (kk > 0) {
+    int r = eq_rank;
+#pragma unroll 1
+    for (int e = 0; e < e_end; ++e) {
+      const uint32_t km = keys[b0 + e] & hi_mask;
+      if (km > prefix) ++take_count;
+      else if (km == prefix) { take_count += (r < need) ? 1 : 0; ++r; }
+    }
+  }
+  int sel_total;
+  const int pos0 = block_exclusive_scan(take_count, scan_w, &sel_total);
+  if (kk > 0) {
+    int r = eq_rank, pos = pos0;
+#pragma unroll 1
+    for (int e = 0; e < e_end; ++e) {
+      const uint32_t km = keys[b0 + e] & hi_mask;
+      bool tk = km > prefix;
+      if (km == prefix) { tk = r < need; ++r; }
+      if (tk) emit(pos++, b0 + e);
+    }
+  }
+  return sel_total;
+}
+
 }  // namespace cobs
