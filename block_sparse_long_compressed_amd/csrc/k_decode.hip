@@ -122,16 +122,16 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
       sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
     }
   }
-  float wlin[NU][4], wquad[NU][4];
+  float wlin[NU][4];
   score_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
-                            p.alpha, wlin, wquad);
+                            wlin);
   float run_m = -INFINITY, run_s = 0.f;        // LSE partial of head n over this lane's blocks
   for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
       const int j = j0 + r, tile = tile0 + j0 + r;
       if (j < p.sel_tpw && tile < tiles_total) {
-        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin, wquad);
+        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
         if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
           const float* mrow;
           rows_of(tile + RING, mrow, vrow[r]);

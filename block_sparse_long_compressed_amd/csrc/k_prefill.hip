@@ -56,16 +56,16 @@ __global__ __launch_bounds__(256) void k_prefill_select(PsParams p) {
   const size_t sum_base = ((size_t)seq * p.hkv + head) * p.nb_max;
   const int tiles = (ncand + 15) / 16;
 
-  float wlin[NU][4], wquad[NU][4];
+  float wlin[NU][4];
   score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
-                            n, g, G, p.scale, p.alpha, wlin, wquad);
+                            n, g, G, p.scale, wlin);
   const bool use_quad = p.alpha != 0.f;
   auto scores = [&](int tile) -> f32x4 {
     const int brow = min(tile * 16 + n, ncand - 1);
     f32x4 s = score_tile<D, KIND>(p.mu + (sum_base + brow) * D,
                                   KIND == 0 ? p.so + (sum_base + brow) * D
                                             : p.so + (sum_base + brow) * (size_t)(p.rank * D),
-                                  p.rank, g, use_quad, p.alpha, wlin, wquad);
+                                  p.rank, g, use_quad, p.alpha, wlin);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = tile * 16 + 4 * g + i;
@@ -170,8 +170,7 @@ __global__ __launch_bounds__(256) void k_prefill_select(PsParams p) {
 }
 
 // One workgroup per (token, kv-head group) for contexts up to kPsWgMaxBlocks
-// blocks: the four waves score interleaved 16-block tiles once (two tiles in
-// flight per wave), keep the per-head scores block-major in LDS, combine their
+// blocks: the four waves score interleaved 16-block tiles once, keep the per-head scores block-major in LDS, combine their
 // per-head log-sum-exp partials, form the group scores from LDS and run the
 // workgroup radix select.  Longer contexts use the one-wave kernel above, which
 // scores twice instead of storing.
@@ -186,9 +185,9 @@ struct PsWgLds {
 };
 
 template <typename E, int D, int KIND>
-__global__ __launch_bounds__(256, 2) void k_prefill_select_wg(PsParams p) {
+__global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
   constexpr int NU = D / 16;
-  constexpr int RING = KIND == 0 ? 2 : 1;
+  constexpr int RING = 1;        // one tile in flight per wave; three waves per SIMD hide the rest
   extern __shared__ __align__(16) unsigned char smem[];
   PsWgLds& sl = *reinterpret_cast<PsWgLds*>(smem);
   float* s_sc = reinterpret_cast<float*>(smem + sizeof(PsWgLds));
@@ -224,9 +223,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_wg(PsParams p) {
       sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
     }
   }
-  float wlin[NU][4], wquad[NU][4];
+  float wlin[NU][4];
   score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
-                            n, g, G, p.scale, p.alpha, wlin, wquad);
+                            n, g, G, p.scale, wlin);
   float run_m = -INFINITY, run_s = 0.f;
 #pragma unroll 1
   for (int j0 = 0; wave + 4 * j0 < tiles; j0 += RING) {
@@ -234,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_wg(PsParams p) {
     for (int r = 0; r < RING; ++r) {
       const int tile = wave + 4 * (j0 + r);
       if (tile < tiles) {
-        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin, wquad);
+        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
         if (tile + 4 * RING < tiles) {
           const float* mrow;
           rows_of(tile + 4 * RING, mrow, vrow[r]);

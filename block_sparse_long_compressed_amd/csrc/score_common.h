@@ -27,11 +27,13 @@ __device__ __forceinline__ void load_q4(const void* Q, size_t off, float* out4) 
   }
 }
 
-// Weights of head n of the group whose first head's query starts at q_base:
-// linear scale*q, quadratic alpha/2 scale^2 q^2 (diagonal form only).
+// Linear weights scale*q of head n of the group whose first head's query starts
+// at q_base (zero for columns n >= G).  The diagonal quadratic weight alpha/2
+// scale^2 q^2 is formed from them inside the contraction, which keeps one set
+// of weight registers.
 template <typename E, int D, int KIND>
 __device__ __forceinline__ void score_weights(const void* Q, size_t q_base, int n, int g, int G, float scale,
-                                              float alpha, float (&wlin)[D / 16][4], float (&wquad)[D / 16][4]) {
+                                              float (&wlin)[D / 16][4]) {
   const bool hv = n < G;
   const size_t qoff = q_base + (size_t)(hv ? n : 0) * D;
 #pragma unroll
@@ -39,11 +41,7 @@ __device__ __forceinline__ void score_weights(const void* Q, size_t q_base, int 
     float q4[4];
     load_q4<E>(Q, qoff + 16 * u + 4 * g, q4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float qv = hv ? q4[c] : 0.f;
-      wlin[u][c] = scale * qv;
-      wquad[u][c] = (KIND == 0) ? 0.5f * alpha * scale * scale * qv * qv : 0.f;
-    }
+    for (int c = 0; c < 4; ++c) wlin[u][c] = hv ? scale * q4[c] : 0.f;
   }
 }
 
@@ -89,8 +87,7 @@ __device__ __forceinline__ void sum_tile_load(const float* mrow, const float* vr
 // loaded rows.  Linear and quadratic terms are independent MFMA chains.
 template <int D, int KIND>
 __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const float* vrow, int rank, int g, bool use_quad,
-                                                float alpha, const float (&wlin)[D / 16][4],
-                                                const float (&wquad)[D / 16][4]) {
+                                                float alpha, const float (&wlin)[D / 16][4]) {
   constexpr int NU = D / 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -103,7 +100,10 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const float
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc2 = mfma_f32_16x16x4(t.v4[0][u][c], wquad[u][c], acc2);
+      for (int c = 0; c < 4; ++c) {
+        const float w = wlin[u][c];
+        acc2 = mfma_f32_16x16x4(t.v4[0][u][c], 0.5f * alpha * w * w, acc2);   // alpha/2 scale^2 q^2
+      }
     }
   } else {
     // (v_i . q)^2 for each scaled eigenvector v_i: the projection is a linear MFMA
@@ -138,11 +138,10 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const float
 // Load and score one tile in one step.
 template <int D, int KIND>
 __device__ __forceinline__ f32x4 score_tile(const float* mrow, const float* vrow, int rank, int g, bool use_quad,
-                                            float alpha, const float (&wlin)[D / 16][4],
-                                            const float (&wquad)[D / 16][4]) {
+                                            float alpha, const float (&wlin)[D / 16][4]) {
   SumTile<D, KIND> t;
   sum_tile_load<D, KIND>(mrow, vrow, rank, g, use_quad, t);
-  return sum_tile_score<D, KIND>(t, vrow, rank, g, use_quad, alpha, wlin, wquad);
+  return sum_tile_score<D, KIND>(t, vrow, rank, g, use_quad, alpha, wlin);
 }
 
 // Number of candidate blocks (a prefix [0, n)) for a query at position t of a
