@@ -133,8 +133,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--eager", action="store_true", help="launch steps directly instead of graph replays")
-    ap.add_argument("--mode", choices=["decode", "prefill", "build", "copy"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "prefill", "build", "update", "copy"], default="decode",
                     help="decode (the metric), prefill (MFMA utilisation), build (summary GB/s), "
+                         "update (one appended token per sequence: incremental summaries), "
                          "copy (plain copy of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -153,6 +154,8 @@ def main():
         return bench_prefill(args)
     if args.mode == "build":
         return bench_build(args)
+    if args.mode == "update":
+        return bench_update(args)
     w = synth.WORKLOADS[args.workload]
     if w.prefill:
         raise SystemExit("use --mode prefill for prefill workloads")
@@ -336,6 +339,28 @@ def bench_build(args):
     print(json.dumps({"mode": "build", "workload": w.name, "second_order": w.so_kind, "rank": w.rank,
                       "ms": t * 1e3, "kv_bytes": kv, "GBps_streamed": kv / t / 1e9,
                       "pct_of_hbm_peak": 100 * kv / t / 1e9 / HBM_PEAK_GBPS}), flush=True)
+
+
+def bench_update(args):
+    """Incremental summaries for one decode step: every sequence grows by one token
+    (L-1 -> L); the touched block's statistics (and rank-r vectors) are recomputed
+    and the pooled token it completes, if any, is emitted."""
+    import torch
+    from block_sparse_long_compressed_amd import binding as B
+    from block_sparse_long_compressed_amd import synth
+    from tests import gpu_util as U
+    w = synth.WORKLOADS[args.workload]
+    x = synth.make_inputs(w, args.seed)
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = B.alloc_summaries(p, w.batch, w.max_len)
+    new = g["lens"]
+    old = (new - 1).contiguous()
+    B.cobs_build_summaries(p, old, g["K"], g["V"], s["mu"], s["so"], s["kc"], s["vc"])
+    fn = lambda: B.cobs_update_summaries(p, old, new, 1, g["K"], g["V"], s["mu"], s["so"], s["kc"], s["vc"])
+    t = timed(fn, max(1, min(args.steps, 50)))
+    print(json.dumps({"mode": "update", "workload": w.name, "second_order": w.so_kind, "rank": w.rank,
+                      "units": w.batch * w.n_kv_heads, "us_per_step": t * 1e6}), flush=True)
 
 
 def prefill_flops(w, lens, sel):

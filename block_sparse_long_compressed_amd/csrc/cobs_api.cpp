@@ -164,8 +164,37 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
   a.var = p->so_kind == COBS_SO_DIAG ? so : nullptr;
   a.lowrank = p->so_kind == COBS_SO_LOWRANK ? so : nullptr;
   a.kc = pool ? kc : nullptr; a.vc = pool ? vc : nullptr;
+  a.old_lens = nullptr; a.touch_blocks = 0;
   a.stream = (hipStream_t)stream;
   if ((st = hip_status(launch_build_diag(a))) != COBS_OK) return st;
+  if (a.lowrank) st = hip_status(launch_build_lowrank(a));
+  return st;
+}
+
+cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* old_lens,
+                                  const int32_t* new_lens, int32_t max_append, const void* K, const void* V,
+                                  float* mu, float* so, void* kc, void* vc, void* stream) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
+  if (max_append < 1 || max_append > max_len) return COBS_ERR_INVALID_ARG;
+  const bool pool = p->cmp_len > 0 && nc_of(p, max_len) > 0;
+  if (!old_lens || !new_lens || !K || !mu || !so) return COBS_ERR_INVALID_ARG;
+  if (pool && (!V || !kc || !vc)) return COBS_ERR_INVALID_ARG;
+  BuildArgs a;
+  a.batch = batch; a.hkv = p->n_kv_heads; a.max_len = max_len;
+  a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len);
+  a.head_dim = p->head_dim; a.rank = p->rank; a.bf16 = p->kv_dtype == COBS_BF16;
+  a.blocks_per_wave = 1;
+  a.seq_lens = new_lens; a.old_lens = old_lens;
+  a.touch_blocks = std::min((int)a.nb_max, cdiv(max_append - 1, 64) + 2);   // blocks a run of new positions can touch
+  a.K = K; a.V = pool ? V : K;
+  a.mu = mu;
+  a.var = p->so_kind == COBS_SO_DIAG ? so : nullptr;
+  a.lowrank = p->so_kind == COBS_SO_LOWRANK ? so : nullptr;
+  a.kc = pool ? kc : nullptr; a.vc = pool ? vc : nullptr;
+  a.stream = (hipStream_t)stream;
+  if ((st = hip_status(launch_append_diag(a))) != COBS_OK) return st;
   if (a.lowrank) st = hip_status(launch_build_lowrank(a));
   return st;
 }

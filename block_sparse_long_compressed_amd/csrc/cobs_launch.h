@@ -10,7 +10,9 @@ struct BuildArgs {
   int batch, hkv, max_len, nb_max, nc_max, head_dim, rank;
   bool bf16;
   int blocks_per_wave;
-  const int32_t* seq_lens;
+  const int32_t* seq_lens;     // lengths the summaries are built for
+  const int32_t* old_lens;     // incremental update: lengths they were valid for (else null)
+  int touch_blocks;            // incremental update: workgroups per (sequence, kv-head)
   const void *K, *V;
   float *mu, *var, *lowrank;   // var: diag channel or null; lowrank: [..][NB][rank][d] or null
   void *kc, *vc;               // null when the compressed branch is off
@@ -55,6 +57,7 @@ struct PrefillArgs {
 
 hipError_t launch_build_diag(const BuildArgs& a);
 hipError_t launch_build_lowrank(const BuildArgs& a);
+hipError_t launch_append_diag(const BuildArgs& a);     // mean, diagonal, pooled tokens of touched blocks
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill_select(const PrefillArgs& a);
 hipError_t launch_prefill_attn(const PrefillArgs& a);

@@ -40,7 +40,8 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 }
 
 template <typename E, int D>
-__global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __restrict__ seq_lens, int max_len,
+__global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __restrict__ seq_lens,
+                                                              const int32_t* __restrict__ old_lens, int max_len,
                                                               int nb_max, int rank,
                                                               const typename E::storage* __restrict__ K,
                                                               float* __restrict__ lowrank) {
@@ -58,10 +59,14 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
 
   const int tid = threadIdx.x;
   const int hkv = gridDim.y;
-  const int b = blockIdx.x, head = blockIdx.y, seq = blockIdx.z;
+  const int head = blockIdx.y, seq = blockIdx.z;
   const int L = seq_lens[seq];
+  // full build: block blockIdx.x; incremental update: the blocks holding positions
+  // >= old_lens[seq], walked with a stride of the grid width
+  const int b_first = (old_lens ? old_lens[seq] / kBlock : 0) + blockIdx.x;
+#pragma unroll 1
+  for (int b = b_first; b * kBlock < L; b += gridDim.x) {
   const int row0 = b * kBlock;
-  if (row0 >= L) return;
   const int n = min(kBlock, L - row0);
   const size_t unit = (size_t)seq * hkv + head;
   const typename E::storage* Kb = K + (unit * (size_t)max_len + row0) * D;
@@ -224,13 +229,15 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
   __syncthreads();
   float* dst = lowrank + ((unit * (size_t)nb_max + b) * rank) * D;
   for (int idx = tid; idx < rank * D; idx += kLrThreads) dst[idx] = (float)vout[idx / D][idx % D];
+  __syncthreads();                         // shared arrays are reused by the next block
+  }
 }
 
 template <typename E, int D>
 static hipError_t launch_lr(const BuildArgs& a) {
-  dim3 grid(a.nb_max, a.hkv, a.batch);
-  hipLaunchKernelGGL((k_build_lowrank<E, D>), grid, dim3(kLrThreads), 0, a.stream, a.seq_lens, a.max_len,
-                     a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank);
+  dim3 grid(a.old_lens ? a.touch_blocks : a.nb_max, a.hkv, a.batch);
+  hipLaunchKernelGGL((k_build_lowrank<E, D>), grid, dim3(kLrThreads), 0, a.stream, a.seq_lens, a.old_lens,
+                     a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank);
   return hipGetLastError();
 }
 

@@ -202,6 +202,110 @@ __global__ __launch_bounds__(64) void k_build_diag(
   }
 }
 
+// Incremental update after tokens are appended (positions [L_old, L_new) of each
+// sequence are new): every block holding a new position gets its mean and
+// diagonal variance recomputed from its keys, and every pooled token whose 32
+// rows become complete is emitted; nothing else is written.  One wave walks the
+// touched blocks b = L_old/64 + blockIdx.x, + gridDim.x, ...; pooled token c is
+// emitted by the wave of the block holding its last row 16c + 31.
+template <typename E, int D>
+__global__ __launch_bounds__(64) void k_append_diag(
+    const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens, int max_len, int nb_max,
+    int nc_max, const typename E::storage* __restrict__ K, const typename E::storage* __restrict__ V,
+    float* __restrict__ mu, float* __restrict__ var, typename E::storage* __restrict__ kc,
+    typename E::storage* __restrict__ vc, int want_pool) {
+  using T = RowTiling<E, D>;
+  constexpr int LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad, NL = T::kLoads, EPL = T::kEpl;
+  const int lane = threadIdx.x;
+  const int cc = lane % LPR, rg = lane / LPR;
+  const int hkv = gridDim.y;
+  const int head = blockIdx.y, seq = blockIdx.z;
+  const int L0 = old_lens[seq], L = new_lens[seq];
+  const size_t unit = (size_t)seq * hkv + head;
+  const typename E::storage* Ku = K + unit * (size_t)max_len * D;
+  const typename E::storage* Vu = V + unit * (size_t)max_len * D;
+  float* mu_u = mu + unit * (size_t)nb_max * D;
+  float* var_u = var ? var + unit * (size_t)nb_max * D : nullptr;
+#pragma unroll 1
+  for (int b = L0 / kBlock + blockIdx.x; b * kBlock < L; b += gridDim.x) {
+    const int row0 = b * kBlock;
+    const int nrows = min(kBlock, L - row0);
+    u32x4 xk[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) xk[i] = ld16(Ku + (size_t)min(row0 + i * RPL + rg, L - 1) * D + cc * EPL);
+    float sum[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sum[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sum[e] += ok * E::get(xk[i], e);
+    }
+    float mean[EPL];
+    const float inv_n = 1.0f / (float)nrows;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) mean[e] = reduce_rows<LPR>(sum[e]) * inv_n;
+    if (rg == 0) {
+      float* dst = mu_u + (size_t)b * D + cc * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]});
+    }
+    if (var_u) {
+      float sq[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sq[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float dlt = E::get(xk[i], e) - mean[e];
+          sq[e] += ok * dlt * dlt;
+        }
+      }
+      float v[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[e] = reduce_rows<LPR>(sq[e]) * inv_n;
+      if (rg == 1 % RPL) {
+        float* dst = var_u + (size_t)b * D + cc * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]});
+      }
+    }
+    if (want_pool) {
+      // pooled tokens c with last row 16c+31 in [max(row0, L0), min(row0+64, L)): newly complete here
+      const int lo = max(row0, L0), hi = min(row0 + kBlock, L);
+      const int c_lo = max(0, (lo - 31 + 15) / 16);
+      const int c_hi = hi >= 32 ? (hi - 32) / 16 + 1 : 0;       // 16c + 31 <= hi - 1
+      typename E::storage* kc_u = kc + unit * (size_t)nc_max * D;
+      typename E::storage* vc_u = vc + unit * (size_t)nc_max * D;
+#pragma unroll 1
+      for (int c = c_lo; c < c_hi; ++c) {
+        float a[EPL], w[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a[e] = w[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32 / RPL; ++i) {
+          const int r = 16 * c + i * RPL + rg;               // r <= 16c + 31 < L
+          const u32x4 xa = ld16(Ku + (size_t)r * D + cc * EPL);
+          const u32x4 xb = ld16(Vu + (size_t)r * D + cc * EPL);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) { a[e] += E::get(xa, e); w[e] += E::get(xb, e); }
+        }
+        float tk[EPL], tv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          tk[e] = reduce_rows<LPR>(a[e]) * (1.0f / 32.0f);
+          tv[e] = reduce_rows<LPR>(w[e]) * (1.0f / 32.0f);
+        }
+        if (rg == 0) store_pooled<E, D>(kc_u + (size_t)c * D + cc * EPL, tk);
+        if (rg == 1 % RPL) store_pooled<E, D>(vc_u + (size_t)c * D + cc * EPL, tv);
+      }
+    }
+  }
+}
+
 template <typename E, int D>
 static hipError_t launch_diag(const BuildArgs& a) {
   const int bpw = a.blocks_per_wave;
@@ -212,6 +316,20 @@ static hipError_t launch_diag(const BuildArgs& a) {
                      a.mu, a.var, (typename E::storage*)a.kc, (typename E::storage*)a.vc,
                      bpw, a.var != nullptr ? 1 : 0, a.kc != nullptr ? 1 : 0);
   return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t launch_append(const BuildArgs& a) {
+  dim3 grid(a.touch_blocks, a.hkv, a.batch);
+  hipLaunchKernelGGL((k_append_diag<E, D>), grid, dim3(64), 0, a.stream, a.old_lens, a.seq_lens, a.max_len,
+                     a.nb_max, a.nc_max, (const typename E::storage*)a.K, (const typename E::storage*)a.V,
+                     a.mu, a.var, (typename E::storage*)a.kc, (typename E::storage*)a.vc, a.kc != nullptr ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_diag(const BuildArgs& a) {
+  if (a.bf16) return a.head_dim == 128 ? launch_append<EltBF16, 128>(a) : launch_append<EltBF16, 64>(a);
+  return a.head_dim == 128 ? launch_append<EltF32, 128>(a) : launch_append<EltF32, 64>(a);
 }
 
 hipError_t launch_build_diag(const BuildArgs& a) {

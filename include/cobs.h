@@ -121,6 +121,25 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
                                  const int32_t* seq_lens, const void* K, const void* V,
                                  float* mu, float* so, void* kc, void* vc, void* stream);
 
+/* Incremental summary update after tokens are appended to the cache (the summaries
+ * stay compact and query-independent as the prefix grows: COBS Technisches
+ * Resuemee 2.1-2.3; NSA compression path).  K and V hold every sequence at its new
+ * length; mu, so, kc, vc hold summaries valid for old_lens (from cobs_build_summaries
+ * or an earlier update).  Every block that holds a position in [old_len, new_len)
+ * is recomputed from its keys (mean, diagonal or rank-r channel) and every pooled
+ * token whose rows [16j, 16j+32) become complete is written; all other entries are
+ * left untouched, so afterwards the summaries equal a build at new_lens.
+ *   old_lens, new_lens  [batch] int32 device, 0 <= old_len <= new_len <= max_len
+ *                       (not checked on the device: the caller's guarantee)
+ *   max_append          host upper bound of new_len - old_len (>= 1); it only sizes the
+ *                       launch, every touched block is updated whatever its value
+ *   K, V, mu, so, kc, vc as for cobs_build_summaries (same layouts and max_len)
+ * Errors as for cobs_build_summaries; INVALID_ARG also when max_append < 1. */
+cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t max_len,
+                                  const int32_t* old_lens, const int32_t* new_lens, int32_t max_append,
+                                  const void* K, const void* V, float* mu, float* so, void* kc, void* vc,
+                                  void* stream);
+
 /* Block scoring, group aggregation and top-k (COBS 2.1-2.3; skill card "Method").
  * Decode when q_pos0 < 0: n_q_tokens must be 1 and each sequence's query sits at
  * t = L_b - 1.  Chunked prefill when q_pos0 >= 0: query i of every sequence sits at

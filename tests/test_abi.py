@@ -104,6 +104,15 @@ def test_null_pointers_and_small_workspace_rejected_before_any_hip_call():
     st = lib.cobs_sparse_attn_prefill(ctypes.byref(p), 1024, 10, 1020, fake, fake, fake, fake, fake, fake, fake,
                                       None, None, fake, fake, 1 << 30, None)
     assert st == B.COBS_ERR_INVALID_ARG                   # tokens run past the prefix
+    st = lib.cobs_update_summaries(ctypes.byref(p), 1, 1024, fake, fake, 0, fake, fake, fake, fake, fake, fake,
+                                   None)
+    assert st == B.COBS_ERR_INVALID_ARG                   # max_append must be >= 1
+    st = lib.cobs_update_summaries(ctypes.byref(p), 1, 1024, None, fake, 1, fake, fake, fake, fake, fake, fake,
+                                   None)
+    assert st == B.COBS_ERR_INVALID_ARG                   # old lengths missing
+    st = lib.cobs_update_summaries(ctypes.byref(p), 1, 1024, fake, fake, 1, fake, fake, fake, fake, None, None,
+                                   None)
+    assert st == B.COBS_ERR_INVALID_ARG                   # pooled outputs missing
 
 
 def test_status_strings():
