@@ -133,9 +133,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--eager", action="store_true", help="launch steps directly instead of graph replays")
-    ap.add_argument("--mode", choices=["decode", "prefill", "build", "update", "copy"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "prefill", "build", "update", "recall", "copy"], default="decode",
                     help="decode (the metric), prefill (MFMA utilisation), build (summary GB/s), "
                          "update (one appended token per sequence: incremental summaries), "
+                         "recall (cumulant selections against the exact-mass selection), "
                          "copy (plain copy of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -156,6 +157,8 @@ def main():
         return bench_build(args)
     if args.mode == "update":
         return bench_update(args)
+    if args.mode == "recall":
+        return bench_recall(args)
     w = synth.WORKLOADS[args.workload]
     if w.prefill:
         raise SystemExit("use --mode prefill for prefill workloads")
@@ -361,6 +364,38 @@ def bench_update(args):
     t = timed(fn, max(1, min(args.steps, 50)))
     print(json.dumps({"mode": "update", "workload": w.name, "second_order": w.so_kind, "rank": w.rank,
                       "units": w.batch * w.n_kv_heads, "us_per_step": t * 1e6}), flush=True)
+
+
+def bench_recall(args):
+    """Quality diagnostic: the share of the exact-mass top-k (every key read) that the
+    cumulant selection keeps, for alpha in {0, 0.5, 1, 2}; and the time of both selectors."""
+    import torch
+    from block_sparse_long_compressed_amd import binding as B
+    from block_sparse_long_compressed_amd import synth
+    from tests import gpu_util as U
+    w = synth.WORKLOADS[args.workload]
+    x = synth.make_inputs(w, args.seed)
+    g = U.to_device(x)
+    p = U.params_for(w)
+    ws = B.alloc_workspace(p, w.batch, w.max_len)
+    exact = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
+    fx = lambda: B.cobs_select_topk_exact(p, g["lens"], g["Q"], g["K"], exact, ws)
+    t_exact = timed(fx, max(1, min(args.steps, 20)))
+    ex = exact.cpu().numpy()
+    res = {"mode": "recall", "workload": w.name, "us_exact_selection": t_exact * 1e6, "recall": {}}
+    for alpha in (0.0, 0.5, 1.0, 2.0):
+        pa = U.params_for(w, alpha=alpha)
+        s = U.build(pa, g)
+        sel = torch.empty_like(exact)
+        fs = lambda: B.cobs_select_topk(pa, g["lens"], g["Q"][:, None], s["mu"], s["so"], sel, ws, max_len=w.max_len)
+        t = timed(fs, max(1, min(args.steps, 20)))
+        sl = sel.cpu().numpy()
+        hit = sum(len(set(sl[b, h][sl[b, h] >= 0]) & set(ex[b, h][ex[b, h] >= 0]))
+                  for b in range(w.batch) for h in range(w.n_kv_heads))
+        tot = sum(int((ex[b, h] >= 0).sum()) for b in range(w.batch) for h in range(w.n_kv_heads))
+        res["recall"][str(alpha)] = hit / max(tot, 1)
+        res[f"us_cumulant_selection_alpha{alpha}"] = t * 1e6
+    print(json.dumps(res), flush=True)
 
 
 def prefill_flops(w, lens, sel):

@@ -58,6 +58,7 @@ _SIGNATURES = {
     "cobs_build_summaries": (_i32, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "cobs_select_topk": (_i32, [_P, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cobs_update_summaries": (_i32, [_P, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "cobs_select_topk_exact": (_i32, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cobs_sparse_attn_decode": (_i32, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _sz, _vp]),
     "cobs_sparse_attn_prefill": (_i32, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -141,6 +142,13 @@ def cobs_update_summaries(p: cobs_params, old_lens, new_lens, max_append: int, K
     _check("cobs_update_summaries", lib().cobs_update_summaries(
         ctypes.byref(p), batch, max_len, _ptr(old_lens), _ptr(new_lens), max_append, _ptr(K), _ptr(V), _ptr(mu),
         _ptr(so), _ptr(kc), _ptr(vc), _stream(stream)))
+
+
+def cobs_select_topk_exact(p: cobs_params, seq_lens, Q, K, sel, ws, sel_score=None, stream=None) -> None:
+    batch, max_len = K.shape[0], K.shape[2]
+    _check("cobs_select_topk_exact", lib().cobs_select_topk_exact(
+        ctypes.byref(p), batch, max_len, _ptr(seq_lens), _ptr(Q), _ptr(K), _ptr(sel), _ptr(sel_score), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def cobs_select_topk(p: cobs_params, seq_lens, Q, mu, so, sel, ws, sel_score=None, max_len: int = 0,

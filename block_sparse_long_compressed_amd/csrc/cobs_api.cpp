@@ -256,6 +256,22 @@ cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_le
   return hip_status(launch_decode(a));
 }
 
+cobs_status cobs_select_topk_exact(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
+                                   const void* Q, const void* K, int32_t* sel, float* sel_score, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
+  if (!seq_lens || !Q || !K || !sel || !ws) return COBS_ERR_INVALID_ARG;
+  const Plan pl = make_plan(p, batch, max_len, 1);
+  if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
+  DecodeArgs a = decode_args(p, pl, batch, max_len, seq_lens, ws, (hipStream_t)stream);
+  a.do_select = true;
+  a.so_kind = 2;                               // exact masses from K
+  a.Q = Q; a.K = K; a.sel = sel; a.sel_score = sel_score;
+  return hip_status(launch_decode(a));
+}
+
 cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
                                     const void* Q, const void* K, const void* V, const float* mu, const float* so,
                                     const void* kc, const void* vc, const float* gates, const int32_t* sel_in,

@@ -96,58 +96,116 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
   const Coherent lp(p.lse_part + (size_t)unit * p.splits * 32, (uint32_t)(p.splits * 32 * 4));
 
   // ---- phase 1: scores of this workgroup's tiles -------------------------
-  // Summary rows are requested before the query so that both arrive in one
-  // round trip, and the wave keeps RING tiles in flight: each tile's slot is
-  // refilled with the tile RING ahead as soon as it is scored.  (A rank-r tile
-  // is already several times larger than a diagonal one.)
-  constexpr int RING = KIND == 0 ? 2 : 1;
-  const bool use_quad = p.alpha != 0.f;
-  const size_t sum_base = (size_t)unit * p.nb_max;
-  const size_t so_row = KIND == 0 ? (size_t)D : (size_t)p.rank * D;
   const int tiles_total = (ncand + 15) / 16;
   const int tile0 = (split * 4 + wave) * p.sel_tpw;
-  auto rows_of = [&](int tile, const float*& mr, const float*& vr) {
-    const int brow = min(tile * 16 + n, ncand - 1);      // A-operand row (block) of this lane
-    mr = p.mu + (sum_base + brow) * D;
-    vr = p.so + (sum_base + brow) * so_row;
-  };
-  SumTile<D, KIND> st[RING];
-  const float* vrow[RING];
-#pragma unroll
-  for (int r = 0; r < RING; ++r) {
-    vrow[r] = nullptr;
-    if (r < p.sel_tpw && tile0 + r < tiles_total) {
-      const float* mrow;
-      rows_of(tile0 + r, mrow, vrow[r]);
-      sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
-    }
-  }
-  float wlin[NU][4];
-  score_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
-                            wlin);
   float run_m = -INFINITY, run_s = 0.f;        // LSE partial of head n over this lane's blocks
-  for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
+  // scores s4[i] of blocks tile*16 + 4g + i for head n: running LSE and block-major hand-off
+  auto post = [&](int tile, const f32x4& s4, bool add_ln_n) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = tile * 16 + 4 * g + i;
+      const int nbk = min(kBlock, L - b * kBlock);
+      const float s = (b < ncand) ? s4[i] + (add_ln_n ? __logf((float)nbk) : 0.f) : -INFINITY;
+      const float mx = fmaxf(run_m, s);
+      if (mx != -INFINITY) {
+        run_s = run_s * __expf(run_m - mx) + __expf(s - mx);
+        run_m = mx;
+      }
+      if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), s);
+    }
+  };
+  if constexpr (KIND == 2) {
+    // Exact masses (the selection oracle of COBS 2.1, a diagnostic that reads every
+    // key): ln m_b = ln sum_r exp(scale q_h . k_r) over the block's keys, from the
+    // 64-key MFMA tile S = K Q^T with a log-sum-exp over the keys of each column.
+    using T = AttnTiling<E, D>;
+    u32x4 qf[T::kChunks];
+    {
+      const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
+                                      ((size_t)seq * p.hkv * G + (size_t)head * G + min(n, G - 1)) * D;
+#pragma unroll
+      for (int c = 0; c < T::kChunks; ++c) qf[c] = ld16(Qh + (4 * c + g) * T::kEpl);
+    }
+    const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
+    const float scale_log2 = p.scale * kLog2e;
+#pragma unroll 1
+    for (int j = 0; j < p.sel_tpw; ++j) {
+      const int tile = tile0 + j;
+      if (tile >= tiles_total) break;
+      f32x4 s4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll 1
+      for (int jb = 0; jb < 16; ++jb) {
+        const int b = tile * 16 + jb;
+        if (b >= ncand) break;
+        const int nvalid = min(kBlock, L - b * kBlock);
+        TileRegs<E, D> tr;
+        tile_load_k<E, D>(Ku + (size_t)b * kBlock * D, nvalid, tr);
+        f32x4 sk[4];
+        tile_scores<E, D>(tr, qf, sk);
+        float mt = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = (16 * t + 4 * g + i < nvalid) ? sk[t][i] * scale_log2 : -INFINITY;
+            sk[t][i] = x;
+            mt = fmaxf(mt, x);
+          }
+        mt = fmaxf(mt, shfl_xor_f(mt, 16));
+        mt = fmaxf(mt, shfl_xor_f(mt, 32));
+        float ss = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ss += fast_exp2(sk[t][i] - mt);
+        ss += shfl_xor_f(ss, 16);
+        ss += shfl_xor_f(ss, 32);
+        const float lm = (mt + fast_log2(ss)) * kLn2;          // ln m_b for head n
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4[i] = (g == jb / 4 && i == jb % 4) ? lm : s4[i];
+      }
+      post(tile, s4, false);
+    }
+  } else {
+    // Summary rows are requested before the query so that both arrive in one
+    // round trip, and the wave keeps RING tiles in flight: each tile's slot is
+    // refilled with the tile RING ahead as soon as it is scored.  (A rank-r tile
+    // is already several times larger than a diagonal one.)
+    constexpr int RING = KIND == 0 ? 2 : 1;
+    const bool use_quad = p.alpha != 0.f;
+    const size_t sum_base = (size_t)unit * p.nb_max;
+    const size_t so_row = KIND == 0 ? (size_t)D : (size_t)p.rank * D;
+    auto rows_of = [&](int tile, const float*& mr, const float*& vr) {
+      const int brow = min(tile * 16 + n, ncand - 1);      // A-operand row (block) of this lane
+      mr = p.mu + (sum_base + brow) * D;
+      vr = p.so + (sum_base + brow) * so_row;
+    };
+    SumTile<D, KIND> st[RING];
+    const float* vrow[RING];
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
-      const int j = j0 + r, tile = tile0 + j0 + r;
-      if (j < p.sel_tpw && tile < tiles_total) {
-        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
-        if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
-          const float* mrow;
-          rows_of(tile + RING, mrow, vrow[r]);
-          sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
-        }
+      vrow[r] = nullptr;
+      if (r < p.sel_tpw && tile0 + r < tiles_total) {
+        const float* mrow;
+        rows_of(tile0 + r, mrow, vrow[r]);
+        sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+      }
+    }
+    float wlin[NU][4];
+    score_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
+                              wlin);
+    for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int b = tile * 16 + 4 * g + i;
-          const int nbk = min(kBlock, L - b * kBlock);
-          const float s = (b < ncand) ? s4[i] + __logf((float)nbk) : -INFINITY;
-          const float mx = fmaxf(run_m, s);
-          if (mx != -INFINITY) {
-            run_s = run_s * __expf(run_m - mx) + __expf(s - mx);
-            run_m = mx;
+      for (int r = 0; r < RING; ++r) {
+        const int j = j0 + r, tile = tile0 + j0 + r;
+        if (j < p.sel_tpw && tile < tiles_total) {
+          const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
+          if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
+            const float* mrow;
+            rows_of(tile + RING, mrow, vrow[r]);
+            sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
           }
-          if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), s);
+          post(tile, s4, true);
         }
       }
     }
@@ -530,6 +588,11 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeParams& dp) {
 template <typename E, int D>
 static hipError_t launch_decode_ed(const DecodeArgs& a, const DecodeParams& dp) {
   const int hv = a.group <= 4 ? 1 : a.group <= 8 ? 2 : 4;
+  if (a.so_kind == 2) {                       // exact masses: scoring roles only
+    if (hv == 1) return launch_decode_t<E, D, 2, 1>(a, dp);
+    if (hv == 2) return launch_decode_t<E, D, 2, 2>(a, dp);
+    return launch_decode_t<E, D, 2, 4>(a, dp);
+  }
   if (a.so_kind == 0) {
     if (hv == 1) return launch_decode_t<E, D, 0, 1>(a, dp);
     if (hv == 2) return launch_decode_t<E, D, 0, 2>(a, dp);

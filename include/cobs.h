@@ -157,6 +157,19 @@ cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_le
                              int32_t* sel, float* sel_score,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Selection by exact attention mass (the selection oracle of COBS Technisches
+ * Resuemee 2.1, a quality diagnostic: it reads every key of every candidate block).
+ * Decode only (query at t = L_b - 1).  Each block is scored by
+ * ln m_b = ln sum_{r in b} exp(scale q_h . k_r) instead of the cumulant estimate; the
+ * group aggregation, candidate rule, tie-break and outputs are those of
+ * cobs_select_topk, so comparing the two selections measures the estimate's recall.
+ *   Q    [batch][1][H_q][d] kv_dtype;  K  [batch][H_kv][max_len][d] kv_dtype
+ *   sel, sel_score, ws  as for cobs_select_topk (decode).
+ * Errors as for cobs_select_topk. */
+cobs_status cobs_select_topk_exact(const cobs_params* p, int32_t batch, int32_t max_len,
+                                   const int32_t* seq_lens, const void* Q, const void* K, int32_t* sel,
+                                   float* sel_score, void* ws, size_t ws_bytes, void* stream);
+
 /* One decode step for every sequence: selection (unless sel_in is given), then the
  * SLC, WIN and CMP branches and the gated combine (NSA three paths, COBS 2.3).
  *   Q        [batch][H_q][d] kv_dtype, query at t = L_b - 1

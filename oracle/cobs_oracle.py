@@ -291,14 +291,21 @@ def run(inputs: dict, p: dict, seqs=None, groups=None, tokens=None):
     return res
 
 
-def oracle_selection_mass(p: dict, qg: np.ndarray, keys: np.ndarray, L: int, t: int) -> np.ndarray:
-    """OSA: the same group ranking, but on exact masses ln m_b instead of the
+def exact_group_scores(p: dict, qg: np.ndarray, keys: np.ndarray, L: int, t: int):
+    """Group scores of the candidate blocks from exact masses ln m_b instead of the
     cumulant estimate ([COBS] 2.1: ranking by exact mass needs every key).
-    Returns the top-k candidate blocks (ascending, -1 padded)."""
+    Returns (candidate block indices, shat over them)."""
     n = block_sizes(L)
     last = np.arange(len(n)) * BLOCK + n - 1
     cand = np.nonzero(last <= t)[0]
     s = np.array([[np.log(attention_mass(qg[h], keys[b * BLOCK: b * BLOCK + n[b]], p["scale"]))
                    for b in cand] for h in range(qg.shape[0])])
-    pick, _ = select_topk(group_scores(s), p["top_k"])
+    return cand, group_scores(s)
+
+
+def oracle_selection_mass(p: dict, qg: np.ndarray, keys: np.ndarray, L: int, t: int) -> np.ndarray:
+    """OSA: the group ranking on exact masses.  Returns the top-k candidate blocks
+    (ascending, -1 padded)."""
+    cand, shat = exact_group_scores(p, qg, keys, L, t)
+    pick, _ = select_topk(shat, p["top_k"])
     return np.array([cand[i] if i >= 0 else -1 for i in pick], dtype=np.int64)
