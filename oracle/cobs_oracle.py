@@ -33,6 +33,12 @@ reason in the design notes of the repository):
   * kappa_2 uses 1/n_b (population covariance of the block's keys);
   * the compressed second-order channel is either the diagonal of kappa_2
     ('diag') or its top-r eigenvectors scaled by sqrt(eigenvalue) ('lowrank');
+  * the compressed storage of [COBS] 2.3 (bf16 mean, FP4 eigenvectors;
+    'lowrank_fp4') rounds the mean to the nearest bf16 (ties to even) and each
+    scaled eigenvector to FP4 E2M1 with one power-of-two scale per 32
+    consecutive entries, the scale and rounding of the OCP microscaling (MX)
+    format: X = 2^(floor(log2 max|v|) - 2), entries round to the nearest of
+    {0, .5, 1, 1.5, 2, 3, 4, 6} * X (ties to the even code), saturating at 6X;
   * a GQA group ranks blocks by the sum over its heads of each head's
     estimated share of attention mass (softmax of the scores over candidates);
   * ties go to the lower block index; fewer candidates than k -> pad with -1;
@@ -104,21 +110,93 @@ def lowrank_second_order(keys: np.ndarray, rank: int) -> np.ndarray:
     return out
 
 
+# FP4 E2M1 magnitudes by code (sign in the fourth bit): 0, .5, 1, 1.5, 2, 3, 4, 6
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MX_GROUP = 32
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 of each value (ties to an even mantissa), as float64: the
+    storage rounding of the compressed mean ([COBS] 2.3, BF16 mean)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    for i, v in np.ndenumerate(x):
+        if v == 0.0:
+            out[i] = 0.0
+            continue
+        e = int(np.floor(np.log2(abs(v))))
+        ulp = 2.0 ** (e - 7)                           # 8 significant bits
+        q = v / ulp
+        f = np.floor(q)
+        r = q - f
+        if r > 0.5 or (r == 0.5 and int(f) % 2 == 1):
+            f += 1
+        out[i] = f * ulp
+    return out
+
+
+def quantize_e2m1(y: float) -> int:
+    """FP4 E2M1 code (0..15) of y (already divided by the group scale): nearest
+    representable magnitude, ties to the even code, saturating at 6."""
+    a = abs(y)
+    sign = 8 if y < 0 else 0
+    best = 0
+    for c in range(8):
+        d, db = abs(a - E2M1[c]), abs(a - E2M1[best])
+        if d < db or (d == db and c % 2 == 0):
+            best = c
+    if a >= E2M1[7]:
+        best = 7
+    return sign | best if best else 0
+
+
+def mx_scale_exponent(group: np.ndarray) -> int:
+    """Shared power-of-two exponent of an MX group: floor(log2(max|v|)) - 2, so
+    the largest entry lands in [4, 8) before rounding (E2M1's top binade)."""
+    amax = float(np.max(np.abs(group)))
+    if amax == 0.0:
+        return -127
+    return int(np.floor(np.log2(amax))) - 2
+
+
+def quantize_mxfp4(v: np.ndarray):
+    """Codes and group exponents of a vector (length a multiple of 32)."""
+    codes = np.zeros(v.shape[0], dtype=np.int64)
+    exps = np.zeros(v.shape[0] // MX_GROUP, dtype=np.int64)
+    for gi in range(exps.shape[0]):
+        grp = v[gi * MX_GROUP:(gi + 1) * MX_GROUP]
+        e = mx_scale_exponent(grp)
+        exps[gi] = e
+        for j, y in enumerate(grp):
+            codes[gi * MX_GROUP + j] = quantize_e2m1(y / 2.0 ** e)
+    return codes, exps
+
+
+def dequantize_mxfp4(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    mag = E2M1[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    return mag * np.repeat(2.0 ** exps.astype(np.float64), MX_GROUP)
+
+
 def summaries(keys: np.ndarray, L: int, so_kind: str, rank: int = 0):
     """Per-block summaries of one (sequence, kv-head): (mu [NB][d], so, n [NB]).
 
-    so is [NB][d] for 'diag', [NB][rank][d] for 'lowrank'."""
+    so is [NB][d] for 'diag', [NB][rank][d] for 'lowrank' and for 'lowrank_fp4'
+    (whose mean and vectors are the stored, rounded values)."""
     n = block_sizes(L)
     mu, so = [], []
     for b, nb in enumerate(n):
         kb = keys[b * BLOCK: b * BLOCK + nb]
-        mu.append(block_mean(kb))
+        m = block_mean(kb)
         if so_kind == "diag":
             so.append(diag_second_order(kb))
         elif so_kind == "lowrank":
             so.append(lowrank_second_order(kb, rank))
+        elif so_kind == "lowrank_fp4":
+            m = round_bf16(m)
+            so.append(np.array([dequantize_mxfp4(*quantize_mxfp4(v)) for v in lowrank_second_order(kb, rank)]))
         else:
             raise ValueError(so_kind)
+        mu.append(m)
     return np.array(mu), np.array(so), n
 
 
@@ -150,6 +228,8 @@ def block_scores(q: np.ndarray, mu: np.ndarray, so: np.ndarray, n: np.ndarray,
     with S_b = diag(so_b) ('diag') or sum_i so_b[i] so_b[i]^T ('lowrank').
     q is [H][d]; returns [H][NB]."""
     lin = scale * (q @ mu.T)
+    if so_kind == "lowrank_fp4":
+        so_kind = "lowrank"                                    # the stored vectors, dequantized
     if so_kind == "diag":
         quad = (q * q) @ so.T                                  # sum_j q_j^2 var_j
     else:

@@ -439,3 +439,78 @@ def test_second_order_recall_against_exact_mass_beats_first_order():
         rec1 += len(osa & set(O.run(x, O.params_of(w))[(0, 0, 0)][1]))
         rec0 += len(osa & set(O.run(x, O.params_of(w, alpha=0.0))[(0, 0, 0)][1]))
     assert rec1 > rec0, (rec1, rec0)
+
+
+# ---------------------------------------------------------------------------
+# Compressed summary storage ([COBS] 2.3: BF16 mean, FP4 eigenvectors) with the
+# OCP microscaling (MX) FP4 rule: per 32 entries X = 2^(floor(log2 amax) - 2),
+# entries rounded to E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6} * X, ties to the even code.
+# ---------------------------------------------------------------------------
+
+def test_e2m1_grid_ties_and_saturation():
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for code, v in enumerate(grid):
+        assert O.quantize_e2m1(v) == code
+        if code:
+            assert O.quantize_e2m1(-v) == 8 | code
+    # midpoints go to the code with a zero mantissa bit (the even code)
+    for mid, code in [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6)]:
+        assert O.quantize_e2m1(mid) == code, mid
+    # just off a midpoint, the nearer value wins
+    assert O.quantize_e2m1(1.2500001) == 3 and O.quantize_e2m1(4.9999) == 6
+    # saturation and signed zero
+    assert O.quantize_e2m1(7.99) == 7 and O.quantize_e2m1(-100.0) == 15
+    assert O.quantize_e2m1(-0.1) == 0
+
+
+def test_mx_group_scale_hand_example():
+    g = np.zeros(32)
+    g[0], g[1], g[2], g[3] = 3.0, 0.3, -1.1, 0.12
+    codes, exps = O.quantize_mxfp4(g)
+    assert exps.tolist() == [-1]                       # floor(log2 3) - 2 = -1: X = 1/2
+    # 3 -> 6X (code 7); .3 -> .6X -> .5X (code 1); -1.1 -> -2.2X -> -2X (code 12); .12 -> .24X -> 0
+    assert codes[:4].tolist() == [7, 1, 12, 0]
+    assert O.dequantize_mxfp4(codes, exps)[:4].tolist() == [3.0, 0.25, -1.0, 0.0]
+    z, ez = O.quantize_mxfp4(np.zeros(32))
+    assert not z.any() and not O.dequantize_mxfp4(z, ez).any()
+
+
+def test_mxfp4_error_bound():
+    """Half the local grid step: at most X below 6X, under 2X in the saturated top."""
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        v = rng.standard_normal(64) * 10.0 ** rng.uniform(-3, 2)
+        codes, exps = O.quantize_mxfp4(v)
+        err = np.abs(O.dequantize_mxfp4(codes, exps) - v)
+        X = np.repeat(2.0 ** exps, 32)
+        assert (err <= np.where(np.abs(v) <= 6 * X, 1.0, 2.0) * X + 1e-300).all()
+        amax = np.abs(v).reshape(-1, 32).max(axis=1)
+        assert ((amax >= 4 * 2.0 ** exps) & (amax < 8 * 2.0 ** exps)).all()
+
+
+def test_round_bf16():
+    assert O.round_bf16(np.array([1.0, -2.0, 0.0, 2.0 ** -130])).tolist() == [1.0, -2.0, 0.0, 2.0 ** -130]
+    # halfway between 1 and 1 + 2^-7 goes to the even mantissa (1), between 1 + 2^-7 and 1 + 2^-6 up
+    assert O.round_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8])).tolist() == [1.0, 1 + 2.0 ** -6]
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(1000) * 10.0 ** rng.uniform(-5, 5, 1000)
+    r = O.round_bf16(x)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(x))) - 7)
+    assert (np.abs(r - x) <= ulp / 2).all()
+
+
+def test_fp4_summaries_are_the_rounded_lowrank_ones():
+    rng = np.random.default_rng(5)
+    keys = rng.standard_normal((150, 64)) * 0.4 + 0.1
+    mu, so, n = O.summaries(keys, 150, "lowrank", 2)
+    mu4, so4, n4 = O.summaries(keys, 150, "lowrank_fp4", 2)
+    assert (n == n4).all()
+    np.testing.assert_array_equal(mu4, O.round_bf16(mu))
+    for b in range(len(n)):
+        for i in range(2):
+            np.testing.assert_array_equal(so4[b, i], O.dequantize_mxfp4(*O.quantize_mxfp4(so[b, i])))
+    # scores from the stored form stay close to the fp64 ones
+    q = rng.standard_normal((4, 64))
+    s32 = O.block_scores(q, mu, so, n, 1.0, 0.125, "lowrank")
+    s4 = O.block_scores(q, mu4, so4, n4, 1.0, 0.125, "lowrank_fp4")
+    assert np.abs(s4 - s32).max() < 0.05 * np.abs(s32).max()
