@@ -43,7 +43,12 @@ def algorithmic_bytes(w, lens, sel, alpha):
     the pooled tokens, summaries of the candidate blocks, Q, gates, output."""
     es = 2 if w.dtype == "bf16" else 4
     d, G = w.head_dim, w.group
-    so_ch = 0 if alpha == 0 else (w.rank if w.so_kind == "lowrank" else 1)
+    if w.so_kind == "lowrank_fp4":           # bf16 mean + one compressed record per block
+        rec = -(-w.rank * (d // 2 + d // 32) // 16) * 16
+        sum_bytes_per_block = d * 2 + (0 if alpha == 0 else rec)
+    else:
+        so_ch = 0 if alpha == 0 else (w.rank if w.so_kind == "lowrank" else 1)
+        sum_bytes_per_block = d * 4 * (1 + so_ch)
     attn = sel_b = 0
     for b in range(w.batch):
         L = int(lens[b])
@@ -56,7 +61,7 @@ def algorithmic_bytes(w, lens, sel, alpha):
                 if blk >= 0:
                     slc.update(range(64 * blk, min(64 * blk + 64, L)))
             attn += (len(slc) + len(win - slc) + nc) * d * 2 * es
-            sel_b += nb * d * 4 * (1 + so_ch)
+            sel_b += nb * sum_bytes_per_block
     q = w.batch * w.n_q_heads * d * es
     attn += q + w.batch * w.n_q_heads * (3 * 4 + d * 4) + sel.size * 4
     sel_b += q + sel.size * 4

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libcobs.so")
 
 COBS_OK, COBS_ERR_INVALID_ARG, COBS_ERR_UNSUPPORTED, COBS_ERR_WORKSPACE, COBS_ERR_HIP = range(5)
 COBS_BF16, COBS_F32 = 0, 1
-COBS_SO_DIAG, COBS_SO_LOWRANK = 0, 1
+COBS_SO_DIAG, COBS_SO_LOWRANK, COBS_SO_LOWRANK_FP4 = 0, 1, 2
 
 
 class cobs_params(ctypes.Structure):
@@ -184,11 +184,14 @@ def cobs_sparse_attn_prefill(p: cobs_params, q_pos0: int, Q, K, V, mu, so, kc, v
 def alloc_summaries(p: cobs_params, batch: int, max_len: int, device="cuda") -> dict:
     sh = cobs_summary_shapes(p, batch, max_len)
     nb, nc, d, hkv = sh["nb_max"], sh["nc_max"], p.head_dim, p.n_kv_heads
-    mu = torch.empty((batch, hkv, nb, d), dtype=torch.float32, device=device)
-    if p.so_kind == COBS_SO_LOWRANK:
-        so = torch.empty((batch, hkv, nb, p.rank, d), dtype=torch.float32, device=device)
+    if p.so_kind == COBS_SO_LOWRANK_FP4:
+        # bf16 means; one byte record per block (codes, exponents, padding)
+        mu = torch.empty((batch, hkv, nb, d), dtype=torch.bfloat16, device=device)
+        so = torch.empty((batch, hkv, nb, sh["so_bytes"] // (batch * hkv * nb)), dtype=torch.uint8, device=device)
     else:
-        so = torch.empty((batch, hkv, nb, d), dtype=torch.float32, device=device)
+        mu = torch.empty((batch, hkv, nb, d), dtype=torch.float32, device=device)
+        so_shape = (batch, hkv, nb, p.rank, d) if p.so_kind == COBS_SO_LOWRANK else (batch, hkv, nb, d)
+        so = torch.empty(so_shape, dtype=torch.float32, device=device)
     kdt = torch.bfloat16 if p.kv_dtype == COBS_BF16 else torch.float32
     kc = vc = None
     if nc > 0:

@@ -26,6 +26,10 @@ int64_t nb_of(int max_len) { return (max_len + 63) / 64; }
 int64_t nc_of(const cobs_params* p, int max_len) {
   return (p->cmp_len > 0 && max_len >= 32) ? (max_len - 32) / 16 + 1 : 0;
 }
+// bytes of one block's compressed low-rank record: codes, exponents, padding to 16
+size_t fp4_record_bytes(int rank, int d) { return ((size_t)rank * (d / 2 + d / 32) + 15) / 16 * 16; }
+// kernel-side score kinds: 0 diag, 1 low-rank fp32, 2 exact masses, 3 low-rank fp4
+int kernel_kind(const cobs_params* p) { return p->so_kind == COBS_SO_LOWRANK_FP4 ? 3 : p->so_kind; }
 float scale_of(const cobs_params* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim); }
 int group_of(const cobs_params* p) { return p->n_q_heads / p->n_kv_heads; }
 
@@ -35,8 +39,9 @@ cobs_status check_params(const cobs_params* p) {
   if (p->top_k < 1 || p->top_k > 64) return COBS_ERR_INVALID_ARG;
   if (p->window < 0) return COBS_ERR_INVALID_ARG;
   if (p->cmp_len < 0 || p->cmp_stride < 0) return COBS_ERR_INVALID_ARG;
-  if (p->so_kind != COBS_SO_DIAG && p->so_kind != COBS_SO_LOWRANK) return COBS_ERR_INVALID_ARG;
-  if (p->so_kind == COBS_SO_LOWRANK && (p->rank < 1 || p->rank > 8)) return COBS_ERR_INVALID_ARG;
+  if (p->so_kind != COBS_SO_DIAG && p->so_kind != COBS_SO_LOWRANK && p->so_kind != COBS_SO_LOWRANK_FP4)
+    return COBS_ERR_INVALID_ARG;
+  if (p->so_kind != COBS_SO_DIAG && (p->rank < 1 || p->rank > 8)) return COBS_ERR_INVALID_ARG;
   if (!(p->alpha >= 0.f) || !isfinite(p->alpha)) return COBS_ERR_INVALID_ARG;
   if (!(p->scale >= 0.f) || !isfinite(p->scale)) return COBS_ERR_INVALID_ARG;
   if (p->kv_dtype != COBS_BF16 && p->kv_dtype != COBS_F32) return COBS_ERR_INVALID_ARG;
@@ -133,8 +138,12 @@ cobs_status cobs_summary_shapes(const cobs_params* p, int32_t batch, int32_t max
   const size_t esz = p->kv_dtype == COBS_BF16 ? 2 : 4;
   if (nb_max) *nb_max = nb;
   if (nc_max) *nc_max = nc;
-  if (mu_bytes) *mu_bytes = rows * nb * p->head_dim * sizeof(float);
-  if (so_bytes) *so_bytes = rows * nb * p->head_dim * sizeof(float) * (p->so_kind == COBS_SO_LOWRANK ? p->rank : 1);
+  const bool fp4 = p->so_kind == COBS_SO_LOWRANK_FP4;
+  if (mu_bytes) *mu_bytes = rows * nb * p->head_dim * (fp4 ? 2 : sizeof(float));
+  if (so_bytes) {
+    if (fp4) *so_bytes = rows * nb * fp4_record_bytes(p->rank, p->head_dim);
+    else *so_bytes = rows * nb * p->head_dim * sizeof(float) * (p->so_kind == COBS_SO_LOWRANK ? p->rank : 1);
+  }
   if (pooled_bytes) *pooled_bytes = rows * nc * p->head_dim * esz;
   return COBS_OK;
 }
@@ -145,7 +154,7 @@ size_t cobs_workspace_bytes(const cobs_params* p, int32_t batch, int32_t max_len
 }
 
 cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
-                                 const void* K, const void* V, float* mu, float* so, void* kc, void* vc,
+                                 const void* K, const void* V, void* mu, void* so, void* kc, void* vc,
                                  void* stream) {
   cobs_status st = check_params(p);
   if (st != COBS_OK) return st;
@@ -161,8 +170,9 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
   a.blocks_per_wave = std::min(8, std::max(2, cdiv(units * a.nb_max, 4 * 256 * 4)));
   a.seq_lens = seq_lens; a.K = K; a.V = pool ? V : K;
   a.mu = mu;
-  a.var = p->so_kind == COBS_SO_DIAG ? so : nullptr;
-  a.lowrank = p->so_kind == COBS_SO_LOWRANK ? so : nullptr;
+  a.var = p->so_kind == COBS_SO_DIAG ? static_cast<float*>(so) : nullptr;
+  a.lowrank = p->so_kind == COBS_SO_DIAG ? nullptr : so;
+  a.fp4 = p->so_kind == COBS_SO_LOWRANK_FP4;
   a.kc = pool ? kc : nullptr; a.vc = pool ? vc : nullptr;
   a.old_lens = nullptr; a.touch_blocks = 0;
   a.stream = (hipStream_t)stream;
@@ -173,7 +183,7 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
 
 cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* old_lens,
                                   const int32_t* new_lens, int32_t max_append, const void* K, const void* V,
-                                  float* mu, float* so, void* kc, void* vc, void* stream) {
+                                  void* mu, void* so, void* kc, void* vc, void* stream) {
   cobs_status st = check_params(p);
   if (st != COBS_OK) return st;
   if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
@@ -190,8 +200,9 @@ cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t m
   a.touch_blocks = std::min((int)a.nb_max, cdiv(max_append - 1, 64) + 2);   // blocks a run of new positions can touch
   a.K = K; a.V = pool ? V : K;
   a.mu = mu;
-  a.var = p->so_kind == COBS_SO_DIAG ? so : nullptr;
-  a.lowrank = p->so_kind == COBS_SO_LOWRANK ? so : nullptr;
+  a.var = p->so_kind == COBS_SO_DIAG ? static_cast<float*>(so) : nullptr;
+  a.lowrank = p->so_kind == COBS_SO_DIAG ? nullptr : so;
+  a.fp4 = p->so_kind == COBS_SO_LOWRANK_FP4;
   a.kc = pool ? kc : nullptr; a.vc = pool ? vc : nullptr;
   a.stream = (hipStream_t)stream;
   if ((st = hip_status(launch_append_diag(a))) != COBS_OK) return st;
@@ -205,7 +216,7 @@ static PrefillArgs prefill_args(const cobs_params* p, int32_t batch, int32_t max
   a.batch = batch; a.tokens = tokens; a.hkv = p->n_kv_heads; a.group = group_of(p); a.head_dim = p->head_dim;
   a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len); a.top_k = p->top_k;
   a.window = p->window; a.cmp_on = (p->cmp_len > 0 && nc_of(p, max_len) > 0) ? 1 : 0; a.rank = p->rank;
-  a.so_kind = p->so_kind; a.q_pos0 = q_pos0; a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha;
+  a.so_kind = kernel_kind(p); a.q_pos0 = q_pos0; a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha;
   a.scale = scale_of(p); a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr;
   a.mu = a.so = a.gates = nullptr; a.sel = nullptr; a.sel_score = nullptr; a.out = nullptr; a.stream = stream;
   return a;
@@ -217,7 +228,7 @@ static DecodeArgs decode_args(const cobs_params* p, const Plan& pl, int32_t batc
   a.batch = batch; a.hkv = p->n_kv_heads; a.group = group_of(p); a.head_dim = p->head_dim;
   a.max_len = max_len; a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len); a.top_k = p->top_k;
   a.window = p->window; a.cmp_on = (p->cmp_len > 0 && nc_of(p, max_len) > 0) ? 1 : 0; a.rank = p->rank;
-  a.so_kind = p->so_kind; a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha; a.scale = scale_of(p);
+  a.so_kind = kernel_kind(p); a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha; a.scale = scale_of(p);
   a.do_select = a.do_attn = false;
   a.splits = pl.sel_splits; a.sel_tpw = pl.sel_tpw;
   a.tpw = pl.attn_tpw; a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
@@ -235,7 +246,7 @@ static DecodeArgs decode_args(const cobs_params* p, const Plan& pl, int32_t batc
 }
 
 cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
-                             int32_t n_q_tokens, int32_t q_pos0, const void* Q, const float* mu, const float* so,
+                             int32_t n_q_tokens, int32_t q_pos0, const void* Q, const void* mu, const void* so,
                              int32_t* sel, float* sel_score, void* ws, size_t ws_bytes, void* stream) {
   cobs_status st = check_params(p);
   if (st != COBS_OK) return st;
@@ -273,7 +284,7 @@ cobs_status cobs_select_topk_exact(const cobs_params* p, int32_t batch, int32_t 
 }
 
 cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t max_len, const int32_t* seq_lens,
-                                    const void* Q, const void* K, const void* V, const float* mu, const float* so,
+                                    const void* Q, const void* K, const void* V, const void* mu, const void* so,
                                     const void* kc, const void* vc, const float* gates, const int32_t* sel_in,
                                     int32_t* sel_out, float* out, void* ws, size_t ws_bytes, void* stream) {
   cobs_status st = check_params(p);
@@ -301,7 +312,7 @@ cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t
 }
 
 cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int32_t n_q_tokens, int32_t q_pos0,
-                                     const void* Q, const void* K, const void* V, const float* mu, const float* so,
+                                     const void* Q, const void* K, const void* V, const void* mu, const void* so,
                                      const void* kc, const void* vc, const float* gates, int32_t* sel_out,
                                      float* out, void* ws, size_t ws_bytes, void* stream) {
   cobs_status st = check_params(p);

@@ -14,7 +14,10 @@ struct BuildArgs {
   const int32_t* old_lens;     // incremental update: lengths they were valid for (else null)
   int touch_blocks;            // incremental update: workgroups per (sequence, kv-head)
   const void *K, *V;
-  float *mu, *var, *lowrank;   // var: diag channel or null; lowrank: [..][NB][rank][d] or null
+  void* mu;                    // fp32 [..][NB][d], or bf16 when fp4 is set
+  float* var;                  // diagonal channel, or null
+  void* lowrank;               // fp32 [..][NB][rank][d], or FP4 records when fp4 is set; or null
+  bool fp4;                    // compressed storage: bf16 mean, MX FP4 vectors
   void *kc, *vc;               // null when the compressed branch is off
   hipStream_t stream;
 };
@@ -29,7 +32,8 @@ struct DecodeArgs {
   int tpw, wg_slc, wg_win, wg_cmp;   // attention: 64-key tiles per wave, workgroups per branch and unit
   const int32_t* seq_lens;
   const void *Q, *K, *V, *kc, *vc;
-  const float *mu, *so, *gates;
+  const void *mu, *so;         // summaries in the layout of so_kind (3: compressed storage)
+  const float* gates;
   int32_t* sel;                // written by the selection role
   const int32_t* sel_in;       // caller's selection (attention only)
   float* sel_score;
@@ -48,7 +52,8 @@ struct PrefillArgs {
   float alpha, scale;
   const int32_t* seq_lens;     // device [batch] or null (then every length is max_len)
   const void *Q, *K, *V, *kc, *vc;
-  const float *mu, *so, *gates;
+  const void *mu, *so;
+  const float* gates;
   int32_t* sel;
   float* sel_score;
   float* out;

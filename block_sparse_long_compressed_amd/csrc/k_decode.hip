@@ -49,7 +49,7 @@ struct DecodeParams {
   // scoring / selection
   int sel_wgs, splits, sel_tpw, rank;
   float alpha, scale;
-  const float *mu, *so;
+  const void *mu, *so;
   int32_t* sel;                 // selection written by the scoring role
   float* sel_score;
   uint32_t* sel_counters;
@@ -174,19 +174,17 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
     constexpr int RING = KIND == 0 ? 2 : 1;
     const bool use_quad = p.alpha != 0.f;
     const size_t sum_base = (size_t)unit * p.nb_max;
-    const size_t so_row = KIND == 0 ? (size_t)D : (size_t)p.rank * D;
-    auto rows_of = [&](int tile, const float*& mr, const float*& vr) {
+    auto rows_of = [&](int tile, const void*& mr, const void*& vr) {
       const int brow = min(tile * 16 + n, ncand - 1);      // A-operand row (block) of this lane
-      mr = p.mu + (sum_base + brow) * D;
-      vr = p.so + (sum_base + brow) * so_row;
+      summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, mr, vr);
     };
     SumTile<D, KIND> st[RING];
-    const float* vrow[RING];
+    const void* vrow[RING];
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
       vrow[r] = nullptr;
       if (r < p.sel_tpw && tile0 + r < tiles_total) {
-        const float* mrow;
+        const void* mrow;
         rows_of(tile0 + r, mrow, vrow[r]);
         sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
       }
@@ -201,7 +199,7 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
         if (j < p.sel_tpw && tile < tiles_total) {
           const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
           if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
-            const float* mrow;
+            const void* mrow;
             rows_of(tile + RING, mrow, vrow[r]);
             sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
           }
@@ -597,6 +595,11 @@ static hipError_t launch_decode_ed(const DecodeArgs& a, const DecodeParams& dp) 
     if (hv == 1) return launch_decode_t<E, D, 0, 1>(a, dp);
     if (hv == 2) return launch_decode_t<E, D, 0, 2>(a, dp);
     return launch_decode_t<E, D, 0, 4>(a, dp);
+  }
+  if (a.so_kind == 3) {                       // compressed storage
+    if (hv == 1) return launch_decode_t<E, D, 3, 1>(a, dp);
+    if (hv == 2) return launch_decode_t<E, D, 3, 2>(a, dp);
+    return launch_decode_t<E, D, 3, 4>(a, dp);
   }
   if (hv == 1) return launch_decode_t<E, D, 1, 1>(a, dp);
   if (hv == 2) return launch_decode_t<E, D, 1, 2>(a, dp);

@@ -17,6 +17,7 @@
 // largest-magnitude entry is positive.
 #include "cobs_device.h"
 #include "cobs_launch.h"
+#include "score_common.h"
 
 namespace cobs {
 
@@ -39,12 +40,75 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   return t;
 }
 
+// FP4 E2M1 code of y (a value already divided by its group scale): the nearest of
+// 0, .5, 1, 1.5, 2, 3, 4, 6 (ties to the even code, saturating at 6), sign in bit 3
+// (none for zero).  The code is the number of midpoints between neighbouring
+// magnitudes that lie below |y|, moved up at an exact midpoint to an even code.
+__device__ __forceinline__ uint32_t e2m1_code(double y) {
+  const double a = fabs(y);
+  const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  uint32_t c = 0;
+  bool tie = false;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    c += (mid[i] < a) ? 1u : 0u;
+    tie |= (mid[i] == a);
+  }
+  if (tie && (c & 1u)) ++c;
+  return (c != 0u && y < 0.0) ? (c | 8u) : c;
+}
+
+// The compressed record of one block from its rank scaled eigenvectors (fp64):
+// per vector d/2 bytes of codes, then per vector d/32 exponent bytes, then zero
+// padding to 16 bytes.  Each group of 32 entries shares the exponent
+// e = floor(log2 max|v|) - 2 (stored as e + 127, 0 for an all-zero group), and
+// entry 16u + 4g + c sits at nibble (g * d/16 + u) * 4 + c of its vector, low
+// nibble first, so that a scoring lane reads its columns as one contiguous run.
+template <int D>
+__device__ void quantize_record(const double (*vout)[D], int (*gexp)[D / 32], uint8_t* rec, int rank, int tid) {
+  constexpr int NG = D / 32;
+  for (int idx = tid; idx < rank * NG; idx += kLrThreads) {
+    const int i = idx / NG, q = idx % NG;
+    double amax = 0.0;
+    for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs(vout[i][32 * q + j]));
+    int e = -127;
+    if (amax > 0.0) {
+      int ex;
+      frexp(amax, &ex);                    // amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+      e = max(-127, min(127, ex - 3));
+    }
+    gexp[i][q] = e;
+  }
+  __syncthreads();
+  const int code_bytes = rank * (D / 2);
+  const int total = (int)fp4_record_bytes_dev(rank, D);
+  for (int idx = tid; idx < total; idx += kLrThreads) {
+    uint32_t byte = 0;
+    if (idx < code_bytes) {
+      const int i = idx / (D / 2), bb = idx % (D / 2);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int P = 2 * bb + h;                       // nibble position within the vector
+        const int g = P / (D / 4), kk = P % (D / 4);
+        const int entry = 16 * (kk / 4) + 4 * g + (kk % 4);
+        const double y = ldexp(vout[i][entry], -gexp[i][entry / 32]);
+        byte |= e2m1_code(y) << (4 * h);
+      }
+    } else if (idx < code_bytes + rank * NG) {
+      const int k = idx - code_bytes;
+      byte = (uint32_t)(gexp[k / NG][k % NG] + 127);
+    }
+    rec[idx] = (uint8_t)byte;
+  }
+  __syncthreads();
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __restrict__ seq_lens,
                                                               const int32_t* __restrict__ old_lens, int max_len,
                                                               int nb_max, int rank,
                                                               const typename E::storage* __restrict__ K,
-                                                              float* __restrict__ lowrank) {
+                                                              void* __restrict__ lowrank, int fp4) {
   __shared__ double A[kN][kN + 1];      // Gram matrix, diagonalised in place (+1: bank spread)
   // the block's keys (fp32, exact for bf16) until G is built, then the rotations
   __shared__ union { float k[kN][D + 1]; double v[kN][kN + 1]; } kv;
@@ -55,6 +119,8 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
   __shared__ int order[8];
   __shared__ double lam_sel[8];
   __shared__ double vout[8][D];
+  __shared__ int gexp[8][D / 32];
+  __shared__ __align__(16) uint8_t rec[8 * (D / 2 + D / 32) + 16];
   auto& Vm = kv.v;
 
   const int tid = threadIdx.x;
@@ -227,8 +293,16 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
     }
   }
   __syncthreads();
-  float* dst = lowrank + ((unit * (size_t)nb_max + b) * rank) * D;
-  for (int idx = tid; idx < rank * D; idx += kLrThreads) dst[idx] = (float)vout[idx / D][idx % D];
+  if (fp4) {
+    quantize_record<D>(vout, gexp, rec, rank, tid);
+    const int words = (int)(fp4_record_bytes_dev(rank, D) / 4);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(lowrank) +
+                                                (unit * (size_t)nb_max + b) * fp4_record_bytes_dev(rank, D));
+    for (int w = tid; w < words; w += kLrThreads) dst[w] = reinterpret_cast<const uint32_t*>(rec)[w];
+  } else {
+    float* dst = static_cast<float*>(lowrank) + ((unit * (size_t)nb_max + b) * rank) * D;
+    for (int idx = tid; idx < rank * D; idx += kLrThreads) dst[idx] = (float)vout[idx / D][idx % D];
+  }
   __syncthreads();                         // shared arrays are reused by the next block
   }
 }
@@ -237,7 +311,7 @@ template <typename E, int D>
 static hipError_t launch_lr(const BuildArgs& a) {
   dim3 grid(a.old_lens ? a.touch_blocks : a.nb_max, a.hkv, a.batch);
   hipLaunchKernelGGL((k_build_lowrank<E, D>), grid, dim3(kLrThreads), 0, a.stream, a.seq_lens, a.old_lens,
-                     a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank);
+                     a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank, a.fp4 ? 1 : 0);
   return hipGetLastError();
 }
 

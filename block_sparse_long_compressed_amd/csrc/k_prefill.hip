@@ -30,7 +30,7 @@ struct PsParams {
   float alpha, scale;
   const int32_t* seq_lens;          // null: every sequence has length L_fixed
   const void* Q;
-  const float *mu, *so;
+  const void *mu, *so;
   int32_t* sel;
   float* sel_score;
 };
@@ -62,10 +62,9 @@ __global__ __launch_bounds__(256) void k_prefill_select(PsParams p) {
   const bool use_quad = p.alpha != 0.f;
   auto scores = [&](int tile) -> f32x4 {
     const int brow = min(tile * 16 + n, ncand - 1);
-    f32x4 s = score_tile<D, KIND>(p.mu + (sum_base + brow) * D,
-                                  KIND == 0 ? p.so + (sum_base + brow) * D
-                                            : p.so + (sum_base + brow) * (size_t)(p.rank * D),
-                                  p.rank, g, use_quad, p.alpha, wlin);
+    const void *mr, *vr;
+    summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, mr, vr);
+    f32x4 s = score_tile<D, KIND>(mr, vr, p.rank, g, use_quad, p.alpha, wlin);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = tile * 16 + 4 * g + i;
@@ -201,24 +200,22 @@ __global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
   const int G = p.group;
   const size_t unit = ((size_t)seq * p.tokens + tok) * p.hkv + head;
   const size_t sum_base = ((size_t)seq * p.hkv + head) * p.nb_max;
-  const size_t so_row = KIND == 0 ? (size_t)D : (size_t)p.rank * D;
   const int tiles = (ncand + 15) / 16;
   const bool use_quad = p.alpha != 0.f;
-  auto rows_of = [&](int tile, const float*& mr, const float*& vr) {
+  auto rows_of = [&](int tile, const void*& mr, const void*& vr) {
     const int brow = min(tile * 16 + n, ncand - 1);
-    mr = p.mu + (sum_base + brow) * D;
-    vr = p.so + (sum_base + brow) * so_row;
+    summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, mr, vr);
   };
 
   // ---- scores of tiles wave, wave+4, ... (summary rows requested before the query)
   SumTile<D, KIND> st[RING];
-  const float* vrow[RING];
+  const void* vrow[RING];
 #pragma unroll
   for (int r = 0; r < RING; ++r) {
     vrow[r] = nullptr;
     const int tile = wave + 4 * r;
     if (tile < tiles) {
-      const float* mrow;
+      const void* mrow;
       rows_of(tile, mrow, vrow[r]);
       sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
     }
@@ -235,7 +232,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
       if (tile < tiles) {
         const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
         if (tile + 4 * RING < tiles) {
-          const float* mrow;
+          const void* mrow;
           rows_of(tile + 4 * RING, mrow, vrow[r]);
           sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
         }
@@ -424,18 +421,21 @@ static hipError_t launch_ps(const PrefillArgs& a, const PsParams& sp) {
   return hipGetLastError();
 }
 
+template <typename E, int D>
+static hipError_t launch_ps_e(const PrefillArgs& a, const PsParams& sp) {
+  if (a.so_kind == 0) return launch_ps<E, D, 0>(a, sp);
+  if (a.so_kind == 3) return launch_ps<E, D, 3>(a, sp);
+  return launch_ps<E, D, 1>(a, sp);
+}
+
 hipError_t launch_prefill_select(const PrefillArgs& a) {
   PsParams sp;
   sp.tokens = a.tokens; sp.hkv = a.hkv; sp.group = a.group; sp.max_len = a.max_len; sp.nb_max = a.nb_max;
   sp.nb_pad = (a.nb_max + 15) / 16 * 16; sp.top_k = a.top_k; sp.rank = a.rank; sp.q_pos0 = a.q_pos0;
   sp.L_fixed = a.max_len; sp.alpha = a.alpha; sp.scale = a.scale; sp.seq_lens = a.seq_lens; sp.Q = a.Q;
   sp.mu = a.mu; sp.so = a.so; sp.sel = a.sel; sp.sel_score = a.sel_score;
-  if (a.bf16) {
-    if (a.head_dim == 128) return a.so_kind == 0 ? launch_ps<EltBF16, 128, 0>(a, sp) : launch_ps<EltBF16, 128, 1>(a, sp);
-    return a.so_kind == 0 ? launch_ps<EltBF16, 64, 0>(a, sp) : launch_ps<EltBF16, 64, 1>(a, sp);
-  }
-  if (a.head_dim == 128) return a.so_kind == 0 ? launch_ps<EltF32, 128, 0>(a, sp) : launch_ps<EltF32, 128, 1>(a, sp);
-  return a.so_kind == 0 ? launch_ps<EltF32, 64, 0>(a, sp) : launch_ps<EltF32, 64, 1>(a, sp);
+  if (a.bf16) return a.head_dim == 128 ? launch_ps_e<EltBF16, 128>(a, sp) : launch_ps_e<EltBF16, 64>(a, sp);
+  return a.head_dim == 128 ? launch_ps_e<EltF32, 128>(a, sp) : launch_ps_e<EltF32, 64>(a, sp);
 }
 
 template <typename E, int D>

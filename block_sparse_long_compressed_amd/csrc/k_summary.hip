@@ -52,13 +52,31 @@ __device__ __forceinline__ void store_pooled(typename E::storage* dst, const flo
   }
 }
 
+// Store this lane's EPL mean columns: fp32, or rounded to bf16 (nearest, ties to
+// even) for the compressed storage.
+template <int EPL>
+__device__ __forceinline__ void store_mean(void* mu_u, bool mu_bf16, int b, int D, int col, const float* mean) {
+  if (mu_bf16) {
+    uint16_t* dst = static_cast<uint16_t*>(mu_u) + (size_t)b * D + col;
+    uint32_t w[EPL / 2];
+#pragma unroll
+    for (int e = 0; e < EPL / 2; ++e) w[e] = f32_to_bf16_bits(mean[2 * e]) | (f32_to_bf16_bits(mean[2 * e + 1]) << 16);
+    if constexpr (EPL == 8) st16(dst, u32x4{w[0], w[1], w[2], w[3]});
+    else *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+  } else {
+    float* dst = static_cast<float*>(mu_u) + (size_t)b * D + col;
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]});
+  }
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(64) void k_build_diag(
     const int32_t* __restrict__ seq_lens, int max_len, int nb_max, int nc_max,
     const typename E::storage* __restrict__ K, const typename E::storage* __restrict__ V,
-    float* __restrict__ mu, float* __restrict__ var,
+    void* __restrict__ mu, float* __restrict__ var,
     typename E::storage* __restrict__ kc, typename E::storage* __restrict__ vc,
-    int blocks_per_wave, int want_var, int want_pool) {
+    int blocks_per_wave, int want_var, int want_pool, int mu_bf16) {
   using T = RowTiling<E, D>;
   constexpr int LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad, NL = T::kLoads, EPL = T::kEpl;
   const int lane = threadIdx.x;
@@ -76,7 +94,8 @@ __global__ __launch_bounds__(64) void k_build_diag(
   const size_t unit = (size_t)seq * hkv + head;
   const typename E::storage* Ku = K + unit * (size_t)max_len * D;
   const typename E::storage* Vu = V + unit * (size_t)max_len * D;
-  float* mu_u = mu + unit * (size_t)nb_max * D;
+  void* mu_u = mu_bf16 ? (void*)(static_cast<uint16_t*>(mu) + unit * (size_t)nb_max * D)
+                       : (void*)(static_cast<float*>(mu) + unit * (size_t)nb_max * D);
   float* var_u = var ? var + unit * (size_t)nb_max * D : nullptr;
   typename E::storage* kc_u = want_pool ? kc + unit * (size_t)nc_max * D : nullptr;
   typename E::storage* vc_u = want_pool ? vc + unit * (size_t)nc_max * D : nullptr;
@@ -108,11 +127,7 @@ __global__ __launch_bounds__(64) void k_build_diag(
     const float inv_n = 1.0f / (float)nrows;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) mean[e] = reduce_rows<LPR>(sum[e]) * inv_n;
-    if (rg == 0) {
-      float* dst = mu_u + (size_t)b * D + cc * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]});
-    }
+    if (rg == 0) store_mean<EPL>(mu_u, mu_bf16 != 0, b, D, cc * EPL, mean);
     if (want_var) {
       float sq[EPL];
 #pragma unroll
@@ -212,8 +227,8 @@ template <typename E, int D>
 __global__ __launch_bounds__(64) void k_append_diag(
     const int32_t* __restrict__ old_lens, const int32_t* __restrict__ new_lens, int max_len, int nb_max,
     int nc_max, const typename E::storage* __restrict__ K, const typename E::storage* __restrict__ V,
-    float* __restrict__ mu, float* __restrict__ var, typename E::storage* __restrict__ kc,
-    typename E::storage* __restrict__ vc, int want_pool) {
+    void* __restrict__ mu, float* __restrict__ var, typename E::storage* __restrict__ kc,
+    typename E::storage* __restrict__ vc, int want_pool, int mu_bf16) {
   using T = RowTiling<E, D>;
   constexpr int LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad, NL = T::kLoads, EPL = T::kEpl;
   const int lane = threadIdx.x;
@@ -224,7 +239,8 @@ __global__ __launch_bounds__(64) void k_append_diag(
   const size_t unit = (size_t)seq * hkv + head;
   const typename E::storage* Ku = K + unit * (size_t)max_len * D;
   const typename E::storage* Vu = V + unit * (size_t)max_len * D;
-  float* mu_u = mu + unit * (size_t)nb_max * D;
+  void* mu_u = mu_bf16 ? (void*)(static_cast<uint16_t*>(mu) + unit * (size_t)nb_max * D)
+                       : (void*)(static_cast<float*>(mu) + unit * (size_t)nb_max * D);
   float* var_u = var ? var + unit * (size_t)nb_max * D : nullptr;
 #pragma unroll 1
   for (int b = L0 / kBlock + blockIdx.x; b * kBlock < L; b += gridDim.x) {
@@ -246,11 +262,7 @@ __global__ __launch_bounds__(64) void k_append_diag(
     const float inv_n = 1.0f / (float)nrows;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) mean[e] = reduce_rows<LPR>(sum[e]) * inv_n;
-    if (rg == 0) {
-      float* dst = mu_u + (size_t)b * D + cc * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{mean[e], mean[e + 1], mean[e + 2], mean[e + 3]});
-    }
+    if (rg == 0) store_mean<EPL>(mu_u, mu_bf16 != 0, b, D, cc * EPL, mean);
     if (var_u) {
       float sq[EPL];
 #pragma unroll
@@ -314,7 +326,7 @@ static hipError_t launch_diag(const BuildArgs& a) {
                      a.seq_lens, a.max_len, a.nb_max, a.nc_max,
                      (const typename E::storage*)a.K, (const typename E::storage*)a.V,
                      a.mu, a.var, (typename E::storage*)a.kc, (typename E::storage*)a.vc,
-                     bpw, a.var != nullptr ? 1 : 0, a.kc != nullptr ? 1 : 0);
+                     bpw, a.var != nullptr ? 1 : 0, a.kc != nullptr ? 1 : 0, a.fp4 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -323,7 +335,8 @@ static hipError_t launch_append(const BuildArgs& a) {
   dim3 grid(a.touch_blocks, a.hkv, a.batch);
   hipLaunchKernelGGL((k_append_diag<E, D>), grid, dim3(64), 0, a.stream, a.old_lens, a.seq_lens, a.max_len,
                      a.nb_max, a.nc_max, (const typename E::storage*)a.K, (const typename E::storage*)a.V,
-                     a.mu, a.var, (typename E::storage*)a.kc, (typename E::storage*)a.vc, a.kc != nullptr ? 1 : 0);
+                     a.mu, a.var, (typename E::storage*)a.kc, (typename E::storage*)a.vc, a.kc != nullptr ? 1 : 0,
+                     a.fp4 ? 1 : 0);
   return hipGetLastError();
 }
 

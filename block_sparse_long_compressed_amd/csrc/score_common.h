@@ -45,55 +45,131 @@ __device__ __forceinline__ void score_weights(const void* Q, size_t q_base, int 
   }
 }
 
+// Score kinds: 0 diagonal, 1 rank-r fp32, 2 exact masses (no summaries), 3 rank-r
+// in the compressed storage (bf16 mean; FP4 E2M1 vectors with one E8M0 exponent
+// per 32 entries, each lane's 32 codes contiguous: entry 16u + 4g + c at nibble
+// (g * d/16 + u) * 4 + c).
+
+// Bytes of one block's compressed record: codes, exponents, padding to 16.
+__host__ __device__ constexpr size_t fp4_record_bytes_dev(int rank, int d) {
+  return ((size_t)rank * (d / 2 + d / 32) + 15) / 16 * 16;
+}
+
+// Summary rows of block row `row` (mean, second-order) for a score kind.
+template <int D, int KIND>
+__device__ __forceinline__ void summary_rows(const void* mu, const void* so, size_t row, int rank,
+                                             const void*& mr, const void*& vr) {
+  if constexpr (KIND == 3) {
+    mr = static_cast<const uint16_t*>(mu) + row * D;
+    vr = static_cast<const uint8_t*>(so) + row * fp4_record_bytes_dev(rank, D);
+  } else {
+    mr = static_cast<const float*>(mu) + row * D;
+    vr = static_cast<const float*>(so) + row * (KIND == 0 ? (size_t)D : (size_t)rank * D);
+  }
+}
+
 // Summary rows of one 16-block tile held in registers: this lane's mean columns
 // and its second-order columns (the diagonal, or the first kRankGroup scaled
-// eigenvectors; further groups are fetched while scoring).
+// eigenvectors, further groups fetched while scoring; for the compressed storage
+// the bf16 mean and the first kRankGroup vectors' FP4 codes and exponents).
 constexpr int kRankGroup = 4;
 
 template <int D, int KIND>
 struct SumTile {
-  f32x4 m4[D / 16];
-  f32x4 v4[KIND == 0 ? 1 : kRankGroup][D / 16];
+  f32x4 m4[KIND == 3 ? 1 : D / 16];
+  f32x4 v4[KIND == 1 ? kRankGroup : 1][KIND == 3 ? 1 : D / 16];
+  uint2 mb[KIND == 3 ? D / 16 : 1];          // bf16 mean columns 16u + 4g .. +3
+  u32x4 code[KIND == 3 ? kRankGroup : 1];    // this lane's D/4 codes of each vector of the group
+  uint32_t ex[KIND == 3 ? kRankGroup : 1];   // the vector's D/32 exponent bytes
 };
 
 template <int D, int KIND>
-__device__ __forceinline__ void sum_tile_load_group(const float* vrow, int r0, int rank, int g, SumTile<D, KIND>& t) {
+__device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, int rank, int g, SumTile<D, KIND>& t) {
+  if constexpr (KIND == 3) {
+    const uint8_t* rec = static_cast<const uint8_t*>(vrow);
 #pragma unroll
-  for (int rr = 0; rr < kRankGroup; ++rr) {
-    if (r0 + rr < rank) {
+    for (int rr = 0; rr < kRankGroup; ++rr) {
+      const int r = r0 + rr;
+      if (r < rank) {
+        const uint8_t* cp = rec + r * (D / 2) + g * (D / 8);
+        if constexpr (D == 128) {
+          t.code[rr] = *reinterpret_cast<const u32x4*>(cp);
+          t.ex[rr] = *reinterpret_cast<const uint32_t*>(rec + rank * (D / 2) + r * (D / 32));
+        } else {
+          const uint2 c2 = *reinterpret_cast<const uint2*>(cp);
+          t.code[rr] = u32x4{c2.x, c2.y, 0u, 0u};
+          t.ex[rr] = *reinterpret_cast<const uint16_t*>(rec + rank * (D / 2) + r * (D / 32));
+        }
+      }
+    }
+  } else {
+    const float* vr = static_cast<const float*>(vrow);
 #pragma unroll
-      for (int u = 0; u < D / 16; ++u) t.v4[rr][u] = ld_f32x4(vrow + (r0 + rr) * D + 16 * u + 4 * g);
+    for (int rr = 0; rr < kRankGroup; ++rr) {
+      if (r0 + rr < rank) {
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) t.v4[rr][u] = ld_f32x4(vr + (r0 + rr) * D + 16 * u + 4 * g);
+      }
     }
   }
 }
 
 // Issue the loads of one tile (mrow / vrow: this lane's block row).
 template <int D, int KIND>
-__device__ __forceinline__ void sum_tile_load(const float* mrow, const float* vrow, int rank, int g, bool use_quad,
+__device__ __forceinline__ void sum_tile_load(const void* mrow, const void* vrow, int rank, int g, bool use_quad,
                                               SumTile<D, KIND>& t) {
+  if constexpr (KIND == 3) {
+    const uint16_t* mr = static_cast<const uint16_t*>(mrow);
 #pragma unroll
-  for (int u = 0; u < D / 16; ++u) t.m4[u] = ld_f32x4(mrow + 16 * u + 4 * g);
-  if (use_quad) {
-    if constexpr (KIND == 0) {
+    for (int u = 0; u < D / 16; ++u) t.mb[u] = *reinterpret_cast<const uint2*>(mr + 16 * u + 4 * g);
+    if (use_quad) sum_tile_load_group<D, KIND>(vrow, 0, rank, g, t);
+  } else {
+    const float* mr = static_cast<const float*>(mrow);
 #pragma unroll
-      for (int u = 0; u < D / 16; ++u) t.v4[0][u] = ld_f32x4(vrow + 16 * u + 4 * g);
-    } else {
-      sum_tile_load_group<D, KIND>(vrow, 0, rank, g, t);
+    for (int u = 0; u < D / 16; ++u) t.m4[u] = ld_f32x4(mr + 16 * u + 4 * g);
+    if (use_quad) {
+      if constexpr (KIND == 0) {
+        const float* vr = static_cast<const float*>(vrow);
+#pragma unroll
+        for (int u = 0; u < D / 16; ++u) t.v4[0][u] = ld_f32x4(vr + 16 * u + 4 * g);
+      } else {
+        sum_tile_load_group<D, KIND>(vrow, 0, rank, g, t);
+      }
     }
   }
 }
 
+// Magnitude-and-sign value of an FP4 E2M1 code (sign in bit 3): 0, .5, 1, 1.5,
+// 2, 3, 4, 6, built directly as fp32 bits.
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+  const uint32_t m3 = nib & 7u;
+  uint32_t bits = (m3 >= 2u) ? (((m3 >> 1) + 126u) << 23) | ((m3 & 1u) << 22) : (m3 ? 0x3F000000u : 0u);
+  return __uint_as_float(bits | ((nib & 8u) << 28));
+}
+
+// 2^(byte - 127) of an E8M0 exponent byte (byte 0, an all-zero group, gives 0).
+__device__ __forceinline__ float e8m0_value(uint32_t byte) { return __uint_as_float(byte << 23); }
+
 // Scores (without ln n_b) of the tile's 16 blocks for the group's heads from the
 // loaded rows.  Linear and quadratic terms are independent MFMA chains.
 template <int D, int KIND>
-__device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const float* vrow, int rank, int g, bool use_quad,
+__device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void* vrow, int rank, int g, bool use_quad,
                                                 float alpha, const float (&wlin)[D / 16][4]) {
   constexpr int NU = D / 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(t.m4[u][c], wlin[u][c], acc);
+    for (int c = 0; c < 4; ++c) {
+      float m;
+      if constexpr (KIND == 3) {
+        const uint32_t w = (c < 2) ? t.mb[u].x : t.mb[u].y;
+        m = (c & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+      } else {
+        m = t.m4[u][c];
+      }
+      acc = mfma_f32_16x16x4(m, wlin[u][c], acc);
+    }
   }
   if (!use_quad) return acc;
   if constexpr (KIND == 0) {
@@ -103,6 +179,40 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const float
       for (int c = 0; c < 4; ++c) {
         const float w = wlin[u][c];
         acc2 = mfma_f32_16x16x4(t.v4[0][u][c], 0.5f * alpha * w * w, acc2);   // alpha/2 scale^2 q^2
+      }
+    }
+  } else if constexpr (KIND == 3) {
+    // (v_i . q)^2 with v_i decoded on the fly: entry 16u + 4g + c is nibble u*4 + c of
+    // this lane's codes, scaled by the exponent of group u/2 of this lane's block (the
+    // scale must be applied on the A side: an output row belongs to another lane's block)
+    constexpr int NG = D / 32;
+#pragma unroll 1
+    for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
+      if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, g, t);
+#pragma unroll
+      for (int rr = 0; rr < kRankGroup; ++rr) {
+        if (r0 + rr < rank) {
+          float sc[NG];
+#pragma unroll
+          for (int q = 0; q < NG; ++q) sc[q] = e8m0_value((t.ex[rr] >> (8 * q)) & 0xFFu);
+          f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int k = u * 4 + c;
+              const uint32_t nib = (t.code[rr][k >> 3] >> (4 * (k & 7))) & 0xFu;
+              const float v = e2m1_value(nib) * sc[u >> 1];
+              if (u & 1) pr2 = mfma_f32_16x16x4(v, wlin[u][c], pr2);
+              else pr = mfma_f32_16x16x4(v, wlin[u][c], pr);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dd = pr[i] + pr2[i];
+            acc2[i] += 0.5f * alpha * dd * dd;
+          }
+        }
       }
     }
   } else {
@@ -137,7 +247,7 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const float
 
 // Load and score one tile in one step.
 template <int D, int KIND>
-__device__ __forceinline__ f32x4 score_tile(const float* mrow, const float* vrow, int rank, int g, bool use_quad,
+__device__ __forceinline__ f32x4 score_tile(const void* mrow, const void* vrow, int rank, int g, bool use_quad,
                                             float alpha, const float (&wlin)[D / 16][4]) {
   SumTile<D, KIND> t;
   sum_tile_load<D, KIND>(mrow, vrow, rank, g, use_quad, t);

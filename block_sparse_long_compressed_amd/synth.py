@@ -47,8 +47,8 @@ class Workload:
     window: int             # 0 = no sliding-window branch
     cmp_len: int            # 0 = no compressed branch
     cmp_stride: int
-    so_kind: str            # 'diag' | 'lowrank'
-    rank: int               # eigenpairs kept when so_kind == 'lowrank'
+    so_kind: str            # 'diag' | 'lowrank' | 'lowrank_fp4' (bf16 mean, MX FP4 vectors)
+    rank: int               # eigenpairs kept by the low-rank kinds
     alpha: float            # weight of the second-order term
     dtype: str              # 'bf16' | 'f32'
     needles: int            # planted needle keys per (sequence, kv-head)
@@ -84,6 +84,9 @@ WORKLOADS = {
     # batch 8, 128k keys, 32 q-heads / 8 kv-heads, top-32, window 1024, rank-4 summaries.
     "decode_b8_L128k_rank4": Workload("decode_b8_L128k_rank4", 8, 131072, 131072, 32, 8, 128, 32,
                                       1024, 32, 16, "lowrank", 4, 1.0, "bf16", 16),
+    # the same with the compressed summary storage (bf16 mean, MX FP4 eigenvectors).
+    "decode_b8_L128k_rank4_fp4": Workload("decode_b8_L128k_rank4_fp4", 8, 131072, 131072, 32, 8, 128,
+                                          32, 1024, 32, 16, "lowrank_fp4", 4, 1.0, "bf16", 16),
 }
 
 

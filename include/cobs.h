@@ -67,7 +67,11 @@ typedef enum cobs_status {
 } cobs_status;
 
 typedef enum cobs_dtype { COBS_BF16 = 0, COBS_F32 = 1 } cobs_dtype;
-typedef enum cobs_so_kind { COBS_SO_DIAG = 0, COBS_SO_LOWRANK = 1 } cobs_so_kind;
+/* Second-order channel of the block summaries (COBS Technisches Resuemee 2.3):
+ * the diagonal of the block's key covariance, its top-r eigenvectors scaled by
+ * sqrt(eigenvalue) in fp32, or the same vectors in the compressed storage of 2.3
+ * (bf16 mean, FP4 eigenvectors; see cobs_summary_shapes for the layout). */
+typedef enum cobs_so_kind { COBS_SO_DIAG = 0, COBS_SO_LOWRANK = 1, COBS_SO_LOWRANK_FP4 = 2 } cobs_so_kind;
 
 /* Method parameters.  Shared by every call of one attention layer. */
 typedef struct cobs_params {
@@ -80,7 +84,7 @@ typedef struct cobs_params {
   int32_t cmp_len;      /* 0 disables the compressed branch; otherwise 32 */
   int32_t cmp_stride;   /* 16 (required when cmp_len == 32) */
   int32_t so_kind;      /* cobs_so_kind */
-  int32_t rank;         /* r in [1, 8] for COBS_SO_LOWRANK; ignored for diag */
+  int32_t rank;         /* r in [1, 8] for the low-rank kinds; ignored for diag */
   float alpha;          /* >= 0; 0 = first-order (mean-pool) selector */
   float scale;          /* logit scale > 0; 0 selects 1/sqrt(head_dim) */
   int32_t kv_dtype;     /* cobs_dtype of Q, K, V and the pooled tokens */
@@ -97,6 +101,16 @@ cobs_status cobs_validate_params(const cobs_params* p);
  * so (lowrank) [batch][H_kv][NB][rank][d] f32, pooled tokens kc/vc
  * [batch][H_kv][NC][d] of kv_dtype, with NB = ceil(max_len/64) and
  * NC = (max_len-32)/16 + 1 (0 if max_len < 32 or the branch is off).
+ * COBS_SO_LOWRANK_FP4: mu [batch][H_kv][NB][d] bf16 (nearest, ties to even) and
+ * so [batch][H_kv][NB] records of R = round_up(rank * (d/2 + d/32), 16) bytes: for
+ * each vector i, d/2 bytes of FP4 E2M1 codes (two per byte, low nibble first;
+ * entry 16u + 4g + c at nibble (g * d/16 + u) * 4 + c), then for each vector
+ * d/32 bytes of shared exponents (E8M0, 2^(byte-127) scales entries [32j, 32j+32))
+ * and zero padding.  A group's exponent is floor(log2 max|v|) - 2, clamped to
+ * [-127, 127] (byte 0 for an all-zero group, read as scale 0); each entry is the
+ * nearest of +-{0, .5, 1, 1.5, 2, 3, 4, 6} times the scale, ties to the even code,
+ * saturating at 6 (the OCP microscaling FP4 format).  The mu and so pointers of the
+ * other calls take these bytes.
  * Each out-pointer may be NULL.  Returns COBS_ERR_INVALID_ARG on bad input. */
 cobs_status cobs_summary_shapes(const cobs_params* p, int32_t batch, int32_t max_len,
                                 int64_t* nb_max, int64_t* nc_max,
@@ -119,7 +133,7 @@ size_t cobs_workspace_bytes(const cobs_params* p, int32_t batch, int32_t max_len
  *             fp32 mean). */
 cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t max_len,
                                  const int32_t* seq_lens, const void* K, const void* V,
-                                 float* mu, float* so, void* kc, void* vc, void* stream);
+                                 void* mu, void* so, void* kc, void* vc, void* stream);
 
 /* Incremental summary update after tokens are appended to the cache (the summaries
  * stay compact and query-independent as the prefix grows: COBS Technisches
@@ -137,7 +151,7 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
  * Errors as for cobs_build_summaries; INVALID_ARG also when max_append < 1. */
 cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t max_len,
                                   const int32_t* old_lens, const int32_t* new_lens, int32_t max_append,
-                                  const void* K, const void* V, float* mu, float* so, void* kc, void* vc,
+                                  const void* K, const void* V, void* mu, void* so, void* kc, void* vc,
                                   void* stream);
 
 /* Block scoring, group aggregation and top-k (COBS 2.1-2.3; skill card "Method").
@@ -153,7 +167,7 @@ cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t m
  *   ws         workspace of at least cobs_workspace_bytes(p, batch, max_len, n_q_tokens) */
 cobs_status cobs_select_topk(const cobs_params* p, int32_t batch, int32_t max_len,
                              const int32_t* seq_lens, int32_t n_q_tokens, int32_t q_pos0,
-                             const void* Q, const float* mu, const float* so,
+                             const void* Q, const void* mu, const void* so,
                              int32_t* sel, float* sel_score,
                              void* ws, size_t ws_bytes, void* stream);
 
@@ -184,7 +198,7 @@ cobs_status cobs_select_topk_exact(const cobs_params* p, int32_t batch, int32_t 
 cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t max_len,
                                     const int32_t* seq_lens, const void* Q,
                                     const void* K, const void* V,
-                                    const float* mu, const float* so,
+                                    const void* mu, const void* so,
                                     const void* kc, const void* vc, const float* gates,
                                     const int32_t* sel_in, int32_t* sel_out, float* out,
                                     void* ws, size_t ws_bytes, void* stream);
@@ -203,7 +217,7 @@ cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t
  * Requires 0 <= q_pos0 and q_pos0 + n_q_tokens <= seq_len. */
 cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int32_t n_q_tokens,
                                      int32_t q_pos0, const void* Q, const void* K, const void* V,
-                                     const float* mu, const float* so,
+                                     const void* mu, const void* so,
                                      const void* kc, const void* vc, const float* gates,
                                      int32_t* sel_out, float* out,
                                      void* ws, size_t ws_bytes, void* stream);

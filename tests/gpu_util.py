@@ -8,13 +8,14 @@ import torch
 from block_sparse_long_compressed_amd import binding as B
 
 GAP = 1e-3          # score gap (natural-log units) below which several selections are correct
+SO_KINDS = {"diag": B.COBS_SO_DIAG, "lowrank": B.COBS_SO_LOWRANK, "lowrank_fp4": B.COBS_SO_LOWRANK_FP4}
 
 
 def params_for(w, alpha=None, top_k=None):
     return B.make_params(w.head_dim, w.n_q_heads, w.n_kv_heads, w.top_k if top_k is None else top_k,
                          window=w.window, cmp_len=w.cmp_len, cmp_stride=w.cmp_stride,
-                         so_kind=B.COBS_SO_LOWRANK if w.so_kind == "lowrank" else B.COBS_SO_DIAG,
-                         rank=w.rank if w.so_kind == "lowrank" else 0,
+                         so_kind=SO_KINDS[w.so_kind],
+                         rank=0 if w.so_kind == "diag" else w.rank,
                          alpha=w.alpha if alpha is None else alpha,
                          kv_dtype=B.COBS_BF16 if w.dtype == "bf16" else B.COBS_F32)
 

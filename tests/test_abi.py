@@ -54,9 +54,10 @@ def test_invalid_params_rejected(field, value, status):
     assert B.cobs_workspace_bytes(p, 1, 1024) == 0
 
 
-def test_lowrank_rank_bounds():
+@pytest.mark.parametrize("kind", [B.COBS_SO_LOWRANK, B.COBS_SO_LOWRANK_FP4])
+def test_lowrank_rank_bounds(kind):
     p = good()
-    p.so_kind = B.COBS_SO_LOWRANK
+    p.so_kind = kind
     for r, st in ((0, B.COBS_ERR_INVALID_ARG), (1, B.COBS_OK), (8, B.COBS_OK), (9, B.COBS_ERR_INVALID_ARG)):
         p.rank = r
         assert B.cobs_validate_params(p) == st
@@ -74,6 +75,15 @@ def test_summary_shapes():
     assert B.cobs_summary_shapes(p, 1, 20)["nc_max"] == 0
     p.so_kind, p.rank = B.COBS_SO_LOWRANK, 4
     assert B.cobs_summary_shapes(p, 1, 128)["so_bytes"] == 4 * 2 * 4 * 128 * 4
+
+
+@pytest.mark.parametrize("d,rank,record", [(128, 4, 272), (128, 1, 80), (128, 8, 544), (64, 3, 112), (64, 1, 48)])
+def test_summary_shapes_fp4(d, rank, record):
+    # per vector d/2 code bytes and d/32 exponent bytes; the record is padded to 16
+    p = B.make_params(d, 8, 2, 8, so_kind=B.COBS_SO_LOWRANK_FP4, rank=rank)
+    sh = B.cobs_summary_shapes(p, 3, 1000)
+    assert sh["mu_bytes"] == 3 * 2 * 16 * d * 2                 # bf16 means
+    assert sh["so_bytes"] == 3 * 2 * 16 * record
 
 
 def test_workspace_grows_with_problem_and_rejects_bad_sizes():

@@ -37,7 +37,8 @@ def run_update(w, new_lens, old_lens, max_append):
     s = B.alloc_summaries(p, w.batch, w.max_len)
     for t in (s["mu"], s["so"], s["kc"], s["vc"]):
         if t is not None:
-            t.fill_(float("nan"))                   # anything the update must write is visibly wrong
+            # anything the update must write is visibly wrong
+            t.fill_(float("nan") if t.is_floating_point() else 0xA5)
     old = torch.tensor(old_lens, dtype=torch.int32, device="cuda")
     new = torch.tensor(new_lens, dtype=torch.int32, device="cuda")
     if min(old_lens) > 0:
