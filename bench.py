@@ -400,6 +400,34 @@ def bench_recall(args):
         tot = sum(int((ex[b, h] >= 0).sum()) for b in range(w.batch) for h in range(w.n_kv_heads))
         res["recall"][str(alpha)] = hit / max(tot, 1)
         res[f"us_cumulant_selection_alpha{alpha}"] = t * 1e6
+    if w.so_kind in ("lowrank", "lowrank_fp4"):
+        # the two storages of the rank-r channel: fp32 vectors against bf16 mean + MX FP4
+        # vectors, at the workload's alpha: agreement of the selections, recall of each
+        # against the exact-mass selection, summary bytes per block
+        sels = {}
+        for kind in ("lowrank", "lowrank_fp4"):
+            wk = w.scaled(so_kind=kind)
+            pk = U.params_for(wk)
+            s = U.build(pk, g)
+            sel = torch.empty_like(exact)
+            B.cobs_select_topk(pk, g["lens"], g["Q"][:, None], s["mu"], s["so"], sel, ws, max_len=w.max_len)
+            torch.cuda.synchronize()
+            sels[kind] = sel.cpu().numpy()
+            sh = B.cobs_summary_shapes(pk, w.batch, w.max_len)
+            res[f"summary_bytes_per_block_{kind}"] = (sh["mu_bytes"] + sh["so_bytes"]) / (
+                w.batch * w.n_kv_heads * sh["nb_max"])
+        a, f = sels["lowrank"], sels["lowrank_fp4"]
+        same = sum(len(set(a[b, h][a[b, h] >= 0]) & set(f[b, h][f[b, h] >= 0]))
+                   for b in range(w.batch) for h in range(w.n_kv_heads))
+        tot_a = int((a >= 0).sum())
+        res["fp4_vs_fp32_selection_agreement"] = same / max(tot_a, 1)
+        res["fp4_identical_units"] = int(sum((a[b, h] == f[b, h]).all()
+                                             for b in range(w.batch) for h in range(w.n_kv_heads)))
+        res["units"] = w.batch * w.n_kv_heads
+        for kind, sl in sels.items():
+            hit = sum(len(set(sl[b, h][sl[b, h] >= 0]) & set(ex[b, h][ex[b, h] >= 0]))
+                      for b in range(w.batch) for h in range(w.n_kv_heads))
+            res[f"recall_{kind}_alpha{w.alpha}"] = hit / max(int((ex >= 0).sum()), 1)
     print(json.dumps(res), flush=True)
 
 

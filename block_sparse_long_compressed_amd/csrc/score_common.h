@@ -139,16 +139,11 @@ __device__ __forceinline__ void sum_tile_load(const void* mrow, const void* vrow
   }
 }
 
-// Magnitude-and-sign value of an FP4 E2M1 code (sign in bit 3): 0, .5, 1, 1.5,
-// 2, 3, 4, 6, built directly as fp32 bits.
-__device__ __forceinline__ float e2m1_value(uint32_t nib) {
-  const uint32_t m3 = nib & 7u;
-  uint32_t bits = (m3 >= 2u) ? (((m3 >> 1) + 126u) << 23) | ((m3 & 1u) << 22) : (m3 ? 0x3F000000u : 0u);
-  return __uint_as_float(bits | ((nib & 8u) << 28));
-}
+// 2^(byte - 127) of an E8M0 exponent byte, as the fp32 scale operand of the gfx950
+// scaled FP4 conversion (which multiplies by 2 to the scale's biased exponent - 127).
+__device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
 
-// 2^(byte - 127) of an E8M0 exponent byte (byte 0, an all-zero group, gives 0).
-__device__ __forceinline__ float e8m0_value(uint32_t byte) { return __uint_as_float(byte << 23); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Scores (without ln n_b) of the tile's 16 blocks for the group's heads from the
 // loaded rows.  Linear and quadratic terms are independent MFMA chains.
@@ -182,29 +177,36 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
       }
     }
   } else if constexpr (KIND == 3) {
-    // (v_i . q)^2 with v_i decoded on the fly: entry 16u + 4g + c is nibble u*4 + c of
-    // this lane's codes, scaled by the exponent of group u/2 of this lane's block (the
-    // scale must be applied on the A side: an output row belongs to another lane's block)
-    constexpr int NG = D / 32;
+    // (v_i . q)^2 with v_i decoded on the fly by the hardware FP4 conversion: entry
+    // 16u + 4g + c is nibble u*4 + c of this lane's codes, scaled by the exponent of
+    // group u/2 of this lane's block (the scale must be applied on the A side: an
+    // output row belongs to another lane's block)
 #pragma unroll 1
     for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
       if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, g, t);
 #pragma unroll
       for (int rr = 0; rr < kRankGroup; ++rr) {
         if (r0 + rr < rank) {
-          float sc[NG];
-#pragma unroll
-          for (int q = 0; q < NG; ++q) sc[q] = e8m0_value((t.ex[rr] >> (8 * q)) & 0xFFu);
           f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
+            // codes of columns 16u + 4g + {0,1} and {2,3}: bytes 2(u&1) and 2(u&1)+1 of word u/2;
+            // group u/2's exponent (columns 16u + 4g + c share group u/2)
+            const uint32_t w = t.code[rr][u >> 1];
+            const float sc = e8m0_scale((t.ex[rr] >> (8 * (u >> 1))) & 0xFFu);
+            f32x2 lo, hi;
+            if (u & 1) {
+              lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+              hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+            } else {
+              lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+              hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+            }
+            const float v[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const int k = u * 4 + c;
-              const uint32_t nib = (t.code[rr][k >> 3] >> (4 * (k & 7))) & 0xFu;
-              const float v = e2m1_value(nib) * sc[u >> 1];
-              if (u & 1) pr2 = mfma_f32_16x16x4(v, wlin[u][c], pr2);
-              else pr = mfma_f32_16x16x4(v, wlin[u][c], pr);
+              if (u & 1) pr2 = mfma_f32_16x16x4(v[c], wlin[u][c], pr2);
+              else pr = mfma_f32_16x16x4(v[c], wlin[u][c], pr);
             }
           }
 #pragma unroll

@@ -107,7 +107,7 @@ cobs_status cobs_validate_params(const cobs_params* p);
  * entry 16u + 4g + c at nibble (g * d/16 + u) * 4 + c), then for each vector
  * d/32 bytes of shared exponents (E8M0, 2^(byte-127) scales entries [32j, 32j+32))
  * and zero padding.  A group's exponent is floor(log2 max|v|) - 2, clamped to
- * [-127, 127] (byte 0 for an all-zero group, read as scale 0); each entry is the
+ * [-127, 127] (an all-zero group stores byte 0 and zero codes); each entry is the
  * nearest of +-{0, .5, 1, 1.5, 2, 3, 4, 6} times the scale, ties to the even code,
  * saturating at 6 (the OCP microscaling FP4 format).  The mu and so pointers of the
  * other calls take these bytes.
