@@ -36,6 +36,8 @@ class cobs_params(ctypes.Structure):
         ("alpha", ctypes.c_float),
         ("scale", ctypes.c_float),
         ("kv_dtype", ctypes.c_int32),
+        ("subspace_dim", ctypes.c_int32),
+        ("subspace", ctypes.c_void_p),
     ]
 
 
@@ -63,6 +65,8 @@ _SIGNATURES = {
                                        _vp, _vp, _sz, _vp]),
     "cobs_sparse_attn_prefill": (_i32, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _sz, _vp]),
+    "cobs_query_subspace_workspace_bytes": (_sz, [_P]),
+    "cobs_query_subspace": (_i32, [_P, _i32, _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -93,9 +97,26 @@ def _check(fn: str, status: int) -> None:
 def make_params(head_dim: int, n_q_heads: int, n_kv_heads: int, top_k: int, window: int = 0,
                 cmp_len: int = 0, cmp_stride: int = 16, so_kind: int = COBS_SO_DIAG, rank: int = 0,
                 alpha: float = 1.0, scale: float = 0.0, kv_dtype: int = COBS_BF16,
-                block_size: int = 64) -> cobs_params:
-    return cobs_params(head_dim, n_q_heads, n_kv_heads, block_size, top_k, window, cmp_len, cmp_stride,
-                       so_kind, rank, alpha, scale, kv_dtype)
+                block_size: int = 64, subspace: Optional[torch.Tensor] = None) -> cobs_params:
+    """Method parameters.  `subspace` ([H_kv][s][d] fp32 on the device) turns on the
+    query-subspace projection with s = its second dimension; the caller keeps the
+    tensor alive while the parameters are in use."""
+    p = cobs_params(head_dim, n_q_heads, n_kv_heads, block_size, top_k, window, cmp_len, cmp_stride,
+                    so_kind, rank, alpha, scale, kv_dtype, 0, None)
+    if subspace is not None:
+        set_subspace(p, subspace)
+    return p
+
+
+def set_subspace(p: cobs_params, P: Optional[torch.Tensor]) -> None:
+    """Point the parameters at a query subspace [H_kv][s][d] (fp32, contiguous), or
+    turn the projection off with None."""
+    if P is None:
+        p.subspace_dim, p.subspace = 0, None
+        return
+    if P.dtype != torch.float32 or P.dim() != 3 or not P.is_contiguous():
+        raise ValueError("subspace must be a contiguous fp32 [H_kv][s][d] tensor")
+    p.subspace_dim, p.subspace = P.shape[1], P.data_ptr()
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -190,7 +211,8 @@ def alloc_summaries(p: cobs_params, batch: int, max_len: int, device="cuda") -> 
         so = torch.empty((batch, hkv, nb, sh["so_bytes"] // (batch * hkv * nb)), dtype=torch.uint8, device=device)
     else:
         mu = torch.empty((batch, hkv, nb, d), dtype=torch.float32, device=device)
-        so_shape = (batch, hkv, nb, p.rank, d) if p.so_kind == COBS_SO_LOWRANK else (batch, hkv, nb, d)
+        vlen = -(-p.subspace_dim // 32) * 32 if p.subspace_dim > 0 else d
+        so_shape = (batch, hkv, nb, p.rank, vlen) if p.so_kind == COBS_SO_LOWRANK else (batch, hkv, nb, d)
         so = torch.empty(so_shape, dtype=torch.float32, device=device)
     kdt = torch.bfloat16 if p.kv_dtype == COBS_BF16 else torch.float32
     kc = vc = None
@@ -198,6 +220,20 @@ def alloc_summaries(p: cobs_params, batch: int, max_len: int, device="cuda") -> 
         kc = torch.empty((batch, hkv, nc, d), dtype=kdt, device=device)
         vc = torch.empty((batch, hkv, nc, d), dtype=kdt, device=device)
     return {"mu": mu, "so": so, "kc": kc, "vc": vc, "nb_max": nb, "nc_max": nc}
+
+
+def cobs_query_subspace(p: cobs_params, Q: torch.Tensor, s: int, stream=None) -> torch.Tensor:
+    """Query subspace [H_kv][s][d] (fp32) from calibration queries Q [n][H_q][d]."""
+    q = cobs_params.from_buffer_copy(p)
+    q.subspace_dim = s
+    n = lib().cobs_query_subspace_workspace_bytes(ctypes.byref(q))
+    if n == 0:
+        raise CobsError("cobs_query_subspace_workspace_bytes", COBS_ERR_INVALID_ARG)
+    ws = torch.empty(n, dtype=torch.uint8, device=Q.device)
+    P = torch.empty((p.n_kv_heads, s, p.head_dim), dtype=torch.float32, device=Q.device)
+    _check("cobs_query_subspace", lib().cobs_query_subspace(ctypes.byref(q), Q.shape[0], _ptr(Q), _ptr(P), _ptr(ws),
+                                                            n, _stream(stream)))
+    return P
 
 
 def alloc_workspace(p: cobs_params, batch: int, max_len: int, n_q_tokens: int = 1, device="cuda") -> torch.Tensor:

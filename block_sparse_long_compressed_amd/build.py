@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libcobs.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["k_summary.hip", "k_lowrank.hip", "k_decode.hip", "k_prefill.hip", "k_prefill_attn.hip", "cobs_api.cpp"]
+SOURCES = ["k_summary.hip", "k_lowrank.hip", "k_subspace.hip", "k_decode.hip", "k_prefill.hip", "k_prefill_attn.hip",
+           "cobs_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -28,8 +28,14 @@ int64_t nc_of(const cobs_params* p, int max_len) {
 }
 // bytes of one block's compressed low-rank record: codes, exponents, padding to 16
 size_t fp4_record_bytes(int rank, int d) { return ((size_t)rank * (d / 2 + d / 32) + 15) / 16 * 16; }
-// kernel-side score kinds: 0 diag, 1 low-rank fp32, 2 exact masses, 3 low-rank fp4
-int kernel_kind(const cobs_params* p) { return p->so_kind == COBS_SO_LOWRANK_FP4 ? 3 : p->so_kind; }
+// kernel-side score kinds: 0 diag, 1 low-rank fp32, 2 exact masses, 3 low-rank fp4,
+// 4 and 5 the low-rank kinds in a query subspace
+int kernel_kind(const cobs_params* p) {
+  const int k = p->so_kind == COBS_SO_LOWRANK_FP4 ? 3 : p->so_kind;
+  return p->subspace_dim > 0 ? (k == 1 ? 4 : 5) : k;
+}
+// length of a stored rank-r vector: the subspace dimension rounded up to 32, else d
+int vec_len(const cobs_params* p) { return p->subspace_dim > 0 ? (p->subspace_dim + 31) / 32 * 32 : p->head_dim; }
 float scale_of(const cobs_params* p) { return p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim); }
 int group_of(const cobs_params* p) { return p->n_q_heads / p->n_kv_heads; }
 
@@ -42,6 +48,10 @@ cobs_status check_params(const cobs_params* p) {
   if (p->so_kind != COBS_SO_DIAG && p->so_kind != COBS_SO_LOWRANK && p->so_kind != COBS_SO_LOWRANK_FP4)
     return COBS_ERR_INVALID_ARG;
   if (p->so_kind != COBS_SO_DIAG && (p->rank < 1 || p->rank > 8)) return COBS_ERR_INVALID_ARG;
+  if (p->subspace_dim < 0) return COBS_ERR_INVALID_ARG;
+  if (p->subspace_dim > 0) {
+    if (p->so_kind == COBS_SO_DIAG || !p->subspace || p->subspace_dim > p->head_dim) return COBS_ERR_INVALID_ARG;
+  }
   if (!(p->alpha >= 0.f) || !isfinite(p->alpha)) return COBS_ERR_INVALID_ARG;
   if (!(p->scale >= 0.f) || !isfinite(p->scale)) return COBS_ERR_INVALID_ARG;
   if (p->kv_dtype != COBS_BF16 && p->kv_dtype != COBS_F32) return COBS_ERR_INVALID_ARG;
@@ -141,8 +151,9 @@ cobs_status cobs_summary_shapes(const cobs_params* p, int32_t batch, int32_t max
   const bool fp4 = p->so_kind == COBS_SO_LOWRANK_FP4;
   if (mu_bytes) *mu_bytes = rows * nb * p->head_dim * (fp4 ? 2 : sizeof(float));
   if (so_bytes) {
-    if (fp4) *so_bytes = rows * nb * fp4_record_bytes(p->rank, p->head_dim);
-    else *so_bytes = rows * nb * p->head_dim * sizeof(float) * (p->so_kind == COBS_SO_LOWRANK ? p->rank : 1);
+    if (fp4) *so_bytes = rows * nb * fp4_record_bytes(p->rank, vec_len(p));
+    else if (p->so_kind == COBS_SO_LOWRANK) *so_bytes = rows * nb * vec_len(p) * sizeof(float) * p->rank;
+    else *so_bytes = rows * nb * p->head_dim * sizeof(float);
   }
   if (pooled_bytes) *pooled_bytes = rows * nc * p->head_dim * esz;
   return COBS_OK;
@@ -173,6 +184,7 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
   a.var = p->so_kind == COBS_SO_DIAG ? static_cast<float*>(so) : nullptr;
   a.lowrank = p->so_kind == COBS_SO_DIAG ? nullptr : so;
   a.fp4 = p->so_kind == COBS_SO_LOWRANK_FP4;
+  a.P = p->subspace_dim > 0 ? p->subspace : nullptr; a.sub_s = p->subspace_dim; a.vlen = vec_len(p);
   a.kc = pool ? kc : nullptr; a.vc = pool ? vc : nullptr;
   a.old_lens = nullptr; a.touch_blocks = 0;
   a.stream = (hipStream_t)stream;
@@ -203,6 +215,7 @@ cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t m
   a.var = p->so_kind == COBS_SO_DIAG ? static_cast<float*>(so) : nullptr;
   a.lowrank = p->so_kind == COBS_SO_DIAG ? nullptr : so;
   a.fp4 = p->so_kind == COBS_SO_LOWRANK_FP4;
+  a.P = p->subspace_dim > 0 ? p->subspace : nullptr; a.sub_s = p->subspace_dim; a.vlen = vec_len(p);
   a.kc = pool ? kc : nullptr; a.vc = pool ? vc : nullptr;
   a.stream = (hipStream_t)stream;
   if ((st = hip_status(launch_append_diag(a))) != COBS_OK) return st;
@@ -219,6 +232,7 @@ static PrefillArgs prefill_args(const cobs_params* p, int32_t batch, int32_t max
   a.so_kind = kernel_kind(p); a.q_pos0 = q_pos0; a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha;
   a.scale = scale_of(p); a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr;
   a.mu = a.so = a.gates = nullptr; a.sel = nullptr; a.sel_score = nullptr; a.out = nullptr; a.stream = stream;
+  a.P = p->subspace_dim > 0 ? p->subspace : nullptr; a.sub_s = p->subspace_dim; a.vlen = vec_len(p);
   return a;
 }
 
@@ -234,6 +248,7 @@ static DecodeArgs decode_args(const cobs_params* p, const Plan& pl, int32_t batc
   a.tpw = pl.attn_tpw; a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
   a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr; a.mu = a.so = a.gates = nullptr;
   a.sel = nullptr; a.sel_in = nullptr; a.sel_score = nullptr; a.out = nullptr;
+  a.P = p->subspace_dim > 0 ? p->subspace : nullptr; a.sub_s = p->subspace_dim; a.vlen = vec_len(p);
   a.sel_counters = at<uint32_t>(ws, pl.off_cnt_sel);
   a.attn_counters = at<uint32_t>(ws, pl.off_cnt_attn);
   a.ready = at<uint32_t>(ws, pl.off_ready);
@@ -330,6 +345,27 @@ cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int3
   cobs_status st2 = hip_status(launch_prefill_select(a));
   if (st2 != COBS_OK) return st2;
   return hip_status(launch_prefill_attn(a));
+}
+
+size_t cobs_query_subspace_workspace_bytes(const cobs_params* p) {
+  if (!p || p->n_kv_heads < 1 || (p->head_dim != 64 && p->head_dim != 128)) return 0;
+  return align_up(subspace_ws_bytes(p->n_kv_heads, p->head_dim));
+}
+
+cobs_status cobs_query_subspace(const cobs_params* p, int32_t n_tokens, const void* Q, float* P_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!p || !P_out || !Q || !ws || n_tokens < 1) return COBS_ERR_INVALID_ARG;
+  cobs_params q = *p;
+  q.subspace = P_out;                          // validated as the subspace it will become
+  cobs_status st = check_params(&q);
+  if (st != COBS_OK) return st;
+  if (q.subspace_dim < 1) return COBS_ERR_INVALID_ARG;
+  if (ws_bytes < cobs_query_subspace_workspace_bytes(p)) return COBS_ERR_WORKSPACE;
+  SubspaceArgs a;
+  a.hkv = p->n_kv_heads; a.hq = p->n_q_heads; a.group = group_of(p); a.head_dim = p->head_dim;
+  a.n = n_tokens; a.s = p->subspace_dim; a.bf16 = p->kv_dtype == COBS_BF16;
+  a.Q = Q; a.P = P_out; a.ws = ws; a.stream = (hipStream_t)stream;
+  return hip_status(launch_query_subspace(a));
 }
 
 }  // extern "C"

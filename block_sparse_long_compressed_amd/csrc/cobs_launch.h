@@ -18,6 +18,8 @@ struct BuildArgs {
   float* var;                  // diagonal channel, or null
   void* lowrank;               // fp32 [..][NB][rank][d], or FP4 records when fp4 is set; or null
   bool fp4;                    // compressed storage: bf16 mean, MX FP4 vectors
+  const float* P;              // query subspaces [hkv][sub_s][d], or null
+  int sub_s, vlen;             // subspace dimension (0: none); length of a rank-r vector
   void *kc, *vc;               // null when the compressed branch is off
   hipStream_t stream;
 };
@@ -32,7 +34,9 @@ struct DecodeArgs {
   int tpw, wg_slc, wg_win, wg_cmp;   // attention: 64-key tiles per wave, workgroups per branch and unit
   const int32_t* seq_lens;
   const void *Q, *K, *V, *kc, *vc;
-  const void *mu, *so;         // summaries in the layout of so_kind (3: compressed storage)
+  const void *mu, *so;         // summaries in the layout of so_kind (3, 5: compressed storage)
+  const float* P;              // query subspaces [hkv][sub_s][d] (so_kind 4, 5), else null
+  int sub_s, vlen;             // subspace dimension; length of a rank-r vector
   const float* gates;
   int32_t* sel;                // written by the selection role
   const int32_t* sel_in;       // caller's selection (attention only)
@@ -53,10 +57,22 @@ struct PrefillArgs {
   const int32_t* seq_lens;     // device [batch] or null (then every length is max_len)
   const void *Q, *K, *V, *kc, *vc;
   const void *mu, *so;
+  const float* P;
+  int sub_s, vlen;
   const float* gates;
   int32_t* sel;
   float* sel_score;
   float* out;
+  hipStream_t stream;
+};
+
+// Query-subspace calibration (see k_subspace.hip).
+struct SubspaceArgs {
+  int hkv, hq, group, head_dim, n, s;
+  bool bf16;
+  const void* Q;               // [n][hq][d] calibration queries
+  float* P;                    // [hkv][s][d] out
+  void* ws;                    // subspace_ws_bytes(hkv, d)
   hipStream_t stream;
 };
 
@@ -67,5 +83,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill_select(const PrefillArgs& a);
 hipError_t launch_prefill_attn(const PrefillArgs& a);
 hipError_t launch_prefill_attn_bf16(const PrefillArgs& a);   // token-blocked, bf16 K/V
+hipError_t launch_query_subspace(const SubspaceArgs& a);
+size_t subspace_ws_bytes(int hkv, int d);
 
 }  // namespace cobs

@@ -50,6 +50,8 @@ struct DecodeParams {
   int sel_wgs, splits, sel_tpw, rank;
   float alpha, scale;
   const void *mu, *so;
+  const float* P;               // query subspaces [hkv][sub_s][d] (subspace score kinds)
+  int sub_s, vlen;              // subspace dimension; length of a rank-r vector
   int32_t* sel;                 // selection written by the scoring role
   float* sel_score;
   uint32_t* sel_counters;
@@ -77,6 +79,7 @@ struct SelLds {
   int bcast[4];
   float lse_sh[16];
   float red_part[kSelMaxSplits * 32];
+  f32x4 wsub_x[8 * 64];          // subspace weights exchanged between the waves
   // followed by [nb_pad] keys and [nb_pad] group scores
 };
 
@@ -176,7 +179,7 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
     const size_t sum_base = (size_t)unit * p.nb_max;
     auto rows_of = [&](int tile, const void*& mr, const void*& vr) {
       const int brow = min(tile * 16 + n, ncand - 1);      // A-operand row (block) of this lane
-      summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, mr, vr);
+      summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, p.vlen, mr, vr);
     };
     SumTile<D, KIND> st[RING];
     const void* vrow[RING];
@@ -186,22 +189,30 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
       if (r < p.sel_tpw && tile0 + r < tiles_total) {
         const void* mrow;
         rows_of(tile0 + r, mrow, vrow[r]);
-        sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+        sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
       }
     }
-    float wlin[NU][4];
+    float wlin[NU][4], wq[NU][4];
     score_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
                               wlin);
+    if constexpr (Kind<KIND>::kSub) {
+      // scale * P q: the four waves each contract a quarter of the column tiles
+      const float* Ph = p.P + (size_t)head * p.sub_s * D;
+      subspace_weights_part<D>(Ph, p.sub_s, p.vlen, wave, 4, n, g, wlin, sl.wsub_x, wq);
+      __syncthreads();
+      subspace_weights_gather<D>(p.vlen, wave, 4, n, g, sl.wsub_x, wq);
+    }
     for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
         const int j = j0 + r, tile = tile0 + j0 + r;
         if (j < p.sel_tpw && tile < tiles_total) {
-          const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
+          const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, wlin,
+                                                   Kind<KIND>::kSub ? wq : wlin);
           if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
             const void* mrow;
             rows_of(tile + RING, mrow, vrow[r]);
-            sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+            sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
           }
           post(tile, s4, true);
         }
@@ -601,6 +612,16 @@ static hipError_t launch_decode_ed(const DecodeArgs& a, const DecodeParams& dp) 
     if (hv == 2) return launch_decode_t<E, D, 3, 2>(a, dp);
     return launch_decode_t<E, D, 3, 4>(a, dp);
   }
+  if (a.so_kind == 4) {                       // rank-r fp32 in a query subspace
+    if (hv == 1) return launch_decode_t<E, D, 4, 1>(a, dp);
+    if (hv == 2) return launch_decode_t<E, D, 4, 2>(a, dp);
+    return launch_decode_t<E, D, 4, 4>(a, dp);
+  }
+  if (a.so_kind == 5) {                       // compressed storage in a query subspace
+    if (hv == 1) return launch_decode_t<E, D, 5, 1>(a, dp);
+    if (hv == 2) return launch_decode_t<E, D, 5, 2>(a, dp);
+    return launch_decode_t<E, D, 5, 4>(a, dp);
+  }
   if (hv == 1) return launch_decode_t<E, D, 1, 1>(a, dp);
   if (hv == 2) return launch_decode_t<E, D, 1, 2>(a, dp);
   return launch_decode_t<E, D, 1, 4>(a, dp);
@@ -613,7 +634,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
   p.nb_pad = (a.nb_max + 15) / 16 * 16; p.top_k = a.top_k; p.seq_lens = a.seq_lens; p.Q = a.Q;
   p.sel_wgs = a.do_select ? units * a.splits : 0;
   p.splits = a.splits; p.sel_tpw = a.sel_tpw; p.rank = a.rank; p.alpha = a.alpha; p.scale = a.scale;
-  p.mu = a.mu; p.so = a.so; p.sel = a.sel; p.sel_score = a.sel_score; p.sel_counters = a.sel_counters;
+  p.mu = a.mu; p.so = a.so; p.P = a.P; p.sub_s = a.sub_s; p.vlen = a.vlen; p.sel = a.sel; p.sel_score = a.sel_score; p.sel_counters = a.sel_counters;
   p.scores = a.scores; p.lse_part = a.lse_part;
   p.pub = (a.do_select && a.do_attn) ? a.ready : nullptr;
   p.wc_wgs = a.do_attn ? units * (a.wg_win + a.wg_cmp) : 0;

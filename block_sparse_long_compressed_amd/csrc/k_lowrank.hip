@@ -15,6 +15,13 @@
 // eigensolver to rounding.  One 256-thread workgroup per block; G and V live in
 // LDS (2 x 32 KiB).  Eigenvalues <= 0 give v = 0; each v is signed so that its
 // largest-magnitude entry is positive.
+//
+// Query-subspace projection (Technisches Resuemee 2.3, "Subraum-Projektion"):
+// with P [s][d] (orthonormal rows spanning the queries' dominant directions) the
+// covariance is first projected, C' = P C P^T.  Its Gram matrix is that of the
+// projected keys Y = X P^T (formed 16 columns at a time in fp64), and its scaled
+// eigenvectors are Y^T w / sqrt(n) = P (X^T w / sqrt(n)), stored with length
+// vlen = s rounded up to 32 (zeros beyond s).
 #include "cobs_device.h"
 #include "cobs_launch.h"
 #include "score_common.h"
@@ -58,15 +65,17 @@ __device__ __forceinline__ uint32_t e2m1_code(double y) {
   return (c != 0u && y < 0.0) ? (c | 8u) : c;
 }
 
-// The compressed record of one block from its rank scaled eigenvectors (fp64):
-// per vector d/2 bytes of codes, then per vector d/32 exponent bytes, then zero
-// padding to 16 bytes.  Each group of 32 entries shares the exponent
-// e = floor(log2 max|v|) - 2 (stored as e + 127, 0 for an all-zero group), and
-// entry 16u + 4g + c sits at nibble (g * d/16 + u) * 4 + c of its vector, low
-// nibble first, so that a scoring lane reads its columns as one contiguous run.
+// The compressed record of one block from its rank scaled eigenvectors (fp64, of
+// length len, a multiple of 32): per vector len/2 bytes of codes, then per vector
+// len/32 exponent bytes, then zero padding to 16 bytes.  Each group of 32 entries
+// shares the exponent e = floor(log2 max|v|) - 2 (stored as e + 127, 0 for an
+// all-zero group), and entry 16u + 4g + c sits at nibble (g * len/16 + u) * 4 + c
+// of its vector, low nibble first, so that a scoring lane reads its columns as one
+// contiguous run.
 template <int D>
-__device__ void quantize_record(const double (*vout)[D], int (*gexp)[D / 32], uint8_t* rec, int rank, int tid) {
-  constexpr int NG = D / 32;
+__device__ void quantize_record(const double (*vout)[D], int (*gexp)[D / 32], uint8_t* rec, int rank, int len,
+                                int tid) {
+  const int NG = len / 32;
   for (int idx = tid; idx < rank * NG; idx += kLrThreads) {
     const int i = idx / NG, q = idx % NG;
     double amax = 0.0;
@@ -80,16 +89,16 @@ __device__ void quantize_record(const double (*vout)[D], int (*gexp)[D / 32], ui
     gexp[i][q] = e;
   }
   __syncthreads();
-  const int code_bytes = rank * (D / 2);
-  const int total = (int)fp4_record_bytes_dev(rank, D);
+  const int code_bytes = rank * (len / 2);
+  const int total = (int)fp4_record_bytes_dev(rank, len);
   for (int idx = tid; idx < total; idx += kLrThreads) {
     uint32_t byte = 0;
     if (idx < code_bytes) {
-      const int i = idx / (D / 2), bb = idx % (D / 2);
+      const int i = idx / (len / 2), bb = idx % (len / 2);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int P = 2 * bb + h;                       // nibble position within the vector
-        const int g = P / (D / 4), kk = P % (D / 4);
+        const int g = P / (len / 4), kk = P % (len / 4);
         const int entry = 16 * (kk / 4) + 4 * g + (kk % 4);
         const double y = ldexp(vout[i][entry], -gexp[i][entry / 32]);
         byte |= e2m1_code(y) << (4 * h);
@@ -108,7 +117,9 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
                                                               const int32_t* __restrict__ old_lens, int max_len,
                                                               int nb_max, int rank,
                                                               const typename E::storage* __restrict__ K,
-                                                              void* __restrict__ lowrank, int fp4) {
+                                                              void* __restrict__ lowrank, int fp4,
+                                                              const float* __restrict__ Psub, int sub_s,
+                                                              int vlen) {
   __shared__ double A[kN][kN + 1];      // Gram matrix, diagonalised in place (+1: bank spread)
   // the block's keys (fp32, exact for bf16) until G is built, then the rotations
   __shared__ union { float k[kN][D + 1]; double v[kN][kN + 1]; } kv;
@@ -153,7 +164,9 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
     mu[c] = s / (double)n;
   }
   __syncthreads();
-  // Gram matrix G = X X^T / n: each thread a 4x4 tile, zero outside the n x n corner
+  // Gram matrix G = X X^T / n (or, with a query subspace P, G = Y Y^T / n for the
+  // projected keys Y = X P^T, whose covariance is P C P^T): each thread a 4x4 tile,
+  // zero outside the n x n corner
   {
     const int ta = tid / 16, tb = tid % 16;
     double acc[4][4];
@@ -161,18 +174,43 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int c = 0; c < D; ++c) {
-      const double m = mu[c];
-      double xi[4], xj[4];
+    if (Psub) {
+      // 16 columns of Y = X P^T at a time, staged in A's space (A is written after)
+      double (*ych)[17] = reinterpret_cast<double (*)[17]>(&A[0][0]);
+      const float* Pu = Psub + (size_t)head * sub_s * D;
+      for (int j0 = 0; j0 < sub_s; j0 += 16) {
+        for (int idx = tid; idx < kN * 16; idx += kLrThreads) {
+          const int r = idx / 16, jj = idx % 16, j = j0 + jj;
+          double y = 0.0;
+          if (r < n && j < sub_s) {
+            const float* pr = Pu + (size_t)j * D;
+            for (int c = 0; c < D; ++c) y += ((double)kv.k[r][c] - mu[c]) * (double)pr[c];
+          }
+          ych[r][jj] = y;
+        }
+        __syncthreads();
+        for (int jj = 0; jj < 16; ++jj) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        xi[k] = (4 * ta + k < n) ? (double)kv.k[4 * ta + k][c] - m : 0.0;
-        xj[k] = (4 * tb + k < n) ? (double)kv.k[4 * tb + k][c] - m : 0.0;
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] += ych[4 * ta + i][jj] * ych[4 * tb + j][jj];
+        }
+        __syncthreads();
       }
+    } else {
+      for (int c = 0; c < D; ++c) {
+        const double m = mu[c];
+        double xi[4], xj[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int k = 0; k < 4; ++k) {
+          xi[k] = (4 * ta + k < n) ? (double)kv.k[4 * ta + k][c] - m : 0.0;
+          xj[k] = (4 * tb + k < n) ? (double)kv.k[4 * tb + k][c] - m : 0.0;
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += xi[i] * xj[j];
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] += xi[i] * xj[j];
+      }
     }
     const double inv_n = 1.0 / (double)n;
 #pragma unroll
@@ -270,12 +308,33 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
     vout[i][c] = s;
   }
   __syncthreads();
+  // subspace: the vectors of P C P^T are P X^T w / sqrt(n) = P v (entries >= sub_s are 0)
+  const int vl = Psub ? vlen : D;
+  if (Psub) {
+    const float* Pu = Psub + (size_t)head * sub_s * D;
+    double pv[8 * D / kLrThreads];
+#pragma unroll
+    for (int k = 0; k < 8 * D / kLrThreads; ++k) {
+      const int idx = tid + k * kLrThreads, i = idx / vl, j = idx % vl;
+      double s = 0.0;
+      if (i < rank && j < sub_s)
+        for (int c = 0; c < D; ++c) s += (double)Pu[(size_t)j * D + c] * vout[i][c];
+      pv[k] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8 * D / kLrThreads; ++k) {
+      const int idx = tid + k * kLrThreads;
+      if (idx < rank * vl) vout[idx / vl][idx % vl] = pv[k];
+    }
+    __syncthreads();
+  }
   // sign: largest-magnitude entry positive (first such entry on ties)
   if (tid < 64) {
     for (int i = 0; i < rank; ++i) {
       double best = -1.0;
       int bi = D;
-      for (int c = tid; c < D; c += 64) {
+      for (int c = tid; c < vl; c += 64) {
         const double a = fabs(vout[i][c]);
         if (a > best) { best = a; bi = c; }
       }
@@ -285,23 +344,23 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
         const int oi = __shfl_xor(bi, m, 64);
         if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
       }
-      if (tid == 0) red[0] = (bi < D && vout[i][bi] < 0.0) ? -1.0 : 1.0;
+      if (tid == 0) red[0] = (bi < vl && vout[i][bi] < 0.0) ? -1.0 : 1.0;
       __builtin_amdgcn_wave_barrier();
       const double sg = red[0];
-      for (int c = tid; c < D; c += 64) vout[i][c] *= sg;
+      for (int c = tid; c < vl; c += 64) vout[i][c] *= sg;
       __builtin_amdgcn_wave_barrier();
     }
   }
   __syncthreads();
   if (fp4) {
-    quantize_record<D>(vout, gexp, rec, rank, tid);
-    const int words = (int)(fp4_record_bytes_dev(rank, D) / 4);
+    quantize_record<D>(vout, gexp, rec, rank, vl, tid);
+    const int words = (int)(fp4_record_bytes_dev(rank, vl) / 4);
     uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(lowrank) +
-                                                (unit * (size_t)nb_max + b) * fp4_record_bytes_dev(rank, D));
+                                                (unit * (size_t)nb_max + b) * fp4_record_bytes_dev(rank, vl));
     for (int w = tid; w < words; w += kLrThreads) dst[w] = reinterpret_cast<const uint32_t*>(rec)[w];
   } else {
-    float* dst = static_cast<float*>(lowrank) + ((unit * (size_t)nb_max + b) * rank) * D;
-    for (int idx = tid; idx < rank * D; idx += kLrThreads) dst[idx] = (float)vout[idx / D][idx % D];
+    float* dst = static_cast<float*>(lowrank) + ((unit * (size_t)nb_max + b) * rank) * vl;
+    for (int idx = tid; idx < rank * vl; idx += kLrThreads) dst[idx] = (float)vout[idx / vl][idx % vl];
   }
   __syncthreads();                         // shared arrays are reused by the next block
   }
@@ -311,7 +370,8 @@ template <typename E, int D>
 static hipError_t launch_lr(const BuildArgs& a) {
   dim3 grid(a.old_lens ? a.touch_blocks : a.nb_max, a.hkv, a.batch);
   hipLaunchKernelGGL((k_build_lowrank<E, D>), grid, dim3(kLrThreads), 0, a.stream, a.seq_lens, a.old_lens,
-                     a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank, a.fp4 ? 1 : 0);
+                     a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank, a.fp4 ? 1 : 0,
+                     a.P, a.sub_s, a.vlen);
   return hipGetLastError();
 }
 

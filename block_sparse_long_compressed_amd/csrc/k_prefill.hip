@@ -31,6 +31,8 @@ struct PsParams {
   const int32_t* seq_lens;          // null: every sequence has length L_fixed
   const void* Q;
   const void *mu, *so;
+  const float* P;                   // query subspaces [hkv][sub_s][d] (subspace score kinds)
+  int sub_s, vlen;                  // subspace dimension; length of a rank-r vector
   int32_t* sel;
   float* sel_score;
 };
@@ -56,15 +58,17 @@ __global__ __launch_bounds__(256) void k_prefill_select(PsParams p) {
   const size_t sum_base = ((size_t)seq * p.hkv + head) * p.nb_max;
   const int tiles = (ncand + 15) / 16;
 
-  float wlin[NU][4];
+  float wlin[NU][4], wq[NU][4];
   score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
                             n, g, G, p.scale, wlin);
+  if constexpr (Kind<KIND>::kSub)
+    subspace_weights_part<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, 0, 1, n, g, wlin, nullptr, wq);
   const bool use_quad = p.alpha != 0.f;
   auto scores = [&](int tile) -> f32x4 {
     const int brow = min(tile * 16 + n, ncand - 1);
     const void *mr, *vr;
-    summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, mr, vr);
-    f32x4 s = score_tile<D, KIND>(mr, vr, p.rank, g, use_quad, p.alpha, wlin);
+    summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, p.vlen, mr, vr);
+    f32x4 s = score_tile<D, KIND>(mr, vr, p.rank, p.vlen, g, use_quad, p.alpha, wlin, Kind<KIND>::kSub ? wq : wlin);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = tile * 16 + 4 * g + i;
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
   const bool use_quad = p.alpha != 0.f;
   auto rows_of = [&](int tile, const void*& mr, const void*& vr) {
     const int brow = min(tile * 16 + n, ncand - 1);
-    summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, mr, vr);
+    summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, p.vlen, mr, vr);
   };
 
   // ---- scores of tiles wave, wave+4, ... (summary rows requested before the query)
@@ -217,12 +221,20 @@ __global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
     if (tile < tiles) {
       const void* mrow;
       rows_of(tile, mrow, vrow[r]);
-      sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+      sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
     }
   }
-  float wlin[NU][4];
+  float wlin[NU][4], wq[NU][4];
   score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
                             n, g, G, p.scale, wlin);
+  if constexpr (Kind<KIND>::kSub) {
+    // scale * P q: the four waves each contract a quarter of the column tiles (exchange
+    // area after the keys)
+    f32x4* xch = reinterpret_cast<f32x4*>(s_key + p.nb_pad);
+    subspace_weights_part<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, wave, 4, n, g, wlin, xch, wq);
+    __syncthreads();
+    subspace_weights_gather<D>(p.vlen, wave, 4, n, g, xch, wq);
+  }
   float run_m = -INFINITY, run_s = 0.f;
 #pragma unroll 1
   for (int j0 = 0; wave + 4 * j0 < tiles; j0 += RING) {
@@ -230,11 +242,12 @@ __global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
     for (int r = 0; r < RING; ++r) {
       const int tile = wave + 4 * (j0 + r);
       if (tile < tiles) {
-        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, g, use_quad, p.alpha, wlin);
+        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, wlin,
+                                                 Kind<KIND>::kSub ? wq : wlin);
         if (tile + 4 * RING < tiles) {
           const void* mrow;
           rows_of(tile + 4 * RING, mrow, vrow[r]);
-          sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, g, use_quad, st[r]);
+          sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -411,7 +424,8 @@ template <typename E, int D, int KIND>
 static hipError_t launch_ps(const PrefillArgs& a, const PsParams& sp) {
   if (sp.nb_pad <= kPsWgMaxBlocks) {
     dim3 grid(a.tokens, a.hkv, a.batch);
-    const size_t lds = sizeof(PsWgLds) + (size_t)sp.nb_pad * 17 * sizeof(float);
+    const size_t lds = sizeof(PsWgLds) + (size_t)sp.nb_pad * 17 * sizeof(float) +
+                       (Kind<KIND>::kSub ? (size_t)(D / 16) * 64 * sizeof(f32x4) : 0);
     hipLaunchKernelGGL((k_prefill_select_wg<E, D, KIND>), grid, dim3(256), lds, a.stream, sp);
     return hipGetLastError();
   }
@@ -425,6 +439,8 @@ template <typename E, int D>
 static hipError_t launch_ps_e(const PrefillArgs& a, const PsParams& sp) {
   if (a.so_kind == 0) return launch_ps<E, D, 0>(a, sp);
   if (a.so_kind == 3) return launch_ps<E, D, 3>(a, sp);
+  if (a.so_kind == 4) return launch_ps<E, D, 4>(a, sp);
+  if (a.so_kind == 5) return launch_ps<E, D, 5>(a, sp);
   return launch_ps<E, D, 1>(a, sp);
 }
 
@@ -433,7 +449,7 @@ hipError_t launch_prefill_select(const PrefillArgs& a) {
   sp.tokens = a.tokens; sp.hkv = a.hkv; sp.group = a.group; sp.max_len = a.max_len; sp.nb_max = a.nb_max;
   sp.nb_pad = (a.nb_max + 15) / 16 * 16; sp.top_k = a.top_k; sp.rank = a.rank; sp.q_pos0 = a.q_pos0;
   sp.L_fixed = a.max_len; sp.alpha = a.alpha; sp.scale = a.scale; sp.seq_lens = a.seq_lens; sp.Q = a.Q;
-  sp.mu = a.mu; sp.so = a.so; sp.sel = a.sel; sp.sel_score = a.sel_score;
+  sp.mu = a.mu; sp.so = a.so; sp.P = a.P; sp.sub_s = a.sub_s; sp.vlen = a.vlen; sp.sel = a.sel; sp.sel_score = a.sel_score;
   if (a.bf16) return a.head_dim == 128 ? launch_ps_e<EltBF16, 128>(a, sp) : launch_ps_e<EltBF16, 64>(a, sp);
   return a.head_dim == 128 ? launch_ps_e<EltF32, 128>(a, sp) : launch_ps_e<EltF32, 64>(a, sp);
 }

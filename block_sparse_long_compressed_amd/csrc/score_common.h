@@ -47,24 +47,34 @@ __device__ __forceinline__ void score_weights(const void* Q, size_t q_base, int 
 
 // Score kinds: 0 diagonal, 1 rank-r fp32, 2 exact masses (no summaries), 3 rank-r
 // in the compressed storage (bf16 mean; FP4 E2M1 vectors with one E8M0 exponent
-// per 32 entries, each lane's 32 codes contiguous: entry 16u + 4g + c at nibble
-// (g * d/16 + u) * 4 + c).
+// per 32 entries), 4 and 5 the rank-r kinds 1 and 3 with the vectors in a query
+// subspace (length vlen = the subspace dimension rounded up to 32; the quadratic
+// term contracts them with scale * P q instead of scale * q).  In the compressed
+// storage a vector of length n has its entry 16u + 4g + c at nibble
+// (g * n/16 + u) * 4 + c, so each lane's codes are contiguous.
+template <int KIND>
+struct Kind {
+  static constexpr bool kFp4 = KIND == 3 || KIND == 5;
+  static constexpr bool kSub = KIND == 4 || KIND == 5;
+  static constexpr bool kRank = KIND == 1 || KIND >= 3;
+};
 
 // Bytes of one block's compressed record: codes, exponents, padding to 16.
-__host__ __device__ constexpr size_t fp4_record_bytes_dev(int rank, int d) {
-  return ((size_t)rank * (d / 2 + d / 32) + 15) / 16 * 16;
+__host__ __device__ constexpr size_t fp4_record_bytes_dev(int rank, int n) {
+  return ((size_t)rank * (n / 2 + n / 32) + 15) / 16 * 16;
 }
 
-// Summary rows of block row `row` (mean, second-order) for a score kind.
+// Summary rows of block row `row` (mean, second-order) for a score kind; vlen is
+// the length of a rank-r vector (D without a subspace).
 template <int D, int KIND>
-__device__ __forceinline__ void summary_rows(const void* mu, const void* so, size_t row, int rank,
+__device__ __forceinline__ void summary_rows(const void* mu, const void* so, size_t row, int rank, int vlen,
                                              const void*& mr, const void*& vr) {
-  if constexpr (KIND == 3) {
+  if constexpr (Kind<KIND>::kFp4) {
     mr = static_cast<const uint16_t*>(mu) + row * D;
-    vr = static_cast<const uint8_t*>(so) + row * fp4_record_bytes_dev(rank, D);
+    vr = static_cast<const uint8_t*>(so) + row * fp4_record_bytes_dev(rank, vlen);
   } else {
     mr = static_cast<const float*>(mu) + row * D;
-    vr = static_cast<const float*>(so) + row * (KIND == 0 ? (size_t)D : (size_t)rank * D);
+    vr = static_cast<const float*>(so) + row * (KIND == 0 ? (size_t)D : (size_t)rank * vlen);
   }
 }
 
@@ -76,29 +86,45 @@ constexpr int kRankGroup = 4;
 
 template <int D, int KIND>
 struct SumTile {
-  f32x4 m4[KIND == 3 ? 1 : D / 16];
-  f32x4 v4[KIND == 1 ? kRankGroup : 1][KIND == 3 ? 1 : D / 16];
-  uint2 mb[KIND == 3 ? D / 16 : 1];          // bf16 mean columns 16u + 4g .. +3
-  u32x4 code[KIND == 3 ? kRankGroup : 1];    // this lane's D/4 codes of each vector of the group
-  uint32_t ex[KIND == 3 ? kRankGroup : 1];   // the vector's D/32 exponent bytes
+  static constexpr bool kF = Kind<KIND>::kFp4;
+  f32x4 m4[kF ? 1 : D / 16];
+  f32x4 v4[(KIND == 1 || KIND == 4) ? kRankGroup : 1][kF ? 1 : D / 16];
+  uint2 mb[kF ? D / 16 : 1];           // bf16 mean columns 16u + 4g .. +3
+  u32x4 code[kF ? kRankGroup : 1];     // this lane's vlen/4 codes of each vector of the group
+  uint32_t ex[kF ? kRankGroup : 1];    // the vector's vlen/32 exponent bytes
 };
 
 template <int D, int KIND>
-__device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, int rank, int g, SumTile<D, KIND>& t) {
-  if constexpr (KIND == 3) {
+__device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, int rank, int vlen, int g,
+                                                    SumTile<D, KIND>& t) {
+  if constexpr (Kind<KIND>::kFp4) {
     const uint8_t* rec = static_cast<const uint8_t*>(vrow);
 #pragma unroll
     for (int rr = 0; rr < kRankGroup; ++rr) {
       const int r = r0 + rr;
       if (r < rank) {
-        const uint8_t* cp = rec + r * (D / 2) + g * (D / 8);
-        if constexpr (D == 128) {
-          t.code[rr] = *reinterpret_cast<const u32x4*>(cp);
-          t.ex[rr] = *reinterpret_cast<const uint32_t*>(rec + rank * (D / 2) + r * (D / 32));
+        if constexpr (!Kind<KIND>::kSub) {
+          const uint8_t* cp = rec + r * (D / 2) + g * (D / 8);
+          if constexpr (D == 128) {
+            t.code[rr] = *reinterpret_cast<const u32x4*>(cp);
+            t.ex[rr] = *reinterpret_cast<const uint32_t*>(rec + rank * (D / 2) + r * (D / 32));
+          } else {
+            const uint2 c2 = *reinterpret_cast<const uint2*>(cp);
+            t.code[rr] = u32x4{c2.x, c2.y, 0u, 0u};
+            t.ex[rr] = *reinterpret_cast<const uint16_t*>(rec + rank * (D / 2) + r * (D / 32));
+          }
         } else {
-          const uint2 c2 = *reinterpret_cast<const uint2*>(cp);
-          t.code[rr] = u32x4{c2.x, c2.y, 0u, 0u};
-          t.ex[rr] = *reinterpret_cast<const uint16_t*>(rec + rank * (D / 2) + r * (D / 32));
+          // vlen/32 code words per lane and vlen/32 exponent bytes per vector
+          const int nw = vlen / 32;
+          const uint32_t* cp = reinterpret_cast<const uint32_t*>(rec + r * (vlen / 2) + g * (vlen / 8));
+          const uint8_t* ep = rec + rank * (vlen / 2) + r * nw;
+          uint32_t ex = 0;
+#pragma unroll
+          for (int w = 0; w < D / 32; ++w) {
+            t.code[rr][w] = w < nw ? cp[w] : 0u;
+            ex |= w < nw ? (uint32_t)ep[w] << (8 * w) : 0u;
+          }
+          t.ex[rr] = ex;
         }
       }
     }
@@ -108,7 +134,8 @@ __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, in
     for (int rr = 0; rr < kRankGroup; ++rr) {
       if (r0 + rr < rank) {
 #pragma unroll
-        for (int u = 0; u < D / 16; ++u) t.v4[rr][u] = ld_f32x4(vr + (r0 + rr) * D + 16 * u + 4 * g);
+        for (int u = 0; u < D / 16; ++u)
+          if (!Kind<KIND>::kSub || 16 * u < vlen) t.v4[rr][u] = ld_f32x4(vr + (r0 + rr) * vlen + 16 * u + 4 * g);
       }
     }
   }
@@ -116,13 +143,13 @@ __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, in
 
 // Issue the loads of one tile (mrow / vrow: this lane's block row).
 template <int D, int KIND>
-__device__ __forceinline__ void sum_tile_load(const void* mrow, const void* vrow, int rank, int g, bool use_quad,
-                                              SumTile<D, KIND>& t) {
-  if constexpr (KIND == 3) {
+__device__ __forceinline__ void sum_tile_load(const void* mrow, const void* vrow, int rank, int vlen, int g,
+                                              bool use_quad, SumTile<D, KIND>& t) {
+  if constexpr (Kind<KIND>::kFp4) {
     const uint16_t* mr = static_cast<const uint16_t*>(mrow);
 #pragma unroll
     for (int u = 0; u < D / 16; ++u) t.mb[u] = *reinterpret_cast<const uint2*>(mr + 16 * u + 4 * g);
-    if (use_quad) sum_tile_load_group<D, KIND>(vrow, 0, rank, g, t);
+    if (use_quad) sum_tile_load_group<D, KIND>(vrow, 0, rank, vlen, g, t);
   } else {
     const float* mr = static_cast<const float*>(mrow);
 #pragma unroll
@@ -133,7 +160,7 @@ __device__ __forceinline__ void sum_tile_load(const void* mrow, const void* vrow
 #pragma unroll
         for (int u = 0; u < D / 16; ++u) t.v4[0][u] = ld_f32x4(vr + 16 * u + 4 * g);
       } else {
-        sum_tile_load_group<D, KIND>(vrow, 0, rank, g, t);
+        sum_tile_load_group<D, KIND>(vrow, 0, rank, vlen, g, t);
       }
     }
   }
@@ -146,18 +173,22 @@ __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_fl
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Scores (without ln n_b) of the tile's 16 blocks for the group's heads from the
-// loaded rows.  Linear and quadratic terms are independent MFMA chains.
+// loaded rows.  Linear and quadratic terms are independent MFMA chains.  wlin are
+// the linear weights scale * q; wq the weights the rank-r vectors are contracted
+// with (wlin, or scale * P q for the subspace kinds).
 template <int D, int KIND>
-__device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void* vrow, int rank, int g, bool use_quad,
-                                                float alpha, const float (&wlin)[D / 16][4]) {
+__device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void* vrow, int rank, int vlen, int g,
+                                                bool use_quad, float alpha, const float (&wlin)[D / 16][4],
+                                                const float (&wq)[D / 16][4]) {
   constexpr int NU = D / 16;
+  constexpr bool kSub = Kind<KIND>::kSub;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float m;
-      if constexpr (KIND == 3) {
+      if constexpr (Kind<KIND>::kFp4) {
         const uint32_t w = (c < 2) ? t.mb[u].x : t.mb[u].y;
         m = (c & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
       } else {
@@ -176,20 +207,21 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
         acc2 = mfma_f32_16x16x4(t.v4[0][u][c], 0.5f * alpha * w * w, acc2);   // alpha/2 scale^2 q^2
       }
     }
-  } else if constexpr (KIND == 3) {
+  } else if constexpr (Kind<KIND>::kFp4) {
     // (v_i . q)^2 with v_i decoded on the fly by the hardware FP4 conversion: entry
     // 16u + 4g + c is nibble u*4 + c of this lane's codes, scaled by the exponent of
     // group u/2 of this lane's block (the scale must be applied on the A side: an
     // output row belongs to another lane's block)
 #pragma unroll 1
     for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
-      if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, g, t);
+      if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, vlen, g, t);
 #pragma unroll
       for (int rr = 0; rr < kRankGroup; ++rr) {
         if (r0 + rr < rank) {
           f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
+            if (kSub && 16 * u >= vlen) break;
             // codes of columns 16u + 4g + {0,1} and {2,3}: bytes 2(u&1) and 2(u&1)+1 of word u/2;
             // group u/2's exponent (columns 16u + 4g + c share group u/2)
             const uint32_t w = t.code[rr][u >> 1];
@@ -205,8 +237,8 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
             const float v[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              if (u & 1) pr2 = mfma_f32_16x16x4(v[c], wlin[u][c], pr2);
-              else pr = mfma_f32_16x16x4(v[c], wlin[u][c], pr);
+              if (u & 1) pr2 = mfma_f32_16x16x4(v[c], wq[u][c], pr2);
+              else pr = mfma_f32_16x16x4(v[c], wq[u][c], pr);
             }
           }
 #pragma unroll
@@ -219,20 +251,21 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
     }
   } else {
     // (v_i . q)^2 for each scaled eigenvector v_i: the projection is a linear MFMA
-    // chain with the linear weights, squared on the VALU
+    // chain with the weights, squared on the VALU
 #pragma unroll 1
     for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
-      if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, g, t);
+      if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, vlen, g, t);
 #pragma unroll
       for (int rr = 0; rr < kRankGroup; ++rr) {
         if (r0 + rr < rank) {
           f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int u = 0; u < NU; u += 2) {
+            if (kSub && 16 * u >= vlen) break;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              pr = mfma_f32_16x16x4(t.v4[rr][u][c], wlin[u][c], pr);
-              pr2 = mfma_f32_16x16x4(t.v4[rr][u + 1][c], wlin[u + 1][c], pr2);
+              pr = mfma_f32_16x16x4(t.v4[rr][u][c], wq[u][c], pr);
+              pr2 = mfma_f32_16x16x4(t.v4[rr][u + 1][c], wq[u + 1][c], pr2);
             }
           }
 #pragma unroll
@@ -249,11 +282,57 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
 
 // Load and score one tile in one step.
 template <int D, int KIND>
-__device__ __forceinline__ f32x4 score_tile(const void* mrow, const void* vrow, int rank, int g, bool use_quad,
-                                            float alpha, const float (&wlin)[D / 16][4]) {
+__device__ __forceinline__ f32x4 score_tile(const void* mrow, const void* vrow, int rank, int vlen, int g,
+                                            bool use_quad, float alpha, const float (&wlin)[D / 16][4],
+                                            const float (&wq)[D / 16][4]) {
   SumTile<D, KIND> t;
-  sum_tile_load<D, KIND>(mrow, vrow, rank, g, use_quad, t);
-  return sum_tile_score<D, KIND>(t, vrow, rank, g, use_quad, alpha, wlin);
+  sum_tile_load<D, KIND>(mrow, vrow, rank, vlen, g, use_quad, t);
+  return sum_tile_score<D, KIND>(t, vrow, rank, vlen, g, use_quad, alpha, wlin, wq);
+}
+
+// Quadratic weights of the subspace kinds, scale * P q, in the B-operand layout:
+// wq[u][c] of lane (n, g) = scale * (P q_n)[16u + 4g + c] for column tiles u < vlen/16
+// (rows of P at or beyond s are zero).  The contraction over d is an MFMA chain whose
+// A operand is P's row 16u + n and whose B operand is the linear weights, so the
+// output (rows 16u + 4g + i, column n) lands in exactly this layout.  Column tiles
+// are split over `nparts` waves (this one computes u = part, part + nparts, ...) and
+// exchanged through `xch` ([D/16][64] f32x4 in LDS) when nparts > 1; the caller
+// synchronises the waves between the two halves.
+template <int D>
+__device__ __forceinline__ void subspace_weights_part(const float* P, int s, int vlen, int part, int nparts, int n,
+                                                      int g, const float (&wlin)[D / 16][4], f32x4* xch,
+                                                      float (&wq)[D / 16][4]) {
+  constexpr int NU = D / 16;
+  const int lane = 16 * g + n;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (16 * u >= vlen || u % nparts != part) continue;
+    const int row = 16 * u + n;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+      const f32x4 p4 = row < s ? ld_f32x4(P + (size_t)row * D + 16 * j + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(p4[c], wlin[j][c], acc);
+    }
+    if (nparts > 1) xch[u * 64 + lane] = acc;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wq[u][c] = acc[c];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void subspace_weights_gather(int vlen, int part, int nparts, int n, int g,
+                                                        const f32x4* xch, float (&wq)[D / 16][4]) {
+  constexpr int NU = D / 16;
+  const int lane = 16 * g + n;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (16 * u >= vlen || u % nparts == part) continue;
+    const f32x4 v = xch[u * 64 + lane];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wq[u][c] = v[c];
+  }
 }
 
 // Number of candidate blocks (a prefix [0, n)) for a query at position t of a

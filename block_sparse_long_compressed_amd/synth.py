@@ -55,6 +55,8 @@ class Workload:
     n_q_tokens: int = 1     # 1 = decode at t = L-1; >1 = prefill chunk
     q_pos0: int = -1        # prefill: position of the first query token
     gates: bool = True      # False -> only the selected-block branch (gates 0,1,0)
+    subspace: int = 0       # query-subspace dimension s of the low-rank kinds (0 = off)
+    n_calib: int = 512      # calibration query tokens drawn when subspace > 0
 
     @property
     def group(self) -> int:
@@ -87,6 +89,9 @@ WORKLOADS = {
     # the same with the compressed summary storage (bf16 mean, MX FP4 eigenvectors).
     "decode_b8_L128k_rank4_fp4": Workload("decode_b8_L128k_rank4_fp4", 8, 131072, 131072, 32, 8, 128,
                                           32, 1024, 32, 16, "lowrank_fp4", 4, 1.0, "bf16", 16),
+    # the same with the rank-4 FP4 vectors in an 85-dimensional query subspace.
+    "decode_b8_L128k_sub85_fp4": Workload("decode_b8_L128k_sub85_fp4", 8, 131072, 131072, 32, 8, 128,
+                                          32, 1024, 32, 16, "lowrank_fp4", 4, 1.0, "bf16", 16, subspace=85),
 }
 
 
@@ -120,6 +125,8 @@ def make_inputs(w: Workload, seed: int, lens: Optional[np.ndarray] = None) -> di
       gates  [B][T][Hq][3] in order (compressed, selected, window), or None
       lens   [B] int32
       needles list of (seq, kv_head, position, q_head, token)
+      Qcal   [n_calib][Hq][d] calibration queries, or None   (subspace > 0)
+      P      [Hkv][s][d] seeded orthonormal rows, or None     (subspace > 0)
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     B, T, Hq, Hkv, d, Lm = w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim, w.max_len
@@ -148,6 +155,26 @@ def make_inputs(w: Workload, seed: int, lens: Optional[np.ndarray] = None) -> di
     for s in range(B):
         V[s, :, int(lens[s]):] = 0.0
 
+    Qcal = P = None
+    if w.subspace:
+        # Queries of each kv-head group concentrated near an s-dimensional subspace:
+        # q = U_h diag(sigma) z with a random orthonormal U_h and sigma_j proportional
+        # to exp(-2j/s) (98% of E|q|^2 in the first s directions), scaled to E|q|^2 = d.
+        # Calibration tokens come from the same distribution.  P is a seeded random
+        # orthonormal [s][d] per kv-head, an input the parity tests hand to both sides.
+        sig = np.exp(-2.0 * np.arange(d) / w.subspace)
+        sig *= math.sqrt(d / float((sig * sig).sum()))
+        Qcal = rng.standard_normal((w.n_calib, Hq, d)).astype(np.float32)
+        P = np.zeros((Hkv, w.subspace, d), dtype=np.float32)
+        for h in range(Hkv):
+            U = np.linalg.qr(rng.standard_normal((d, d)))[0]
+            hs = slice(h * G, (h + 1) * G)
+            Q[:, :, hs] = ((Q[:, :, hs].astype(np.float64) * sig) @ U.T).astype(np.float32)
+            Qcal[:, hs] = ((Qcal[:, hs].astype(np.float64) * sig) @ U.T).astype(np.float32)
+            P[h] = np.linalg.qr(rng.standard_normal((d, w.subspace)))[0].T.astype(np.float32)
+        if w.dtype == "bf16":
+            round_bf16(Qcal)
+
     if w.dtype == "bf16":
         round_bf16(Q)
         # needle direction is taken from the bf16 query so it is exact on both sides
@@ -171,5 +198,5 @@ def make_inputs(w: Workload, seed: int, lens: Optional[np.ndarray] = None) -> di
         round_bf16(K)
         round_bf16(V)
     return {"Q": Q, "K": K, "V": V, "gates": gates, "lens": lens, "needles": needles,
-            "workload": w, "seed": seed}
+            "workload": w, "seed": seed, "Qcal": Qcal, "P": P}
 

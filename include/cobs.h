@@ -88,6 +88,17 @@ typedef struct cobs_params {
   float alpha;          /* >= 0; 0 = first-order (mean-pool) selector */
   float scale;          /* logit scale > 0; 0 selects 1/sqrt(head_dim) */
   int32_t kv_dtype;     /* cobs_dtype of Q, K, V and the pooled tokens */
+  /* Query-subspace projection of the second-order channel (COBS Technisches
+   * Resuemee 2.3, "Subraum-Projektion"; low-rank kinds only).  subspace_dim = s in
+   * [1, head_dim] projects each block covariance into the span of the rows of
+   * `subspace`, C' = P C P^T, and stores the top-r scaled eigenvectors of C' with
+   * length vlen = s rounded up to 32 (zeros beyond s); the quadratic term becomes
+   * sum_i ((P q) . v_i)^2 while the linear term keeps the full q . mu.  0 = off
+   * (vlen = head_dim; `subspace` is ignored). */
+  int32_t subspace_dim;
+  const float* subspace; /* DEVICE [H_kv][s][d] fp32, rows orthonormal (e.g. from
+                          * cobs_query_subspace); caller-owned, read by the build,
+                          * update, selection, decode and prefill calls */
 } cobs_params;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -96,7 +107,8 @@ const char* cobs_status_string(int32_t status);
 /* Checks `p` alone.  Host only. */
 cobs_status cobs_validate_params(const cobs_params* p);
 
-/* Sizes of the caller-allocated summary tensors for a [batch][H_kv][max_len][d] KV cache:
+/* Sizes of the caller-allocated summary tensors for a [batch][H_kv][max_len][d] KV cache
+ * (with a query subspace, every rank-r vector below has length vlen instead of d):
  * mu [batch][H_kv][NB][d] f32, so (diag) [batch][H_kv][NB][d] f32 or
  * so (lowrank) [batch][H_kv][NB][rank][d] f32, pooled tokens kc/vc
  * [batch][H_kv][NC][d] of kv_dtype, with NB = ceil(max_len/64) and
@@ -221,6 +233,21 @@ cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int3
                                      const void* kc, const void* vc, const float* gates,
                                      int32_t* sel_out, float* out,
                                      void* ws, size_t ws_bytes, void* stream);
+
+/* Query subspace from calibration queries (COBS Technisches Resuemee 2.3,
+ * "Subraum-Projektion": the span of the top eigenvectors of the queries' second
+ * moment).  For each kv-head group, M = (1/N) sum q q^T over the group's heads of
+ * every calibration token (uncentred, fp64), and P_out[h] = its top-s eigenvectors
+ * (s = p->subspace_dim >= 1) as rows, largest eigenvalue first, each signed so its
+ * largest-magnitude entry is positive; ties in the ranking go to the lower index.
+ *   Q      [n_tokens][H_q][d] kv_dtype, DEVICE
+ *   P_out  [H_kv][s][d] fp32 out, DEVICE (the buffer to pass as p->subspace)
+ *   ws     DEVICE workspace of at least cobs_query_subspace_workspace_bytes(p)
+ * p->subspace is not read.  Errors: INVALID_ARG (null pointer, n_tokens < 1,
+ * subspace_dim < 1 or > head_dim, a diagonal so_kind), WORKSPACE, HIP. */
+size_t cobs_query_subspace_workspace_bytes(const cobs_params* p);
+cobs_status cobs_query_subspace(const cobs_params* p, int32_t n_tokens, const void* Q, float* P_out,
+                                void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

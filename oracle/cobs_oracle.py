@@ -39,6 +39,14 @@ reason in the design notes of the repository):
     consecutive entries, the scale and rounding of the OCP microscaling (MX)
     format: X = 2^(floor(log2 max|v|) - 2), entries round to the nearest of
     {0, .5, 1, 1.5, 2, 3, 4, 6} * X (ties to the even code), saturating at 6X;
+  * the query-subspace projection of [COBS] 2.3 ("Subraum-Projektion") takes
+    P [s][d] = the top-s eigenvectors of the queries' uncentred second moment
+    E[q q^T] (rows signed so the largest-magnitude entry is positive), projects
+    each block covariance into that subspace, C' = P kappa_2 P^T (s x s), and
+    keeps the top-r scaled eigenvectors of C' (length s); the quadratic term is
+    then sum_i ((P q) . v_i)^2, the linear term stays q . mu in full dimension;
+    with the compressed storage the length-s vectors are padded with zeros to a
+    multiple of 32 before the MX quantization;
   * a GQA group ranks blocks by the sum over its heads of each head's
     estimated share of attention mass (softmax of the scores over candidates);
   * ties go to the lower block index; fewer candidates than k -> pad with -1;
@@ -88,19 +96,15 @@ def diag_second_order(keys: np.ndarray) -> np.ndarray:
     return np.diag(block_covariance(keys)).copy()
 
 
-def lowrank_second_order(keys: np.ndarray, rank: int) -> np.ndarray:
-    """Low-rank compression of kappa_2 ([COBS] 2.3, "Low-Rank-Faktorisierung").
-
-    Keeps the `rank` largest eigenpairs (lambda_i, u_i) of the block covariance
-    and stores the scaled eigenvectors v_i = sqrt(lambda_i) * u_i, so that
-    sum_i v_i v_i^T is the best rank-r approximation of kappa_2.  Eigenvalues
-    <= 0 give v_i = 0.  Each v_i is signed so its largest-magnitude entry is
-    positive (sign is irrelevant to the score; fixed only for reporting).
-    Returns [rank][d]."""
-    cov = block_covariance(keys)
+def top_scaled_eigenvectors(cov: np.ndarray, rank: int) -> np.ndarray:
+    """The `rank` largest eigenpairs (lambda_i, u_i) of a symmetric PSD matrix as
+    v_i = sqrt(lambda_i) * u_i ([COBS] 2.3, "Low-Rank-Faktorisierung"), so that
+    sum_i v_i v_i^T is its best rank-r approximation.  Eigenvalues <= 0 give
+    v_i = 0.  Each v_i is signed so its largest-magnitude entry is positive (sign
+    is irrelevant to the score; fixed only for reporting).  Returns [rank][n]."""
     lam, U = np.linalg.eigh(cov)            # ascending eigenvalues
     order = np.argsort(-lam, kind="stable")[:rank]
-    out = np.zeros((rank, keys.shape[1]))
+    out = np.zeros((rank, cov.shape[0]))
     for i, j in enumerate(order):
         if lam[j] > 0.0:
             v = np.sqrt(lam[j]) * U[:, j]
@@ -108,6 +112,31 @@ def lowrank_second_order(keys: np.ndarray, rank: int) -> np.ndarray:
                 v = -v
             out[i] = v
     return out
+
+
+def lowrank_second_order(keys: np.ndarray, rank: int) -> np.ndarray:
+    """Low-rank compression of kappa_2: its top-r scaled eigenvectors, [rank][d]."""
+    return top_scaled_eigenvectors(block_covariance(keys), rank)
+
+
+def query_subspace(queries: np.ndarray, s: int) -> np.ndarray:
+    """Query subspace of [COBS] 2.3 ("Subraum-Projektion"): the top-s eigenvectors
+    of the queries' second moment M = (1/N) sum q q^T (uncentred), as the rows of
+    P [s][d], each signed so its largest-magnitude entry is positive."""
+    M = queries.T @ queries / queries.shape[0]
+    lam, U = np.linalg.eigh(M)
+    order = np.argsort(-lam, kind="stable")[:s]
+    P = U[:, order].T.copy()
+    for i in range(s):
+        if P[i, np.argmax(np.abs(P[i]))] < 0:
+            P[i] = -P[i]
+    return P
+
+
+def subspace_second_order(keys: np.ndarray, rank: int, P: np.ndarray) -> np.ndarray:
+    """kappa_2 projected into the query subspace, C' = P kappa_2 P^T, compressed to
+    its top-r scaled eigenvectors: [rank][s]."""
+    return top_scaled_eigenvectors(P @ block_covariance(keys) @ P.T, rank)
 
 
 # FP4 E2M1 magnitudes by code (sign in the fourth bit): 0, .5, 1, 1.5, 2, 3, 4, 6
@@ -177,27 +206,38 @@ def dequantize_mxfp4(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
     return mag * np.repeat(2.0 ** exps.astype(np.float64), MX_GROUP)
 
 
-def summaries(keys: np.ndarray, L: int, so_kind: str, rank: int = 0):
+def summaries(keys: np.ndarray, L: int, so_kind: str, rank: int = 0, P: np.ndarray | None = None):
     """Per-block summaries of one (sequence, kv-head): (mu [NB][d], so, n [NB]).
 
     so is [NB][d] for 'diag', [NB][rank][d] for 'lowrank' and for 'lowrank_fp4'
-    (whose mean and vectors are the stored, rounded values)."""
+    (whose mean and vectors are the stored, rounded values).  With a query
+    subspace P [s][d] (low-rank kinds only) the vectors have length s."""
     n = block_sizes(L)
     mu, so = [], []
     for b, nb in enumerate(n):
         kb = keys[b * BLOCK: b * BLOCK + nb]
         m = block_mean(kb)
         if so_kind == "diag":
+            assert P is None, "the query subspace applies to the low-rank kinds"
             so.append(diag_second_order(kb))
-        elif so_kind == "lowrank":
-            so.append(lowrank_second_order(kb, rank))
-        elif so_kind == "lowrank_fp4":
-            m = round_bf16(m)
-            so.append(np.array([dequantize_mxfp4(*quantize_mxfp4(v)) for v in lowrank_second_order(kb, rank)]))
+        elif so_kind in ("lowrank", "lowrank_fp4"):
+            v = lowrank_second_order(kb, rank) if P is None else subspace_second_order(kb, rank, P)
+            if so_kind == "lowrank_fp4":
+                m = round_bf16(m)
+                v = np.array([quantize_dequantize_padded(x) for x in v])
+            so.append(v)
         else:
             raise ValueError(so_kind)
         mu.append(m)
     return np.array(mu), np.array(so), n
+
+
+def quantize_dequantize_padded(v: np.ndarray) -> np.ndarray:
+    """The stored value of a vector in the compressed storage: zero-padded to a
+    multiple of the MX group, quantized, dequantized, cut back to its length."""
+    pad = -len(v) % MX_GROUP
+    x = np.concatenate([v, np.zeros(pad)])
+    return dequantize_mxfp4(*quantize_mxfp4(x))[:len(v)]
 
 
 def compressed_tokens(x: np.ndarray, L: int, cmp_len: int = 32, cmp_stride: int = 16) -> np.ndarray:
@@ -220,20 +260,22 @@ def attention_mass(q: np.ndarray, keys: np.ndarray, scale: float) -> float:
 
 
 def block_scores(q: np.ndarray, mu: np.ndarray, so: np.ndarray, n: np.ndarray,
-                 alpha: float, scale: float, so_kind: str) -> np.ndarray:
+                 alpha: float, scale: float, so_kind: str, P: np.ndarray | None = None) -> np.ndarray:
     """Cumulant estimate of ln m_b for every query head and block ([COBS] 2.2, 2.3):
 
         s[h, b] = ln n_b + scale * q_h . mu_b + alpha * 1/2 * scale^2 * q_h^T S_b q_h
 
-    with S_b = diag(so_b) ('diag') or sum_i so_b[i] so_b[i]^T ('lowrank').
-    q is [H][d]; returns [H][NB]."""
+    with S_b = diag(so_b) ('diag') or sum_i so_b[i] so_b[i]^T ('lowrank'); with a
+    query subspace P the quadratic term is (P q_h)^T S_b (P q_h), S_b built from
+    the length-s vectors.  q is [H][d]; returns [H][NB]."""
     lin = scale * (q @ mu.T)
     if so_kind == "lowrank_fp4":
         so_kind = "lowrank"                                    # the stored vectors, dequantized
     if so_kind == "diag":
         quad = (q * q) @ so.T                                  # sum_j q_j^2 var_j
     else:
-        proj = np.einsum("hd,brd->hbr", q, so)                 # q . v_{b,i}
+        qp = q if P is None else q @ P.T                       # coordinates of q in the subspace
+        proj = np.einsum("hd,brd->hbr", qp, so)                # q . v_{b,i}
         quad = (proj * proj).sum(axis=2)
     return np.log(n.astype(np.float64))[None, :] + lin + alpha * 0.5 * scale * scale * quad
 
@@ -299,7 +341,7 @@ def query_group(p: dict, qg: np.ndarray, keys: np.ndarray, vals: np.ndarray, L: 
     G = qg.shape[0]
     k = p["top_k"]
     if len(cand) > 0:
-        s = block_scores(qg, mu[cand], so[cand], n[cand], p["alpha"], scale, p["so_kind"])
+        s = block_scores(qg, mu[cand], so[cand], n[cand], p["alpha"], scale, p["so_kind"], p.get("P"))
         shat = group_scores(s)
         pick, gap = select_topk(shat, k)
         sel = np.array([cand[i] if i >= 0 else -1 for i in pick], dtype=np.int64)
@@ -336,7 +378,7 @@ def params_of(w, scale: float | None = None, alpha: float | None = None) -> dict
 
 def build_unit(p: dict, keys: np.ndarray, vals: np.ndarray, L: int):
     """Summaries and compressed tokens of one (sequence, kv-head)."""
-    summ = summaries(keys[:L], L, p["so_kind"], p["rank"])
+    summ = summaries(keys[:L], L, p["so_kind"], p["rank"], p.get("P"))
     if p["cmp_len"] > 0:
         kc = compressed_tokens(keys, L, p["cmp_len"], p["cmp_stride"])
         vc = compressed_tokens(vals, L, p["cmp_len"], p["cmp_stride"])
@@ -346,7 +388,8 @@ def build_unit(p: dict, keys: np.ndarray, vals: np.ndarray, L: int):
 
 
 def run(inputs: dict, p: dict, seqs=None, groups=None, tokens=None):
-    """Oracle over a batch (decode: t = L-1; prefill: t = q_pos0 + i).
+    """Oracle over a batch (decode: t = L-1; prefill: t = q_pos0 + i).  When the
+    inputs carry query subspaces P [H_kv][s][d], group g scores with P[g].
 
     Returns a dict keyed by (seq, group, token) with out [G][d], sel [k],
     shat (over candidates), gap; only the requested subsets are computed."""
@@ -355,19 +398,21 @@ def run(inputs: dict, p: dict, seqs=None, groups=None, tokens=None):
     seqs = range(B) if seqs is None else seqs
     groups = range(Hkv) if groups is None else groups
     res = {}
+    subspace = inputs.get("P")                  # [H_kv][s][d] query subspaces, or None
     for s in seqs:
         L = int(inputs["lens"][s])
         for g in groups:
+            pg = p if subspace is None else dict(p, P=np.asarray(subspace[g], dtype=np.float64))
             keys = inputs["K"][s, g, :L].astype(np.float64)
             vals = inputs["V"][s, g, :L].astype(np.float64)
-            summ, kc, vc = build_unit(p, keys, vals, L)
+            summ, kc, vc = build_unit(pg, keys, vals, L)
             toks = range(w.n_q_tokens) if tokens is None else tokens
             for i in toks:
                 t = (w.q_pos0 + i) if w.prefill else L - 1
                 qg = inputs["Q"][s, i, g * G:(g + 1) * G].astype(np.float64)
                 gt = inputs["gates"][s, i, g * G:(g + 1) * G].astype(np.float64) \
                     if inputs["gates"] is not None else None
-                res[(s, g, i)] = query_group(p, qg, keys, vals, L, t, summ, kc, vc, gt)
+                res[(s, g, i)] = query_group(pg, qg, keys, vals, L, t, summ, kc, vc, gt)
     return res
 
 

@@ -11,13 +11,14 @@ GAP = 1e-3          # score gap (natural-log units) below which several selectio
 SO_KINDS = {"diag": B.COBS_SO_DIAG, "lowrank": B.COBS_SO_LOWRANK, "lowrank_fp4": B.COBS_SO_LOWRANK_FP4}
 
 
-def params_for(w, alpha=None, top_k=None):
+def params_for(w, alpha=None, top_k=None, P=None):
+    """Parameters of a workload; P (device [H_kv][s][d] fp32) for the subspace kinds."""
     return B.make_params(w.head_dim, w.n_q_heads, w.n_kv_heads, w.top_k if top_k is None else top_k,
                          window=w.window, cmp_len=w.cmp_len, cmp_stride=w.cmp_stride,
                          so_kind=SO_KINDS[w.so_kind],
                          rank=0 if w.so_kind == "diag" else w.rank,
                          alpha=w.alpha if alpha is None else alpha,
-                         kv_dtype=B.COBS_BF16 if w.dtype == "bf16" else B.COBS_F32)
+                         kv_dtype=B.COBS_BF16 if w.dtype == "bf16" else B.COBS_F32, subspace=P)
 
 
 def to_device(x: dict, dev="cuda") -> dict:
@@ -26,6 +27,9 @@ def to_device(x: dict, dev="cuda") -> dict:
     g = {"K": torch.from_numpy(x["K"]).to(dev).to(dt).contiguous(),
          "V": torch.from_numpy(x["V"]).to(dev).to(dt).contiguous(),
          "lens": torch.from_numpy(x["lens"]).to(dev).contiguous()}
+    if x.get("P") is not None:                 # query subspaces (an input of the subspace kinds)
+        g["P"] = torch.from_numpy(x["P"]).to(dev).contiguous()
+        g["Qcal"] = torch.from_numpy(x["Qcal"]).to(dev).to(dt).contiguous()
     q = torch.from_numpy(x["Q"]).to(dev).to(dt)
     if w.prefill:                      # one sequence: Q [T][Hq][d], gates [T][Hq][3]
         g["Q"] = q[0].contiguous()

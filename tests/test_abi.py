@@ -129,3 +129,50 @@ def test_status_strings():
     assert B.status_string(0) == "ok"
     assert "workspace" in B.status_string(3)
     assert B.status_string(99) == "unknown status"
+
+
+def test_subspace_params_validated():
+    p = B.make_params(128, 8, 2, 8, so_kind=B.COBS_SO_LOWRANK, rank=4)
+    fake = 0x1000                                  # never dereferenced by validation
+    p.subspace_dim, p.subspace = 85, fake
+    assert B.cobs_validate_params(p) == B.COBS_OK
+    p.subspace = None
+    assert B.cobs_validate_params(p) == B.COBS_ERR_INVALID_ARG     # dimension without a subspace
+    p.subspace, p.subspace_dim = fake, 129
+    assert B.cobs_validate_params(p) == B.COBS_ERR_INVALID_ARG     # more than head_dim
+    p.subspace_dim = -1
+    assert B.cobs_validate_params(p) == B.COBS_ERR_INVALID_ARG
+    p.subspace_dim, p.so_kind, p.rank = 40, B.COBS_SO_DIAG, 0
+    assert B.cobs_validate_params(p) == B.COBS_ERR_INVALID_ARG     # diagonal kind has no vectors
+    p.subspace_dim = 0
+    assert B.cobs_validate_params(p) == B.COBS_OK                  # pointer ignored when off
+
+
+@pytest.mark.parametrize("kind,s,so_bytes", [
+    (B.COBS_SO_LOWRANK, 85, 3 * 2 * 16 * 4 * 96 * 4),     # vectors of length 96 (85 rounded up to 32)
+    (B.COBS_SO_LOWRANK, 32, 3 * 2 * 16 * 4 * 32 * 4),
+    (B.COBS_SO_LOWRANK_FP4, 85, 3 * 2 * 16 * 208),         # 4 * (48 + 3) = 204 -> 208
+    (B.COBS_SO_LOWRANK_FP4, 20, 3 * 2 * 16 * 80),          # 4 * (16 + 1) = 68 -> 80
+])
+def test_summary_shapes_subspace(kind, s, so_bytes):
+    p = B.make_params(128, 8, 2, 8, so_kind=kind, rank=4)
+    p.subspace_dim, p.subspace = s, 0x1000
+    sh = B.cobs_summary_shapes(p, 3, 1000)
+    assert sh["so_bytes"] == so_bytes
+    assert sh["mu_bytes"] == 3 * 2 * 16 * 128 * (2 if kind == B.COBS_SO_LOWRANK_FP4 else 4)
+
+
+def test_query_subspace_rejects_bad_calls():
+    lib = B.lib()
+    p = B.make_params(128, 8, 2, 8, so_kind=B.COBS_SO_LOWRANK, rank=4)
+    p.subspace_dim = 16
+    n = lib.cobs_query_subspace_workspace_bytes(ctypes.byref(p))
+    assert n == 2 * 2 * 128 * 128 * 8
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.cobs_query_subspace(ctypes.byref(p), 0, fake, fake, fake, n, None) == B.COBS_ERR_INVALID_ARG
+    assert lib.cobs_query_subspace(ctypes.byref(p), 10, fake, None, fake, n, None) == B.COBS_ERR_INVALID_ARG
+    assert lib.cobs_query_subspace(ctypes.byref(p), 10, fake, fake, fake, n - 1, None) == B.COBS_ERR_WORKSPACE
+    p.subspace_dim = 0
+    assert lib.cobs_query_subspace(ctypes.byref(p), 10, fake, fake, fake, n, None) == B.COBS_ERR_INVALID_ARG
+    p.subspace_dim, p.so_kind, p.rank = 16, B.COBS_SO_DIAG, 0
+    assert lib.cobs_query_subspace(ctypes.byref(p), 10, fake, fake, fake, n, None) == B.COBS_ERR_INVALID_ARG

@@ -62,39 +62,55 @@ def unpack_records(rec: np.ndarray, rank: int, d: int):
 
 
 def check_fp4(w, x, s, units=None, gap_min=1e-2):
+    """Compressed summaries against the oracle's (see the module docstring); with a
+    query subspace (w.subspace > 0, P = x["P"]) the vectors are those of P C P^T,
+    stored with length vlen = s rounded up to 32."""
     p = O.params_of(w)
     d, r, G = w.head_dim, w.rank, w.group
+    vlen = -(-w.subspace // 32) * 32 if w.subspace else d
     mu = s["mu"].float().cpu().numpy().astype(np.float64)
-    codes, exps = unpack_records(s["so"].cpu().numpy(), r, d)
+    codes, exps = unpack_records(s["so"].cpu().numpy(), r, vlen)
     units = units or [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
     strict = loose = exempt = total = mu_equal = mu_total = 0
     for (b, h) in units:
         L = int(x["lens"][b])
         keys = x["K"][b, h, :L].astype(np.float64)
-        rmu, rso, n = O.summaries(keys, L, "lowrank_fp4", r)
+        Ph = None if not w.subspace else x["P"][h].astype(np.float64)
+        rmu, rso, n = O.summaries(keys, L, "lowrank_fp4", r, Ph)
         nb = len(n)
         ulp = np.maximum(np.abs(rmu), 1e-38) * 2.0 ** -7
         assert (np.abs(mu[b, h, :nb] - rmu) <= ulp * 1.0001).all(), (b, h)
         mu_equal += int((mu[b, h, :nb] == rmu).sum())
         mu_total += rmu.size
         q = x["Q"][b, 0, h * G:(h + 1) * G].astype(np.float64) * p["scale"]
+        if Ph is not None:
+            q = q @ Ph.T                                          # coordinates in the subspace
         for blk in range(nb):
             kb = keys[blk * 64: blk * 64 + n[blk]]
-            lam = np.sort(np.linalg.eigvalsh(O.block_covariance(kb)))[::-1]
-            v_ref = O.lowrank_second_order(kb, r)
+            C = O.block_covariance(kb)
+            if Ph is not None:
+                C = Ph @ C @ Ph.T
+                v_ref = O.subspace_second_order(kb, r, Ph)
+            else:
+                v_ref = O.lowrank_second_order(kb, r)
+            lam = np.sort(np.linalg.eigvalsh(C))[::-1]
+            v_ref = np.concatenate([v_ref, np.zeros((r, vlen - v_ref.shape[1]))], axis=1)
             if n[blk] > r + 1 and (lam[r - 1] - lam[r]) >= gap_min * lam[r - 1]:
                 strict += 1
                 for i in range(r):
                     c_ref, e_ref = O.quantize_mxfp4(v_ref[i])
                     c_got, e_got = codes[b, h, blk, i], exps[b, h, blk, i]
                     top2 = np.sort(np.abs(v_ref[i]))[-2:]
-                    if top2[1] - top2[0] <= 1e-9 * top2[1] and (c_got != c_ref).sum() > d // 4:
+                    if top2[1] - top2[0] <= 1e-9 * top2[1] and (c_got != c_ref).sum() > vlen // 4:
                         c_got = np.where(c_got & 7, c_got ^ 8, c_got)         # sign convention tie
-                    for gi in range(d // 32):
+                    for gi in range(vlen // 32):
                         sl = slice(32 * gi, 32 * gi + 32)
                         amax = np.abs(v_ref[i, sl]).max()
-                        l2 = np.log2(amax)
                         total += 32
+                        if amax == 0.0:
+                            assert e_got[gi] == -127 and (c_got[sl] == 0).all(), (b, h, blk, i, gi)
+                            continue
+                        l2 = np.log2(amax)
                         if abs(l2 - np.round(l2)) < 1e-9:
                             exempt += 32
                             continue
@@ -107,7 +123,7 @@ def check_fp4(w, x, s, units=None, gap_min=1e-2):
             else:
                 loose += 1
                 got = O.dequantize_mxfp4(codes[b, h, blk].reshape(-1), exps[b, h, blk].reshape(-1))
-                got = got.reshape(r, d)
+                got = got.reshape(r, vlen)[:, :q.shape[1]]
                 qg = np.einsum("hd,rd->hr", q, got)
                 qr = np.einsum("hd,rd->hr", q, rso[blk])
                 dq = (qg * qg).sum(1) - (qr * qr).sum(1)

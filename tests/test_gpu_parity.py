@@ -101,8 +101,8 @@ def run_and_check(w, x, alpha=None, out_tol=1e-2, seqs=None):
     """Full decode on the GPU vs the oracle: selection by the gap rule, outputs
     where the selection is unambiguous, and outputs of the attention path fed with
     the oracle's selection everywhere."""
-    p = U.params_for(w, alpha=alpha)
     g = U.to_device(x)
+    p = U.params_for(w, alpha=alpha, P=g.get("P"))
     s = U.build(p, g)
     out, sel = U.decode(p, g, s)
     op = O.params_of(w, alpha=alpha)

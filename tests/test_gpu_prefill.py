@@ -23,8 +23,8 @@ def _gpu():
 
 
 def check_prefill(w, x, tokens, out_tol=1e-2):
-    p = U.params_for(w)
     g = U.to_device(x)
+    p = U.params_for(w, P=g.get("P"))
     s = U.build(p, g)
     out, sel = U.prefill(p, g, s, w.q_pos0)
     ref = O.run(x, O.params_of(w), tokens=tokens)

@@ -32,8 +32,8 @@ def run_update(w, new_lens, old_lens, max_append):
     """Build at old_lens (where > 0), update to new_lens; returns (inputs at new_lens,
     summaries, snapshot of the summaries before the update)."""
     x = synth.make_inputs(w, 21, lens=np.array(new_lens))
-    p = U.params_for(w)
     g = U.to_device(x)
+    p = U.params_for(w, P=g.get("P"))
     s = B.alloc_summaries(p, w.batch, w.max_len)
     for t in (s["mu"], s["so"], s["kc"], s["vc"]):
         if t is not None:

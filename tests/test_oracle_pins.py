@@ -514,3 +514,92 @@ def test_fp4_summaries_are_the_rounded_lowrank_ones():
     s32 = O.block_scores(q, mu, so, n, 1.0, 0.125, "lowrank")
     s4 = O.block_scores(q, mu4, so4, n4, 1.0, 0.125, "lowrank_fp4")
     assert np.abs(s4 - s32).max() < 0.05 * np.abs(s32).max()
+
+
+# --------------------------------------------------------------------------
+# Query-subspace projection (COBS sec. 2.3, "Subraum-Projektion")
+# --------------------------------------------------------------------------
+
+def test_query_subspace_of_a_known_second_moment():
+    """Queries = rows of H diag(sigma) U^T with a Hadamard H (H^T H = N I): the
+    sample second moment is U diag(sigma^2) U^T exactly, so P is the columns of U
+    with the s largest sigma, largest first, each signed by its largest entry."""
+    rng = np.random.default_rng(21)
+    d, N, s = 16, 64, 5
+    U = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    sigma = np.array([0.3, 2.5, 0.1, 1.7, 0.9, 3.1, 0.05, 1.2, 0.4, 0.6, 0.2, 0.8, 0.15, 1.0, 0.7, 0.5])
+    H = hadamard(N)[:, :d]
+    Q = (H * sigma) @ U.T
+    P = O.query_subspace(Q, s)
+    assert P.shape == (s, d)
+    for i, j in enumerate(np.argsort(-sigma)[:s]):
+        u = U[:, j] * np.sign(U[np.argmax(np.abs(U[:, j])), j])
+        np.testing.assert_allclose(P[i], u, atol=1e-12)
+    np.testing.assert_allclose(P @ P.T, np.eye(s), atol=1e-12)
+
+
+def test_full_orthogonal_subspace_leaves_the_scores_unchanged():
+    """s = d with an orthogonal P: (Pq)^T (P C P^T)_r (Pq) = q^T C_r q, because the top-r
+    eigenvectors of P C P^T are P times those of C; the vectors are P v_i up to sign."""
+    rng = np.random.default_rng(22)
+    d, L, r = 16, 150, 3
+    keys = rng.standard_normal((L, d)) * rng.uniform(0.2, 2.0, d)
+    q = rng.standard_normal((4, d))
+    P = np.linalg.qr(rng.standard_normal((d, d)))[0].T
+    mu0, so0, n0 = O.summaries(keys, L, "lowrank", r)
+    mu1, so1, n1 = O.summaries(keys, L, "lowrank", r, P)
+    s0 = O.block_scores(q, mu0, so0, n0, 1.0, 0.25, "lowrank")
+    s1 = O.block_scores(q, mu1, so1, n1, 1.0, 0.25, "lowrank", P)
+    np.testing.assert_allclose(s1, s0, atol=1e-11)
+    for b in range(len(n0)):
+        for i in range(r):
+            pv = P @ so0[b, i]
+            assert min(np.abs(so1[b, i] - pv).max(), np.abs(so1[b, i] + pv).max()) < 1e-10
+
+
+def test_subspace_query_with_full_rank_sees_the_whole_covariance():
+    """q in span(P) (q = P^T a) and r = s: the quadratic term is exactly q^T kappa_2 q,
+    the full second-order term, whatever the covariance outside the subspace."""
+    rng = np.random.default_rng(23)
+    d, s = 32, 6
+    P = np.linalg.qr(rng.standard_normal((d, d)))[0][:, :s].T
+    keys = rng.standard_normal((64, d)) * rng.uniform(0.1, 2.0, d) + rng.standard_normal(d)
+    a = rng.standard_normal((3, s))
+    q = a @ P
+    mu, so, n = O.summaries(keys, 64, "lowrank", s, P)
+    got = O.block_scores(q, mu, so, n, 1.0, 1.0, "lowrank", P)[:, 0]
+    C = O.block_covariance(keys)
+    ref = np.log(64) + q @ keys.mean(0) + 0.5 * np.einsum("hd,de,he->h", q, C, q)
+    np.testing.assert_allclose(got, ref, atol=1e-10)
+
+
+def test_covariance_orthogonal_to_the_subspace_gives_the_first_order_score():
+    """Keys varying only in directions orthogonal to P: the projected covariance is 0,
+    so every block scores like the alpha = 0 (mean-pool) selector."""
+    rng = np.random.default_rng(24)
+    d, s = 16, 4
+    B = np.linalg.qr(rng.standard_normal((d, d)))[0]
+    P = B[:, :s].T
+    keys = rng.standard_normal(d) + rng.standard_normal((130, d - s)) @ B[:, s:].T
+    q = rng.standard_normal((2, d))
+    mu, so, n = O.summaries(keys, 130, "lowrank", 3, P)
+    assert np.abs(so).max() < 1e-7                       # sqrt of rounding-level eigenvalues
+    got = O.block_scores(q, mu, so, n, 1.0, 0.5, "lowrank", P)
+    ref = O.block_scores(q, mu, so, n, 0.0, 0.5, "lowrank", P)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_subspace_fp4_pads_to_the_mx_group():
+    """s = 20: each vector is quantized as 32 entries (12 zeros appended), so its
+    stored value is the MX quantization of the padded vector, cut to 20 entries."""
+    rng = np.random.default_rng(25)
+    d, s = 32, 20
+    P = np.linalg.qr(rng.standard_normal((d, d)))[0][:, :s].T
+    keys = rng.standard_normal((64, d)) * 0.7
+    _, so32, _ = O.summaries(keys, 64, "lowrank", 2, P)
+    _, so4, _ = O.summaries(keys, 64, "lowrank_fp4", 2, P)
+    for i in range(2):
+        v = so32[0, i]
+        e = int(np.floor(np.log2(np.abs(v).max()))) - 2
+        ref = np.array([O.E2M1[O.quantize_e2m1(y / 2.0 ** e) & 7] * (1 if y >= 0 else -1) for y in v]) * 2.0 ** e
+        np.testing.assert_allclose(so4[0, i], ref, atol=0)
