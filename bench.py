@@ -43,12 +43,14 @@ def algorithmic_bytes(w, lens, sel, alpha):
     the pooled tokens, summaries of the candidate blocks, Q, gates, output."""
     es = 2 if w.dtype == "bf16" else 4
     d, G = w.head_dim, w.group
+    vlen = -(-w.subspace // 32) * 32 if w.subspace else d      # length of a stored rank-r vector
     if w.so_kind == "lowrank_fp4":           # bf16 mean + one compressed record per block
-        rec = -(-w.rank * (d // 2 + d // 32) // 16) * 16
+        rec = -(-w.rank * (vlen // 2 + vlen // 32) // 16) * 16
         sum_bytes_per_block = d * 2 + (0 if alpha == 0 else rec)
+    elif w.so_kind == "lowrank":
+        sum_bytes_per_block = d * 4 + (0 if alpha == 0 else w.rank * vlen * 4)
     else:
-        so_ch = 0 if alpha == 0 else (w.rank if w.so_kind == "lowrank" else 1)
-        sum_bytes_per_block = d * 4 * (1 + so_ch)
+        sum_bytes_per_block = d * 4 * (1 if alpha == 0 else 2)
     attn = sel_b = 0
     for b in range(w.batch):
         L = int(lens[b])
@@ -66,6 +68,16 @@ def algorithmic_bytes(w, lens, sel, alpha):
     attn += q + w.batch * w.n_q_heads * (3 * 4 + d * 4) + sel.size * 4
     sel_b += q + sel.size * 4
     return attn, sel_b
+
+
+def calibrated_subspace(w, g):
+    """Query subspaces [H_kv][s][d] computed on the GPU from the workload's calibration
+    queries (cobs_query_subspace), or None when the workload has no subspace."""
+    if not w.subspace:
+        return None
+    from block_sparse_long_compressed_amd import binding as B
+    from tests import gpu_util as U
+    return B.cobs_query_subspace(U.params_for(w), g["Qcal"], w.subspace)
 
 
 def counter_traffic(workload):
@@ -170,9 +182,10 @@ def main():
     alpha = w.alpha if args.alpha is None else args.alpha
     log(f"[bench] workload {w.name} alpha {alpha}: generating inputs")
     x = synth.make_inputs(w, args.seed)
-    p = U.params_for(w, alpha=alpha)
     B.lib()
     g0 = U.to_device(x)
+    P = calibrated_subspace(w, g0)
+    p = U.params_for(w, alpha=alpha, P=P)
     s0 = U.build(p, g0)
     torch.cuda.synchronize()
 
@@ -337,8 +350,8 @@ def bench_build(args):
     from tests import gpu_util as U
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w, args.seed)
-    p = U.params_for(w)
     g = U.to_device(x)
+    p = U.params_for(w, P=calibrated_subspace(w, g))
     s = B.alloc_summaries(p, w.batch, w.max_len)
     fn = lambda: B.cobs_build_summaries(p, g["lens"], g["K"], g["V"], s["mu"], s["so"], s["kc"], s["vc"])
     t = timed(fn, max(1, min(args.steps, 20)))
@@ -359,8 +372,8 @@ def bench_update(args):
     from tests import gpu_util as U
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w, args.seed)
-    p = U.params_for(w)
     g = U.to_device(x)
+    p = U.params_for(w, P=calibrated_subspace(w, g))
     s = B.alloc_summaries(p, w.batch, w.max_len)
     new = g["lens"]
     old = (new - 1).contiguous()
@@ -381,7 +394,8 @@ def bench_recall(args):
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w, args.seed)
     g = U.to_device(x)
-    p = U.params_for(w)
+    Pw = calibrated_subspace(w, g)
+    p = U.params_for(w, P=Pw)
     ws = B.alloc_workspace(p, w.batch, w.max_len)
     exact = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
     fx = lambda: B.cobs_select_topk_exact(p, g["lens"], g["Q"], g["K"], exact, ws)
@@ -389,7 +403,7 @@ def bench_recall(args):
     ex = exact.cpu().numpy()
     res = {"mode": "recall", "workload": w.name, "us_exact_selection": t_exact * 1e6, "recall": {}}
     for alpha in (0.0, 0.5, 1.0, 2.0):
-        pa = U.params_for(w, alpha=alpha)
+        pa = U.params_for(w, alpha=alpha, P=Pw)
         s = U.build(pa, g)
         sel = torch.empty_like(exact)
         fs = lambda: B.cobs_select_topk(pa, g["lens"], g["Q"][:, None], s["mu"], s["so"], sel, ws, max_len=w.max_len)
@@ -401,33 +415,38 @@ def bench_recall(args):
         res["recall"][str(alpha)] = hit / max(tot, 1)
         res[f"us_cumulant_selection_alpha{alpha}"] = t * 1e6
     if w.so_kind in ("lowrank", "lowrank_fp4"):
-        # the two storages of the rank-r channel: fp32 vectors against bf16 mean + MX FP4
-        # vectors, at the workload's alpha: agreement of the selections, recall of each
-        # against the exact-mass selection, summary bytes per block
+        # the storages of the rank-r channel: fp32 vectors, bf16 mean + MX FP4 vectors, and
+        # (for a subspace workload) both again in the calibrated query subspace, at the
+        # workload's alpha: recall of each against the exact-mass selection, agreement
+        # with the fp32 full-dimension selection, summary bytes per block
+        P = Pw
+        variants = [("lowrank", None), ("lowrank_fp4", None)]
+        if P is not None:
+            variants += [("lowrank", P), ("lowrank_fp4", P)]
         sels = {}
-        for kind in ("lowrank", "lowrank_fp4"):
-            wk = w.scaled(so_kind=kind)
-            pk = U.params_for(wk)
+        for kind, Pv in variants:
+            name = kind + ("" if Pv is None else f"_sub{w.subspace}")
+            wk = w.scaled(so_kind=kind, subspace=0 if Pv is None else w.subspace)
+            pk = U.params_for(wk, P=Pv)
             s = U.build(pk, g)
             sel = torch.empty_like(exact)
             B.cobs_select_topk(pk, g["lens"], g["Q"][:, None], s["mu"], s["so"], sel, ws, max_len=w.max_len)
             torch.cuda.synchronize()
-            sels[kind] = sel.cpu().numpy()
+            sels[name] = sel.cpu().numpy()
             sh = B.cobs_summary_shapes(pk, w.batch, w.max_len)
-            res[f"summary_bytes_per_block_{kind}"] = (sh["mu_bytes"] + sh["so_bytes"]) / (
+            res[f"summary_bytes_per_block_{name}"] = (sh["mu_bytes"] + sh["so_bytes"]) / (
                 w.batch * w.n_kv_heads * sh["nb_max"])
-        a, f = sels["lowrank"], sels["lowrank_fp4"]
-        same = sum(len(set(a[b, h][a[b, h] >= 0]) & set(f[b, h][f[b, h] >= 0]))
-                   for b in range(w.batch) for h in range(w.n_kv_heads))
+        a = sels["lowrank"]
         tot_a = int((a >= 0).sum())
-        res["fp4_vs_fp32_selection_agreement"] = same / max(tot_a, 1)
-        res["fp4_identical_units"] = int(sum((a[b, h] == f[b, h]).all()
-                                             for b in range(w.batch) for h in range(w.n_kv_heads)))
-        res["units"] = w.batch * w.n_kv_heads
-        for kind, sl in sels.items():
-            hit = sum(len(set(sl[b, h][sl[b, h] >= 0]) & set(ex[b, h][ex[b, h] >= 0]))
+        for name, f in sels.items():
+            hit = sum(len(set(f[b, h][f[b, h] >= 0]) & set(ex[b, h][ex[b, h] >= 0]))
                       for b in range(w.batch) for h in range(w.n_kv_heads))
-            res[f"recall_{kind}_alpha{w.alpha}"] = hit / max(int((ex >= 0).sum()), 1)
+            res[f"recall_{name}_alpha{w.alpha}"] = hit / max(int((ex >= 0).sum()), 1)
+            if name != "lowrank":
+                same = sum(len(set(a[b, h][a[b, h] >= 0]) & set(f[b, h][f[b, h] >= 0]))
+                           for b in range(w.batch) for h in range(w.n_kv_heads))
+                res[f"agreement_{name}_vs_lowrank"] = same / max(tot_a, 1)
+        res["units"] = w.batch * w.n_kv_heads
     print(json.dumps(res), flush=True)
 
 
