@@ -31,8 +31,8 @@ struct DecodeArgs {
   float alpha, scale;
   bool do_select, do_attn;
   int splits, sel_tpw;         // scoring workgroups per (sequence, kv-head), 16-block tiles per wave
-  int tpw, tpw_slc, wg_slc, wg_win, wg_cmp;   // attention: 64-key tiles per wave (window and pooled
-                                             // branches; selected branch), workgroups per branch and unit
+  int tpw_slc, tpw_win, tpw_cmp;   // attention: 64-key tiles per wave of each branch
+  int wg_slc, wg_win, wg_cmp;      // attention workgroups per branch and unit
   const int32_t* seq_lens;
   const void *Q, *K, *V, *kc, *vc;
   const void *mu, *so;         // summaries in the layout of so_kind (3, 5: compressed storage)

@@ -59,7 +59,7 @@ struct DecodeParams {
   float* lse_part;              // [unit][splits][16][2]
   uint32_t* pub;                // [unit][top_k] published selection codes (null: nobody waits)
   // attention
-  int wc_wgs, slc_wgs, nc_max, window, cmp_on, tpw, tpw_slc, wg_slc, wg_win, wg_cmp;
+  int wc_wgs, slc_wgs, nc_max, window, cmp_on, tpw_slc, tpw_win, tpw_cmp, wg_slc, wg_win, wg_cmp;
   float scale_log2;
   const void *K, *V, *kc, *vc;
   const float* gates;
@@ -353,7 +353,7 @@ __device__ void attn_role(const DecodeParams& p, int unit, int branch, int local
   // none).  Selected blocks come from the published codes (polled, bounded) or
   // the caller's selection; every block index is bounds-checked.
   auto tile_src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
-    const int tpw = branch == 0 ? p.tpw_slc : p.tpw;       // tiles per wave of this branch
+    const int tpw = branch == 0 ? p.tpw_slc : branch == 1 ? p.tpw_win : p.tpw_cmp;   // tiles per wave
     if (j >= tpw) return 0;
     const int tile = (local * nw + wave) * tpw + j;
     if (branch == 0) {
@@ -640,7 +640,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
   p.pub = (a.do_select && a.do_attn) ? a.ready : nullptr;
   p.wc_wgs = a.do_attn ? units * (a.wg_win + a.wg_cmp) : 0;
   p.slc_wgs = a.do_attn ? units * a.wg_slc : 0;
-  p.nc_max = a.nc_max; p.window = a.window; p.cmp_on = a.cmp_on; p.tpw = a.tpw; p.tpw_slc = a.tpw_slc;
+  p.nc_max = a.nc_max; p.window = a.window; p.cmp_on = a.cmp_on; p.tpw_slc = a.tpw_slc; p.tpw_win = a.tpw_win;
+  p.tpw_cmp = a.tpw_cmp;
   p.wg_slc = a.wg_slc; p.wg_win = a.wg_win; p.wg_cmp = a.wg_cmp; p.scale_log2 = a.scale * kLog2e;
   p.K = a.K; p.V = a.V; p.kc = a.kc; p.vc = a.vc; p.gates = a.gates;
   p.sel_attn = a.do_select ? a.sel : a.sel_in;
