@@ -73,7 +73,7 @@ cobs_status check_sizes(int batch, int max_len, int tokens) {
 struct Plan {
   int units_sel, units_attn;
   int sel_tpw, sel_splits;
-  int attn_waves, tpw_slc, tpw_win, tpw_cmp, wg_slc, wg_win, wg_cmp, attn_P;
+  int attn_waves, tpw_wc, tpw_slc, wg_slc, wg_win, wg_cmp, attn_P;
   size_t off_cnt_sel, off_cnt_attn, off_ready, off_scores, off_lse, off_sel, off_ml, off_o, total;
 };
 
@@ -102,16 +102,15 @@ Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
   // workgroups.
   const int wc_tiles = pl.units_attn * (t_win + t_cmp);
   if (wc_tiles <= 2048) {
-    pl.tpw_cmp = 4; pl.tpw_slc = 1;
+    pl.tpw_wc = 4; pl.tpw_slc = 1;
   } else if (wc_tiles <= 6144) {
-    pl.tpw_cmp = 8; pl.tpw_slc = 4;
+    pl.tpw_wc = 8; pl.tpw_slc = 4;
   } else {
-    pl.tpw_cmp = 4; pl.tpw_slc = 2;
+    pl.tpw_wc = 4; pl.tpw_slc = 2;
   }
-  pl.tpw_win = pl.tpw_cmp;
   pl.wg_slc = cdiv(t_slc, pl.attn_waves * pl.tpw_slc);
-  pl.wg_win = cdiv(t_win, pl.attn_waves * pl.tpw_win);
-  pl.wg_cmp = cdiv(t_cmp, pl.attn_waves * pl.tpw_cmp);
+  pl.wg_win = cdiv(t_win, pl.attn_waves * pl.tpw_wc);
+  pl.wg_cmp = cdiv(t_cmp, pl.attn_waves * pl.tpw_wc);
   pl.attn_P = pl.wg_slc + pl.wg_win + pl.wg_cmp;
 
   // with several query tokens only the selection buffer is used (prefill path)
@@ -258,7 +257,7 @@ static DecodeArgs decode_args(const cobs_params* p, const Plan& pl, int32_t batc
   a.so_kind = kernel_kind(p); a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha; a.scale = scale_of(p);
   a.do_select = a.do_attn = false;
   a.splits = pl.sel_splits; a.sel_tpw = pl.sel_tpw;
-  a.tpw_slc = pl.tpw_slc; a.tpw_win = pl.tpw_win; a.tpw_cmp = pl.tpw_cmp; a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
+  a.tpw_wc = pl.tpw_wc; a.tpw_slc = pl.tpw_slc; a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
   a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr; a.mu = a.so = a.gates = nullptr;
   a.sel = nullptr; a.sel_in = nullptr; a.sel_score = nullptr; a.out = nullptr;
   a.P = p->subspace_dim > 0 ? p->subspace : nullptr; a.sub_s = p->subspace_dim; a.vlen = vec_len(p);

@@ -31,7 +31,7 @@ struct DecodeArgs {
   float alpha, scale;
   bool do_select, do_attn;
   int splits, sel_tpw;         // scoring workgroups per (sequence, kv-head), 16-block tiles per wave
-  int tpw_slc, tpw_win, tpw_cmp;   // attention: 64-key tiles per wave of each branch
+  int tpw_wc, tpw_slc;             // attention: 64-key tiles per wave (window and pooled; selected)
   int wg_slc, wg_win, wg_cmp;      // attention workgroups per branch and unit
   const int32_t* seq_lens;
   const void *Q, *K, *V, *kc, *vc;

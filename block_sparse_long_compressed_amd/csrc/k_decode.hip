@@ -59,7 +59,7 @@ struct DecodeParams {
   float* lse_part;              // [unit][splits][16][2]
   uint32_t* pub;                // [unit][top_k] published selection codes (null: nobody waits)
   // attention
-  int wc_wgs, slc_wgs, nc_max, window, cmp_on, tpw_slc, tpw_win, tpw_cmp, wg_slc, wg_win, wg_cmp;
+  int wc_wgs, slc_wgs, nc_max, window, cmp_on, tpw, tpw_slc, wg_slc, wg_win, wg_cmp;
   float scale_log2;
   const void *K, *V, *kc, *vc;
   const float* gates;
@@ -192,23 +192,23 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
         sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
       }
     }
-    float wlin[NU][4], wq[NU][4];
-    score_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
-                              wlin);
+    ScoreW<D> W;
+    prepare_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
+                                W);
     if constexpr (Kind<KIND>::kSub) {
       // scale * P q: the four waves each contract a quarter of the column tiles
       const float* Ph = p.P + (size_t)head * p.sub_s * D;
-      subspace_weights_part<D>(Ph, p.sub_s, p.vlen, wave, 4, n, g, wlin, sl.wsub_x, wq);
+      subspace_weights_part<D>(Ph, p.sub_s, p.vlen, wave, 4, n, g, W.lin, sl.wsub_x, W.quad);
       __syncthreads();
-      subspace_weights_gather<D>(p.vlen, wave, 4, n, g, sl.wsub_x, wq);
+      subspace_weights_gather<D>(p.vlen, wave, 4, n, g, sl.wsub_x, W.quad);
+      finish_subspace_weights<E, D, KIND>(W);
     }
     for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
         const int j = j0 + r, tile = tile0 + j0 + r;
         if (j < p.sel_tpw && tile < tiles_total) {
-          const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, wlin,
-                                                   Kind<KIND>::kSub ? wq : wlin);
+          const f32x4 s4 = tile_score<E, D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, p.scale, W);
           if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
             const void* mrow;
             rows_of(tile + RING, mrow, vrow[r]);
@@ -353,7 +353,7 @@ __device__ void attn_role(const DecodeParams& p, int unit, int branch, int local
   // none).  Selected blocks come from the published codes (polled, bounded) or
   // the caller's selection; every block index is bounds-checked.
   auto tile_src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
-    const int tpw = branch == 0 ? p.tpw_slc : branch == 1 ? p.tpw_win : p.tpw_cmp;   // tiles per wave
+    const int tpw = branch == 0 ? p.tpw_slc : p.tpw;       // tiles per wave of this branch
     if (j >= tpw) return 0;
     const int tile = (local * nw + wave) * tpw + j;
     if (branch == 0) {
@@ -640,8 +640,7 @@ hipError_t launch_decode(const DecodeArgs& a) {
   p.pub = (a.do_select && a.do_attn) ? a.ready : nullptr;
   p.wc_wgs = a.do_attn ? units * (a.wg_win + a.wg_cmp) : 0;
   p.slc_wgs = a.do_attn ? units * a.wg_slc : 0;
-  p.nc_max = a.nc_max; p.window = a.window; p.cmp_on = a.cmp_on; p.tpw_slc = a.tpw_slc; p.tpw_win = a.tpw_win;
-  p.tpw_cmp = a.tpw_cmp;
+  p.nc_max = a.nc_max; p.window = a.window; p.cmp_on = a.cmp_on; p.tpw = a.tpw_wc; p.tpw_slc = a.tpw_slc;
   p.wg_slc = a.wg_slc; p.wg_win = a.wg_win; p.wg_cmp = a.wg_cmp; p.scale_log2 = a.scale * kLog2e;
   p.K = a.K; p.V = a.V; p.kc = a.kc; p.vc = a.vc; p.gates = a.gates;
   p.sel_attn = a.do_select ? a.sel : a.sel_in;

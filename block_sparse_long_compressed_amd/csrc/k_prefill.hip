@@ -58,17 +58,19 @@ __global__ __launch_bounds__(256) void k_prefill_select(PsParams p) {
   const size_t sum_base = ((size_t)seq * p.hkv + head) * p.nb_max;
   const int tiles = (ncand + 15) / 16;
 
-  float wlin[NU][4], wq[NU][4];
-  score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
-                            n, g, G, p.scale, wlin);
-  if constexpr (Kind<KIND>::kSub)
-    subspace_weights_part<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, 0, 1, n, g, wlin, nullptr, wq);
+  ScoreW<D> W;
+  prepare_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
+                              n, g, G, p.scale, W);
+  if constexpr (Kind<KIND>::kSub) {
+    subspace_weights_part<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, 0, 1, n, g, W.lin, nullptr, W.quad);
+    finish_subspace_weights<E, D, KIND>(W);
+  }
   const bool use_quad = p.alpha != 0.f;
   auto scores = [&](int tile) -> f32x4 {
     const int brow = min(tile * 16 + n, ncand - 1);
     const void *mr, *vr;
     summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, p.vlen, mr, vr);
-    f32x4 s = score_tile<D, KIND>(mr, vr, p.rank, p.vlen, g, use_quad, p.alpha, wlin, Kind<KIND>::kSub ? wq : wlin);
+    f32x4 s = score_tile<E, D, KIND>(mr, vr, p.rank, p.vlen, g, use_quad, p.alpha, p.scale, W);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = tile * 16 + 4 * g + i;
@@ -188,7 +190,7 @@ struct PsWgLds {
 };
 
 template <typename E, int D, int KIND>
-__global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
+__global__ __launch_bounds__(256, (KIND == 1 || KIND == 4) ? 2 : 3) void k_prefill_select_wg(PsParams p) {
   constexpr int NU = D / 16;
   constexpr int RING = 1;        // one tile in flight per wave; three waves per SIMD hide the rest
   extern __shared__ __align__(16) unsigned char smem[];
@@ -224,16 +226,17 @@ __global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
       sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
     }
   }
-  float wlin[NU][4], wq[NU][4];
-  score_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
-                            n, g, G, p.scale, wlin);
+  ScoreW<D> W;
+  prepare_weights<E, D, KIND>(p.Q, (((size_t)seq * p.tokens + tok) * (size_t)(p.hkv * G) + (size_t)head * G) * D,
+                              n, g, G, p.scale, W);
   if constexpr (Kind<KIND>::kSub) {
     // scale * P q: the four waves each contract a quarter of the column tiles (exchange
     // area after the keys)
     f32x4* xch = reinterpret_cast<f32x4*>(s_key + p.nb_pad);
-    subspace_weights_part<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, wave, 4, n, g, wlin, xch, wq);
+    subspace_weights_part<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, wave, 4, n, g, W.lin, xch, W.quad);
     __syncthreads();
-    subspace_weights_gather<D>(p.vlen, wave, 4, n, g, xch, wq);
+    subspace_weights_gather<D>(p.vlen, wave, 4, n, g, xch, W.quad);
+    finish_subspace_weights<E, D, KIND>(W);
   }
   float run_m = -INFINITY, run_s = 0.f;
 #pragma unroll 1
@@ -242,8 +245,7 @@ __global__ __launch_bounds__(256, 3) void k_prefill_select_wg(PsParams p) {
     for (int r = 0; r < RING; ++r) {
       const int tile = wave + 4 * (j0 + r);
       if (tile < tiles) {
-        const f32x4 s4 = sum_tile_score<D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, wlin,
-                                                 Kind<KIND>::kSub ? wq : wlin);
+        const f32x4 s4 = tile_score<E, D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, p.scale, W);
         if (tile + 4 * RING < tiles) {
           const void* mrow;
           rows_of(tile + 4 * RING, mrow, vrow[r]);

@@ -45,6 +45,51 @@ __device__ __forceinline__ void score_weights(const void* Q, size_t q_base, int 
   }
 }
 
+// Query weights of one wave, in B-operand layout.  lin: scale * q (fp32 MFMA);
+// quad: scale * P q (subspace kinds).  For the compressed kinds with bf16 queries
+// the contraction runs on v_mfma_f32_16x16x32_bf16 instead: lane (n, g)'s eight
+// k-slots of chunk j are columns 16u + 4g + c for u = 2j, 2j+1 (the columns the
+// compressed storage keeps together per lane), qb holds q in that order (bf16,
+// exact), qh + ql the two-part bf16 split of scale * P q.  Members a kind does not
+// use are never written and cost no registers.
+template <int D>
+struct ScoreW {
+  float lin[D / 16][4];
+  float quad[D / 16][4];
+  u32x4 qb[D / 32];
+  u32x4 qh[D / 32], ql[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void score_weights_bf16(const void* Q, size_t q_base, int n, int g, int G,
+                                                   u32x4 (&qb)[D / 32]) {
+  const bool hv = n < G;
+  const uint16_t* qh = static_cast<const uint16_t*>(Q) + q_base + (size_t)(hv ? n : 0) * D;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const uint2 a = *reinterpret_cast<const uint2*>(qh + 32 * j + 4 * g);
+    const uint2 b = *reinterpret_cast<const uint2*>(qh + 32 * j + 16 + 4 * g);
+    qb[j] = hv ? u32x4{a.x, a.y, b.x, b.y} : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// scale * P q (fp32, [u][c] layout) as two bf16 parts in the chunk order above.
+template <int D>
+__device__ __forceinline__ void split_bf16(const float (&w)[D / 16][4], u32x4 (&hi)[D / 32], u32x4 (&lo)[D / 32]) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {           // slots 2h, 2h+1: u = 2j + h/2, c = 2(h%2), 2(h%2)+1
+      const float a = w[2 * j + h / 2][2 * (h % 2)], b = w[2 * j + h / 2][2 * (h % 2) + 1];
+      const uint32_t ah = f32_to_bf16_bits(a), bh = f32_to_bf16_bits(b);
+      const uint32_t al = f32_to_bf16_bits(a - __uint_as_float(ah << 16));
+      const uint32_t bl = f32_to_bf16_bits(b - __uint_as_float(bh << 16));
+      hi[j][h] = ah | (bh << 16);
+      lo[j][h] = al | (bl << 16);
+    }
+  }
+}
+
 // Score kinds: 0 diagonal, 1 rank-r fp32, 2 exact masses (no summaries), 3 rank-r
 // in the compressed storage (bf16 mean; FP4 E2M1 vectors with one E8M0 exponent
 // per 32 entries), 4 and 5 the rank-r kinds 1 and 3 with the vectors in a query
@@ -99,6 +144,18 @@ __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, in
                                                     SumTile<D, KIND>& t) {
   if constexpr (Kind<KIND>::kFp4) {
     const uint8_t* rec = static_cast<const uint8_t*>(vrow);
+    // subspace kinds: the exponent block starts 16-aligned at rank * vlen/2 and the
+    // record extends at least 16 bytes past it (32 when it holds more than 16 bytes)
+    u32x4 e0 = {0u, 0u, 0u, 0u}, e1 = {0u, 0u, 0u, 0u};
+    if constexpr (Kind<KIND>::kSub) {
+      const uint8_t* ep = rec + rank * (vlen / 2);
+      e0 = *reinterpret_cast<const u32x4*>(ep);
+      if (rank * (vlen / 32) > 16) e1 = *reinterpret_cast<const u32x4*>(ep + 16);
+    }
+    auto ew = [&](int i) -> uint32_t {                // word i of the 32-byte exponent window
+      return i == 0 ? e0[0] : i == 1 ? e0[1] : i == 2 ? e0[2] : i == 3 ? e0[3]
+           : i == 4 ? e1[0] : i == 5 ? e1[1] : i == 6 ? e1[2] : e1[3];
+    };
 #pragma unroll
     for (int rr = 0; rr < kRankGroup; ++rr) {
       const int r = r0 + rr;
@@ -114,17 +171,25 @@ __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, in
             t.ex[rr] = *reinterpret_cast<const uint16_t*>(rec + rank * (D / 2) + r * (D / 32));
           }
         } else {
-          // vlen/32 code words per lane and vlen/32 exponent bytes per vector
+          // vlen/32 code words per lane (one load of 1-4 dwords, 4-byte aligned) and
+          // vlen/32 exponent bytes per vector, cut from the record's exponent block
           const int nw = vlen / 32;
-          const uint32_t* cp = reinterpret_cast<const uint32_t*>(rec + r * (vlen / 2) + g * (vlen / 8));
-          const uint8_t* ep = rec + rank * (vlen / 2) + r * nw;
-          uint32_t ex = 0;
-#pragma unroll
-          for (int w = 0; w < D / 32; ++w) {
-            t.code[rr][w] = w < nw ? cp[w] : 0u;
-            ex |= w < nw ? (uint32_t)ep[w] << (8 * w) : 0u;
+          const uint8_t* cp = rec + r * (vlen / 2) + g * (vlen / 8);
+          if (nw == 4) {
+            t.code[rr] = *reinterpret_cast<const u32x4*>(cp);
+          } else if (nw == 3) {
+            const uint3 c3 = *reinterpret_cast<const uint3*>(cp);
+            t.code[rr] = u32x4{c3.x, c3.y, c3.z, 0u};
+          } else if (nw == 2) {
+            const uint2 c2 = *reinterpret_cast<const uint2*>(cp);
+            t.code[rr] = u32x4{c2.x, c2.y, 0u, 0u};
+          } else {
+            t.code[rr] = u32x4{*reinterpret_cast<const uint32_t*>(cp), 0u, 0u, 0u};
           }
-          t.ex[rr] = ex;
+          const int o = r * nw, wi = o >> 2, sh = 8 * (o & 3);
+          const uint32_t lo = ew(wi), hi = ew(wi + 1);
+          const uint32_t ex = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
+          t.ex[rr] = nw == 4 ? ex : ex & ((1u << (8 * nw)) - 1u);
         }
       }
     }
@@ -171,6 +236,59 @@ __device__ __forceinline__ void sum_tile_load(const void* mrow, const void* vrow
 __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The compressed kinds with bf16 queries on the bf16 MFMA: the bf16 mean and the
+// decoded FP4 entries (E2M1 times a power of two, exact in bf16) against q in bf16,
+// products exact and accumulated in fp32; scale is applied to the sums.
+template <int D, int KIND>
+__device__ __forceinline__ f32x4 sum_tile_score_bf16(SumTile<D, KIND>& t, const void* vrow, int rank, int vlen, int g,
+                                                     bool use_quad, float alpha, float scale, const ScoreW<D>& W) {
+  constexpr int NJ = D / 32;
+  constexpr bool kSub = Kind<KIND>::kSub;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    acc = mfma_bf16_16x16x32(u32x4{t.mb[2 * j].x, t.mb[2 * j].y, t.mb[2 * j + 1].x, t.mb[2 * j + 1].y}, W.qb[j],
+                             acc);
+  acc *= scale;
+  if (!use_quad) return acc;
+  f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
+    if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, vlen, g, t);
+#pragma unroll
+    for (int rr = 0; rr < kRankGroup; ++rr) {
+      if (r0 + rr < rank) {
+        f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (kSub && 32 * j >= vlen) break;
+          // chunk j: the eight codes of word j, all in exponent group j
+          const uint32_t w = t.code[rr][j];
+          const float sc = e8m0_scale((t.ex[rr] >> (8 * j)) & 0xFFu);
+          const u32x4 a = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3))};
+          if constexpr (kSub) {
+            pr = mfma_bf16_16x16x32(a, W.qh[j], pr);
+            pr2 = mfma_bf16_16x16x32(a, W.ql[j], pr2);
+          } else {
+            pr = mfma_bf16_16x16x32(a, W.qb[j], pr);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float dd = kSub ? pr[i] + pr2[i] : scale * pr[i];
+          acc2[i] += 0.5f * alpha * dd * dd;
+        }
+      }
+    }
+  }
+  return acc + acc2;
+}
 
 // Scores (without ln n_b) of the tile's 16 blocks for the group's heads from the
 // loaded rows.  Linear and quadratic terms are independent MFMA chains.  wlin are
@@ -280,14 +398,42 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
   return acc + acc2;
 }
 
+// Whether a kind runs its contraction on the bf16 MFMA (compressed kinds, bf16 queries).
+template <typename E, int KIND>
+constexpr bool kBf16Path = E::kBytes == 2 && Kind<KIND>::kFp4;
+
+// The wave's query weights other than the subspace ones (which need the workgroup).
+template <typename E, int D, int KIND>
+__device__ __forceinline__ void prepare_weights(const void* Q, size_t q_base, int n, int g, int G, float scale,
+                                                ScoreW<D>& W) {
+  score_weights<E, D, KIND>(Q, q_base, n, g, G, scale, W.lin);
+  if constexpr (kBf16Path<E, KIND>) score_weights_bf16<D>(Q, q_base, n, g, G, W.qb);
+}
+
+// After W.quad holds scale * P q: its bf16 split for the bf16 path.
+template <typename E, int D, int KIND>
+__device__ __forceinline__ void finish_subspace_weights(ScoreW<D>& W) {
+  if constexpr (kBf16Path<E, KIND> && Kind<KIND>::kSub) split_bf16<D>(W.quad, W.qh, W.ql);
+}
+
+// Score a loaded tile on the kind's path.
+template <typename E, int D, int KIND>
+__device__ __forceinline__ f32x4 tile_score(SumTile<D, KIND>& t, const void* vrow, int rank, int vlen, int g,
+                                            bool use_quad, float alpha, float scale, const ScoreW<D>& W) {
+  if constexpr (kBf16Path<E, KIND>)
+    return sum_tile_score_bf16<D, KIND>(t, vrow, rank, vlen, g, use_quad, alpha, scale, W);
+  else
+    return sum_tile_score<D, KIND>(t, vrow, rank, vlen, g, use_quad, alpha, W.lin,
+                                   Kind<KIND>::kSub ? W.quad : W.lin);
+}
+
 // Load and score one tile in one step.
-template <int D, int KIND>
+template <typename E, int D, int KIND>
 __device__ __forceinline__ f32x4 score_tile(const void* mrow, const void* vrow, int rank, int vlen, int g,
-                                            bool use_quad, float alpha, const float (&wlin)[D / 16][4],
-                                            const float (&wq)[D / 16][4]) {
+                                            bool use_quad, float alpha, float scale, const ScoreW<D>& W) {
   SumTile<D, KIND> t;
   sum_tile_load<D, KIND>(mrow, vrow, rank, vlen, g, use_quad, t);
-  return sum_tile_score<D, KIND>(t, vrow, rank, vlen, g, use_quad, alpha, wlin, wq);
+  return tile_score<E, D, KIND>(t, vrow, rank, vlen, g, use_quad, alpha, scale, W);
 }
 
 // Quadratic weights of the subspace kinds, scale * P q, in the B-operand layout:
