@@ -6,27 +6,43 @@
 // softmax, combined as g_cmp o_cmp + g_slc o_slc + g_win o_win.
 //
 // A workgroup owns 8 consecutive tokens of one kv-head group (two per wave, so a
-// wave's B operand covers 2 x 16 query heads).  The window and pooled-token keys
-// of consecutive tokens nearly coincide, so those 64-key tiles are staged once in
-// LDS for all 8 tokens (double buffered, the next tile's global loads in flight
-// while the current one is consumed) and every token masks its own key range:
+// wave's B operand covers 2 x 16 query heads) and runs the three branches one
+// after the other over 64-key tiles staged once in LDS for all 8 tokens (double
+// buffered, the next tile's global loads in flight while the current one is
+// consumed); every token masks its own keys:
+//   window and pooled tokens: consecutive tokens' key ranges nearly coincide, so
+//   each tile of the union range is staged once and a token masks positions
+//   outside its range;
+//   selected blocks: the workgroup stages the union of its tokens' selections
+//   (consecutive tokens pick largely the same blocks: about 21 distinct blocks for
+//   8 x 16 picks on the 32k workload) and a token keeps a tile only if the block is
+//   one of its own; a wave whose two tokens both skip a tile does no arithmetic.
+// Staged tiles:
 //   K rows padded to d+8 elements, read as the A operand of S = K Q^T with
 //   16-byte reads;
 //   V rows padded to d+4 elements, its transpose (the A operand of O^T = V^T P^T)
 //   gathered with 16-bit reads, shared by both tokens of a wave.
-// Selected blocks differ per token: a second launch gives each (token, group)
-// one wave that gathers its blocks straight into registers with the shared
-// 64-key tile steps (software pipelined) and adds its gated output.  Keeping the
-// two phases in separate launches lets each run two waves per SIMD.
 #include "attn_tile.h"
 #include "cobs_device.h"
 #include "cobs_launch.h"
+#include "score_common.h"
 
 #include <algorithm>
 
 namespace cobs {
 
 constexpr int kPfTokens = 8;          // query tokens per workgroup (two per wave)
+constexpr int kPfMaxBlocks = 4096;    // longest prefix (blocks) the selected-block union supports
+constexpr int kPfMaskWords = kPfMaxBlocks / 32;
+
+// Selected-block bookkeeping of a workgroup (LDS, after the staging buffers): one
+// bitmap per token over the prefix's blocks, their union as an ascending list.
+struct PfSel {
+  uint32_t mask[kPfTokens][kPfMaskWords];
+  int32_t list[kPfTokens * 64];
+  int scan_w[4];
+  int count;
+};
 
 template <int D>
 struct PfShape {
@@ -170,20 +186,22 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
   }
 }
 
-// Window and pooled-token branches for the workgroup's 8 tokens; writes
-// out = g_win o_win + g_cmp o_cmp (zero where a token has no such keys).
+// The three branches for the workgroup's 8 tokens; writes
+// out = g_win o_win + g_cmp o_cmp + g_slc o_slc (a branch with no keys adds 0).
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
   using S = PfShape<D>;
   constexpr int NCH = S::kNch, NDT = S::kDt;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* bufs = reinterpret_cast<uint16_t*>(smem);
+  PfSel& ps = *reinterpret_cast<PfSel*>(smem + (size_t)2 * S::kBufElems * sizeof(uint16_t));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int head = blockIdx.y, G = p.group, L = p.seq_len;
   const int tok0 = blockIdx.x * kPfTokens;
   const int last_tok = min(tok0 + kPfTokens, p.tokens) - 1;
   const int hcol = min(n, G - 1);           // columns n >= G repeat head G-1 and are never written
+  const int nb = (L + kBlock - 1) / kBlock;
 
   // this wave's two tokens (a token past the chunk sees nothing and writes nothing)
   int tok[2], t[2];
@@ -203,10 +221,47 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
     for (int c = 0; c < NCH; ++c) qf[u][c] = ld16(Qh + (4 * c + g) * 8);
   }
 
+  // the tokens' selections as bitmaps (bounds-checked block indices) and their
+  // union as an ascending list
+  for (int i = threadIdx.x; i < kPfTokens * kPfMaskWords; i += 256) (&ps.mask[0][0])[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPfTokens * p.top_k; i += 256) {
+    const int u = i / p.top_k, k = tok0 + u;
+    if (k < p.tokens) {
+      const int b = p.sel[((size_t)k * p.hkv + head) * p.top_k + i % p.top_k];
+      if (b >= 0 && b < nb) atomicOr(&ps.mask[u][b >> 5], 1u << (b & 31));
+    }
+  }
+  __syncthreads();
+  {
+    const int nwords = (nb + 31) / 32;
+    int cnt = 0;                               // thread i owns word i (at most 4096 blocks: 128 words)
+    for (int w = threadIdx.x; w < nwords; w += 256) {
+      uint32_t x = 0u;
+#pragma unroll
+      for (int u = 0; u < kPfTokens; ++u) x |= ps.mask[u][w];
+      cnt += __builtin_popcount(x);
+    }
+    int total;
+    int pos = block_exclusive_scan(cnt, ps.scan_w, &total);
+    for (int w = threadIdx.x; w < nwords; w += 256) {
+      uint32_t x = 0u;
+#pragma unroll
+      for (int u = 0; u < kPfTokens; ++u) x |= ps.mask[u][w];
+      while (x) {
+        const int bit = __builtin_ctz(x);
+        ps.list[pos++] = 32 * w + bit;
+        x &= x - 1u;
+      }
+    }
+    if (threadIdx.x == 0) ps.count = total;
+    __syncthreads();
+  }
+
   const int t_first = p.q_pos0 + tok0, t_last = p.q_pos0 + last_tok;
-  bool have_out = false;                     // uniform: the window branch already wrote the outputs
+  bool have_out = false;                     // uniform: an earlier branch already wrote the outputs
 #pragma unroll 1
-  for (int br = 0; br < 2; ++br) {             // 0 = window, 1 = pooled tokens
+  for (int br = 0; br < 3; ++br) {             // 0 = window, 1 = pooled tokens, 2 = selected blocks
     int lo[2], hi[2], base = 0, count = 0;
     const uint16_t *Ksrc, *Vsrc;
     if (br == 0) {
@@ -221,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
         lo[u] = max(0, t[u] - p.window + 1);
         hi[u] = live[u] ? t[u] : -1;
       }
-    } else {
+    } else if (br == 1) {
       if (p.cmp_on) count = t_last >= 31 ? (t_last - 31) / 16 + 1 : 0;
       Ksrc = p.kc + (size_t)head * p.nc_max * D;
       Vsrc = p.vc + (size_t)head * p.nc_max * D;
@@ -230,7 +285,21 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
         lo[u] = 0;
         hi[u] = (live[u] && t[u] >= 31) ? (t[u] - 31) / 16 : -1;
       }
+    } else {
+      count = ps.count * kBlock;               // tiles = the union's blocks
+      Ksrc = p.K + (size_t)head * L * D;
+      Vsrc = p.V + (size_t)head * L * D;
     }
+    // tile j: its first position and valid rows (the union's j-th block for the
+    // selected branch, else the j-th 64 positions from base)
+    auto tile_at = [&](int j, int& start) -> int {
+      if (br == 2) {
+        start = ps.list[j] * kBlock;
+        return min(kBlock, L - start);
+      }
+      start = base + j * kBlock;
+      return min(kBlock, base + count - start);
+    };
     const int ntiles = (count + kBlock - 1) / kBlock;
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
     f32x4 acc[2][NDT];
@@ -241,16 +310,35 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
 
     if (ntiles > 0) {
       StageRegs<D> sr;
-      stage_load<D>(Ksrc + (size_t)base * D, Vsrc + (size_t)base * D, min(kBlock, count), sr);
+      int st0;
+      const int nv0 = tile_at(0, st0);
+      stage_load<D>(Ksrc + (size_t)st0 * D, Vsrc + (size_t)st0 * D, nv0, sr);
       __syncthreads();                         // the previous branch is done with the buffers
       stage_store<D>(sr, bufs);
 #pragma unroll 1
       for (int j = 0; j < ntiles; ++j) {
         uint16_t* cur = bufs + (j & 1) * S::kBufElems;
-        const int nstart = base + (j + 1) * kBlock;
-        if (j + 1 < ntiles) stage_load<D>(Ksrc + (size_t)nstart * D, Vsrc + (size_t)nstart * D, min(kBlock, base + count - nstart), sr);
+        if (j + 1 < ntiles) {
+          int stn;
+          const int nvn = tile_at(j + 1, stn);
+          stage_load<D>(Ksrc + (size_t)stn * D, Vsrc + (size_t)stn * D, nvn, sr);
+        }
         __syncthreads();                       // tile j staged by every thread
-        shared_tile<D>(cur, base + j * kBlock, lo, hi, qf, p.scale_log2, m, l, acc);
+        int tstart;
+        const int nvj = tile_at(j, tstart);
+        bool any = true;
+        if (br == 2) {                         // a token keeps the block only if it selected it
+          const int b = tstart / kBlock;
+          any = false;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bool mine = live[u] && ((ps.mask[2 * wave + u][b >> 5] >> (b & 31)) & 1u);
+            lo[u] = mine ? tstart : 1;
+            hi[u] = mine ? tstart + nvj - 1 : 0;
+            any |= mine;
+          }
+        }
+        if (any) shared_tile<D>(cur, tstart, lo, hi, qf, p.scale_log2, m, l, acc);
         if (j + 1 < ntiles) stage_store<D>(sr, bufs + ((j + 1) & 1) * S::kBufElems);
       }
     }
@@ -262,7 +350,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
       lt += shfl_xor_f(lt, 32);
       if (live[u] && n < G) {
         const size_t row = (size_t)tok[u] * p.hkv * G + (size_t)head * G + n;
-        const float gate = p.gates ? p.gates[row * 3 + (br == 0 ? 2 : 0)] : 0.f;    // (cmp, slc, win)
+        // (cmp, slc, win); without gates the selected branch alone, weight 1
+        const float gate = p.gates ? p.gates[row * 3 + (br == 0 ? 2 : br == 1 ? 0 : 1)] : (br == 2 ? 1.f : 0.f);
         const float f = lt > 0.f ? gate / lt : 0.f;
         float* op = p.out + row * D + 4 * g;
 #pragma unroll
@@ -276,72 +365,6 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
   }
 }
 
-// Selected blocks: one wave per (token, kv-head group), gathered straight into
-// registers (software pipelined); adds g_slc o_slc to the outputs.
-template <int D>
-__global__ __launch_bounds__(256, 2) void k_prefill_slc(PaParams p) {
-  using T = AttnTiling<EltBF16, D>;
-  constexpr int NCH = T::kChunks, NDT = T::kDt;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int head = blockIdx.y, G = p.group, L = p.seq_len;
-  const int tok = blockIdx.x * 4 + wave;
-  if (tok >= p.tokens) return;                 // waves are independent: no barriers below
-  const int hcol = min(n, G - 1);
-  const uint16_t* Kh = p.K + (size_t)head * L * D;
-  const uint16_t* Vh = p.V + (size_t)head * L * D;
-  const int32_t* selu = p.sel + ((size_t)tok * p.hkv + head) * p.top_k;
-  const int nb = (L + kBlock - 1) / kBlock;
-  auto src = [&](int j, const uint16_t*& Kt, const uint16_t*& Vt) -> int {
-    if (j >= p.top_k) return 0;
-    const int b = selu[j];
-    if (b < 0 || b >= nb) return 0;            // bounds-checked block index
-    Kt = Kh + (size_t)b * kBlock * D;
-    Vt = Vh + (size_t)b * kBlock * D;
-    return min(kBlock, L - b * kBlock);
-  };
-  uint16_t* lds = reinterpret_cast<uint16_t*>(smem) + (size_t)wave * kBlock * T::kRowStride;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  TileRegs<EltBF16, D> tr;
-  const uint16_t *Kt = nullptr, *Vt = nullptr;
-  int nv = src(0, Kt, Vt);
-  if (nv > 0) {
-    tile_load_k<EltBF16, D>(Kt, nv, tr);
-    tile_load_v<EltBF16, D>(Vt, nv, tr);
-  }
-  u32x4 qf[NCH];
-  {
-    const uint16_t* Qh = p.Q + ((size_t)tok * p.hkv * G + (size_t)head * G + hcol) * D;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * 8);
-  }
-  for (int j = 0; nv > 0; ++j) {
-    f32x4 sc4[4];
-    tile_scores<EltBF16, D>(tr, qf, sc4);
-    const uint16_t *Kn = nullptr, *Vn = nullptr;
-    const int nv_next = src(j + 1, Kn, Vn);
-    if (nv_next > 0) tile_load_k<EltBF16, D>(Kn, nv_next, tr);
-    tile_stage_v<EltBF16, D>(tr, lds);
-    tile_softmax_pv<EltBF16, D>(sc4, nv, p.scale_log2, lds, m_run, l_run, acc);
-    if (nv_next > 0) tile_load_v<EltBF16, D>(Vn, nv_next, tr);
-    nv = nv_next;
-  }
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
-  if (n < G) {
-    const size_t row = (size_t)tok * p.hkv * G + (size_t)head * G + n;
-    const float gate = p.gates ? p.gates[row * 3 + 1] : 1.f;    // slc only without gates
-    const float f = l_run > 0.f ? gate / l_run : 0.f;
-    float* op = p.out + row * D + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) st_f32x4(op + 16 * dt, ld_f32x4(op + 16 * dt) + f * acc[dt]);
-  }
-}
-
 template <int D>
 static hipError_t launch_pa(const PrefillArgs& a) {
   PaParams p;
@@ -351,13 +374,10 @@ static hipError_t launch_pa(const PrefillArgs& a) {
   p.Q = static_cast<const uint16_t*>(a.Q); p.K = static_cast<const uint16_t*>(a.K);
   p.V = static_cast<const uint16_t*>(a.V); p.kc = static_cast<const uint16_t*>(a.kc);
   p.vc = static_cast<const uint16_t*>(a.vc); p.gates = a.gates; p.sel = a.sel; p.out = a.out;
+  if ((a.max_len + kBlock - 1) / kBlock > kPfMaxBlocks || a.top_k > 64) return hipErrorInvalidValue;
   dim3 g1((a.tokens + kPfTokens - 1) / kPfTokens, a.hkv, 1);
-  hipLaunchKernelGGL((k_prefill_shared<D>), g1, dim3(256), (size_t)2 * PfShape<D>::kBufElems * 2, a.stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 g2((a.tokens + 3) / 4, a.hkv, 1);
-  const size_t lds2 = attn_lds_bytes<EltBF16, D>(4);
-  hipLaunchKernelGGL((k_prefill_slc<D>), g2, dim3(256), lds2, a.stream, p);
+  const size_t lds = (size_t)2 * PfShape<D>::kBufElems * sizeof(uint16_t) + sizeof(PfSel);
+  hipLaunchKernelGGL((k_prefill_shared<D>), g1, dim3(256), lds, a.stream, p);
   return hipGetLastError();
 }
 
