@@ -71,6 +71,16 @@ def test_prefill_variants(kind, d, G):
     check_prefill(w, x, tokens=list(range(T)))
 
 
+def test_prefill_f32_inputs():
+    # fp32 Q/K/V take the one-workgroup-per-(token, group) attention path
+    L, T = 700, 40
+    w = synth.Workload("pff", max_len=L, min_len=L, n_q_tokens=T, q_pos0=L - T,
+                       **dict(BASE, head_dim=64, n_q_heads=8, dtype="f32", top_k=4, window=100))
+    x = synth.make_inputs(w, 16)
+    worst, _, _ = check_prefill(w, x, tokens=list(range(T)), out_tol=1e-4)
+    assert worst <= 1e-4
+
+
 def test_prefill_last_token_matches_decode():
     L = 1280
     wp = synth.Workload("pfd", max_len=L, min_len=L, n_q_tokens=1, q_pos0=L - 1, **BASE)
