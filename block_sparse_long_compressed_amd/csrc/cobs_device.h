@@ -22,6 +22,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two floats rounded to nearest-even bf16, packed (lo in bits 0..15): one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
 // Element traits.  A 16-byte chunk holds kPer16 elements.
 struct EltBF16 {
   typedef uint16_t storage;

@@ -5,23 +5,25 @@
 // window [t-W+1, t] and the pooled tokens j with 16j + 31 <= t, each an exact
 // softmax, combined as g_cmp o_cmp + g_slc o_slc + g_win o_win.
 //
-// A workgroup owns 8 consecutive tokens of one kv-head group (two per wave, so a
-// wave's B operand covers 2 x 16 query heads) and runs the three branches one
-// after the other over 64-key tiles staged once in LDS for all 8 tokens (double
-// buffered, the next tile's global loads in flight while the current one is
-// consumed); every token masks its own keys:
+// A workgroup of 8 waves owns 16 consecutive tokens of one kv-head group (two per
+// wave, so a wave's B operand covers 2 x 16 query heads) and runs the three
+// branches one after the other over 64-key tiles staged once in LDS for all 16
+// tokens (two LDS buffers; the global loads of the next two tiles are in flight
+// in registers while the current tile is consumed); every token masks its own
+// keys:
 //   window and pooled tokens: consecutive tokens' key ranges nearly coincide, so
 //   each tile of the union range is staged once and a token masks positions
 //   outside its range;
 //   selected blocks: the workgroup stages the union of its tokens' selections
-//   (consecutive tokens pick largely the same blocks: about 21 distinct blocks for
-//   8 x 16 picks on the 32k workload) and a token keeps a tile only if the block is
+//   (consecutive tokens pick largely the same blocks: about 22 distinct blocks for
+//   16 x 16 picks on the 32k workload) and a token keeps a tile only if the block is
 //   one of its own; a wave whose two tokens both skip a tile does no arithmetic.
 // Staged tiles:
 //   K rows padded to d+8 elements, read as the A operand of S = K Q^T with
 //   16-byte reads;
-//   V rows padded to d+4 elements, its transpose (the A operand of O^T = V^T P^T)
-//   gathered with 16-bit reads, shared by both tokens of a wave.
+//   V rows padded to d+16 elements, its transpose (the A operand of O^T = V^T P^T)
+//   read with gfx950's transposing LDS read (ds_read_b64_tr_b16: four lanes' 4 x
+//   16-bit rows come back as columns), shared by both tokens of a wave.
 #include "attn_tile.h"
 #include "cobs_device.h"
 #include "cobs_launch.h"
@@ -31,7 +33,9 @@
 
 namespace cobs {
 
-constexpr int kPfTokens = 8;          // query tokens per workgroup (two per wave)
+constexpr int kPfThreads = 512;       // 8 waves
+constexpr int kPfWaves = kPfThreads / 64;
+constexpr int kPfTokens = 2 * kPfWaves;   // query tokens per workgroup (two per wave)
 constexpr int kPfMaxBlocks = 4096;    // longest prefix (blocks) the selected-block union supports
 constexpr int kPfMaskWords = kPfMaxBlocks / 32;
 
@@ -40,9 +44,27 @@ constexpr int kPfMaskWords = kPfMaxBlocks / 32;
 struct PfSel {
   uint32_t mask[kPfTokens][kPfMaskWords];
   int32_t list[kPfTokens * 64];
-  int scan_w[4];
+  int scan_w[kPfWaves];
   int count;
 };
+
+// Exclusive prefix sum over the workgroup's threads, in thread order.
+__device__ __forceinline__ int pf_block_scan(int v, int* lds_w, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x = wave_inclusive_sum(v);
+  if (lane == 63) lds_w[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPfWaves; ++i) {
+    const int c = lds_w[i];
+    base += (i < w) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
 
 template <int D>
 struct PfShape {
@@ -50,8 +72,8 @@ struct PfShape {
   static constexpr int kDt = D / 16;                     // 16-row output tiles of O^T
   static constexpr int kKs = D + 8;                      // LDS row stride of staged K (elements)
   static constexpr int kRowChunks = D / 8;               // 16-byte chunks per K/V row
-  static constexpr int kLoads = kBlock * kRowChunks / 256;   // 16-byte loads per thread per tile (K or V)
-  static constexpr int kVs = D + 4;                      // LDS row stride of staged V (elements)
+  static constexpr int kLoads = kBlock * kRowChunks / kPfThreads;   // 16-byte loads per thread per tile (K or V)
+  static constexpr int kVs = D + 16;                     // LDS row stride of staged V (elements): 8 banks apart
   static constexpr int kKElems = kBlock * kKs;
   static constexpr int kBufElems = kKElems + kBlock * kVs;   // one staged tile: K then V
 };
@@ -77,7 +99,7 @@ __device__ __forceinline__ void stage_load(const uint16_t* __restrict__ Ks, cons
   using S = PfShape<D>;
 #pragma unroll
   for (int i = 0; i < S::kLoads; ++i) {
-    const int id = threadIdx.x + 256 * i;
+    const int id = threadIdx.x + kPfThreads * i;
     const int row = min(id / S::kRowChunks, nvalid - 1), cc = id % S::kRowChunks;
     r.k[i] = ld16(Ks + (size_t)row * D + cc * 8);
     r.v[i] = ld16(Vs + (size_t)row * D + cc * 8);
@@ -90,12 +112,10 @@ __device__ __forceinline__ void stage_store(const StageRegs<D>& r, uint16_t* buf
   uint16_t* vs = buf + S::kKElems;
 #pragma unroll
   for (int i = 0; i < S::kLoads; ++i) {
-    const int id = threadIdx.x + 256 * i;
+    const int id = threadIdx.x + kPfThreads * i;
     const int row = id / S::kRowChunks, cc = id % S::kRowChunks;
     st16(buf + row * S::kKs + cc * 8, r.k[i]);
-    uint2* d2 = reinterpret_cast<uint2*>(vs + row * S::kVs + cc * 8);    // 8-byte aligned rows
-    d2[0] = make_uint2(r.v[i][0], r.v[i][1]);
-    d2[1] = make_uint2(r.v[i][2], r.v[i][3]);
+    st16(vs + row * S::kVs + cc * 8, r.v[i]);
   }
 }
 
@@ -124,20 +144,29 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
   u32x4 pb[2][2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
+    // max of the raw scores over the token's visible keys (the mask is skipped for a
+    // tile the token sees whole); the softmax runs in log2 units, x = s * scale_log2
     float mt = -INFINITY;
+    if (tile_start >= lo[u] && tile_start + kBlock - 1 <= hi[u]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = tile_start + 16 * t + 4 * g + i;
-        const float x = (pos >= lo[u] && pos <= hi[u]) ? s[u][t][i] * scale_log2 : -INFINITY;
-        s[u][t][i] = x;
-        mt = fmaxf(mt, x);
+        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[u][t][i]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = tile_start + 16 * t + 4 * g + i;
+          const float x = (pos >= lo[u] && pos <= hi[u]) ? s[u][t][i] : -INFINITY;
+          s[u][t][i] = x;
+          mt = fmaxf(mt, x);
+        }
       }
     }
     mt = fmaxf(mt, shfl_xor_f(mt, 16));
     mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    const float m_new = fmaxf(m[u], mt);
+    const float m_new = fmaxf(m[u], mt * scale_log2);
     // a token with no visible key yet keeps (m, l, acc) = (-inf, 0, 0); its P is all zero
     const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m[u] - m_new);
     const float mref = (m_new == -INFINITY) ? 0.f : m_new;
@@ -146,7 +175,7 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = fast_exp2(s[u][t][i] - mref);
+        const float pv = fast_exp2(fmaf(s[u][t][i], scale_log2, -mref));
         s[u][t][i] = pv;
         psum += pv;
       }
@@ -157,28 +186,31 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
     for (int dt = 0; dt < S::kDt; ++dt) acc[u][dt] *= corr;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      pb[u][h][0] = f32_to_bf16_bits(s[u][2 * h][0]) | (f32_to_bf16_bits(s[u][2 * h][1]) << 16);
-      pb[u][h][1] = f32_to_bf16_bits(s[u][2 * h][2]) | (f32_to_bf16_bits(s[u][2 * h][3]) << 16);
-      pb[u][h][2] = f32_to_bf16_bits(s[u][2 * h + 1][0]) | (f32_to_bf16_bits(s[u][2 * h + 1][1]) << 16);
-      pb[u][h][3] = f32_to_bf16_bits(s[u][2 * h + 1][2]) | (f32_to_bf16_bits(s[u][2 * h + 1][3]) << 16);
+      pb[u][h][0] = pack_bf16x2(s[u][2 * h][0], s[u][2 * h][1]);
+      pb[u][h][1] = pack_bf16x2(s[u][2 * h][2], s[u][2 * h][3]);
+      pb[u][h][2] = pack_bf16x2(s[u][2 * h + 1][0], s[u][2 * h + 1][1]);
+      pb[u][h][3] = pack_bf16x2(s[u][2 * h + 1][2], s[u][2 * h + 1][3]);
     }
   }
-  // O^T += V^T P^T: the A operand (V^T rows d, keys of lane group g) is gathered
-  // from the row-major V with 16-bit reads (padded stride: conflict-free)
+  // O^T += V^T P^T.  The A operand of lane (n, g) is V[kb + j][16 dt + n] for the
+  // key runs kb = 32h + 4g and 32h + 16 + 4g, j = 0..3.  ds_read_b64_tr_b16 over a
+  // group of 16 lanes returns to lane 4a + b the b-th 16-bit element of the rows
+  // read by lanes a, a + 4, a + 8, a + 12; so lane (n, g) points at row kb + n/4,
+  // columns 16 dt + 4(n%4) .. +3.
   const uint16_t* vs = buf + S::kKElems;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int dt = 0; dt < S::kDt; ++dt) {
-      const int col = 16 * dt + n;
       u32x4 vop;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int kb = 32 * h + 16 * e + 4 * g;
-        const uint32_t v0 = vs[(kb + 0) * S::kVs + col], v1 = vs[(kb + 1) * S::kVs + col];
-        const uint32_t v2 = vs[(kb + 2) * S::kVs + col], v3 = vs[(kb + 3) * S::kVs + col];
-        vop[2 * e] = v0 | (v1 << 16);
-        vop[2 * e + 1] = v2 | (v3 << 16);
+        const uint16_t* src = vs + (32 * h + 16 * e + 4 * g + (n >> 2)) * S::kVs + 16 * dt + 4 * (n & 3);
+        const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
+        vop[2 * e] = w.x;
+        vop[2 * e + 1] = w.y;
       }
       acc[0][dt] = mfma_bf16_16x16x32(vop, pb[0][h], acc[0][dt]);
       acc[1][dt] = mfma_bf16_16x16x32(vop, pb[1][h], acc[1][dt]);
@@ -186,10 +218,10 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
   }
 }
 
-// The three branches for the workgroup's 8 tokens; writes
+// The three branches for the workgroup's 16 tokens; writes
 // out = g_win o_win + g_cmp o_cmp + g_slc o_slc (a branch with no keys adds 0).
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
+__global__ __launch_bounds__(kPfThreads, 1) void k_prefill_shared(PaParams p) {
   using S = PfShape<D>;
   constexpr int NCH = S::kNch, NDT = S::kDt;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -223,9 +255,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
 
   // the tokens' selections as bitmaps (bounds-checked block indices) and their
   // union as an ascending list
-  for (int i = threadIdx.x; i < kPfTokens * kPfMaskWords; i += 256) (&ps.mask[0][0])[i] = 0u;
+  for (int i = threadIdx.x; i < kPfTokens * kPfMaskWords; i += kPfThreads) (&ps.mask[0][0])[i] = 0u;
   __syncthreads();
-  for (int i = threadIdx.x; i < kPfTokens * p.top_k; i += 256) {
+  for (int i = threadIdx.x; i < kPfTokens * p.top_k; i += kPfThreads) {
     const int u = i / p.top_k, k = tok0 + u;
     if (k < p.tokens) {
       const int b = p.sel[((size_t)k * p.hkv + head) * p.top_k + i % p.top_k];
@@ -236,15 +268,15 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
   {
     const int nwords = (nb + 31) / 32;
     int cnt = 0;                               // thread i owns word i (at most 4096 blocks: 128 words)
-    for (int w = threadIdx.x; w < nwords; w += 256) {
+    for (int w = threadIdx.x; w < nwords; w += kPfThreads) {
       uint32_t x = 0u;
 #pragma unroll
       for (int u = 0; u < kPfTokens; ++u) x |= ps.mask[u][w];
       cnt += __builtin_popcount(x);
     }
     int total;
-    int pos = block_exclusive_scan(cnt, ps.scan_w, &total);
-    for (int w = threadIdx.x; w < nwords; w += 256) {
+    int pos = pf_block_scan(cnt, ps.scan_w, &total);
+    for (int w = threadIdx.x; w < nwords; w += kPfThreads) {
       uint32_t x = 0u;
 #pragma unroll
       for (int u = 0; u < kPfTokens; ++u) x |= ps.mask[u][w];
@@ -290,16 +322,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
       Ksrc = p.K + (size_t)head * L * D;
       Vsrc = p.V + (size_t)head * L * D;
     }
-    // tile j: its first position and valid rows (the union's j-th block for the
-    // selected branch, else the j-th 64 positions from base)
-    auto tile_at = [&](int j, int& start) -> int {
-      if (br == 2) {
-        start = ps.list[j] * kBlock;
-        return min(kBlock, L - start);
-      }
-      start = base + j * kBlock;
-      return min(kBlock, base + count - start);
-    };
+    // tile j's first position (the union's j-th block for the selected branch, else
+    // the j-th 64 positions from base); its valid rows are min(64, lim - start)
+    const int lim = (br == 2) ? L : base + count;
+    auto tile_start = [&](int j) -> int { return (br == 2) ? ps.list[j] * kBlock : base + j * kBlock; };
     const int ntiles = (count + kBlock - 1) / kBlock;
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
     f32x4 acc[2][NDT];
@@ -309,23 +335,24 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
       for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (ntiles > 0) {
-      StageRegs<D> sr;
-      int st0;
-      const int nv0 = tile_at(0, st0);
-      stage_load<D>(Ksrc + (size_t)st0 * D, Vsrc + (size_t)st0 * D, nv0, sr);
+      // Tile j is computed from LDS buffer j&1 while the global loads of tiles j+1
+      // and j+2 are in flight in the two register sets (tile j+1's are stored to
+      // the other buffer after the compute, then that set loads tile j+3).
+      StageRegs<D> sr0, sr1;
+      auto load_tile = [&](int j, StageRegs<D>& r) {
+        const int st = tile_start(j);
+        stage_load<D>(Ksrc + (size_t)st * D, Vsrc + (size_t)st * D, min(kBlock, lim - st), r);
+      };
+      load_tile(0, sr0);
+      if (ntiles > 1) load_tile(1, sr1);
       __syncthreads();                         // the previous branch is done with the buffers
-      stage_store<D>(sr, bufs);
+      stage_store<D>(sr0, bufs);
+      if (ntiles > 2) load_tile(2, sr0);
 #pragma unroll 1
       for (int j = 0; j < ntiles; ++j) {
-        uint16_t* cur = bufs + (j & 1) * S::kBufElems;
-        if (j + 1 < ntiles) {
-          int stn;
-          const int nvn = tile_at(j + 1, stn);
-          stage_load<D>(Ksrc + (size_t)stn * D, Vsrc + (size_t)stn * D, nvn, sr);
-        }
         __syncthreads();                       // tile j staged by every thread
-        int tstart;
-        const int nvj = tile_at(j, tstart);
+        const int tstart = tile_start(j);
+        const int nvj = min(kBlock, lim - tstart);
         bool any = true;
         if (br == 2) {                         // a token keeps the block only if it selected it
           const int b = tstart / kBlock;
@@ -338,8 +365,16 @@ __global__ __launch_bounds__(256, 2) void k_prefill_shared(PaParams p) {
             any |= mine;
           }
         }
-        if (any) shared_tile<D>(cur, tstart, lo, hi, qf, p.scale_log2, m, l, acc);
-        if (j + 1 < ntiles) stage_store<D>(sr, bufs + ((j + 1) & 1) * S::kBufElems);
+        if (any) shared_tile<D>(bufs + (j & 1) * S::kBufElems, tstart, lo, hi, qf, p.scale_log2, m, l, acc);
+        // the register set holding tile j+1 (sr1 for even j) goes to the other
+        // buffer and then loads tile j+3
+        if (j & 1) {
+          if (j + 1 < ntiles) stage_store<D>(sr0, bufs);
+          if (j + 3 < ntiles) load_tile(j + 3, sr0);
+        } else {
+          if (j + 1 < ntiles) stage_store<D>(sr1, bufs + S::kBufElems);
+          if (j + 3 < ntiles) load_tile(j + 3, sr1);
+        }
       }
     }
     // this branch's gated, normalised output goes straight to (or onto) the outputs
@@ -377,7 +412,7 @@ static hipError_t launch_pa(const PrefillArgs& a) {
   if ((a.max_len + kBlock - 1) / kBlock > kPfMaxBlocks || a.top_k > 64) return hipErrorInvalidValue;
   dim3 g1((a.tokens + kPfTokens - 1) / kPfTokens, a.hkv, 1);
   const size_t lds = (size_t)2 * PfShape<D>::kBufElems * sizeof(uint16_t) + sizeof(PfSel);
-  hipLaunchKernelGGL((k_prefill_shared<D>), g1, dim3(256), lds, a.stream, p);
+  hipLaunchKernelGGL((k_prefill_shared<D>), g1, dim3(kPfThreads), lds, a.stream, p);
   return hipGetLastError();
 }
 
