@@ -6,7 +6,7 @@
 // lane owns one head and a fixed set of 16 keys; the probabilities it holds are
 // exactly the B operand of O^T = V^T P^T, so P never leaves registers.  V is
 // staged in LDS row-major (padded so the transposed reads are conflict-free) and
-// read as the A operand.  K is loaded straight into the MFMA layout.  fp32
+// read as the A operand (bf16: with gfx950's transposing LDS read).  K is loaded straight into the MFMA layout.  fp32
 // inputs use v_mfma_f32_16x16x4_f32 with the same lane layout.  The softmax is
 // online, in the log2 domain.  The steps are separate so that a caller walking
 // several tiles can issue the next tile's K loads once the scores are formed and
@@ -23,7 +23,9 @@ struct AttnTiling {
   static constexpr int kLanesPerRow = D * E::kBytes / 16;
   static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
   static constexpr int kLoads = kBlock / kRowsPerLoad;    // V staging loads per lane
-  static constexpr int kRowStride = D + 4;                // LDS row stride (elements), see reads
+  // LDS row stride (elements): bf16 rows 8 banks apart for the transposing reads,
+  // fp32 rows one bank apart for the column reads
+  static constexpr int kRowStride = E::kBytes == 2 ? D + 16 : D + 4;
   static constexpr int kDt = D / 16;                      // 16-wide output column tiles
 };
 
@@ -101,10 +103,7 @@ __device__ __forceinline__ void tile_stage_v(const TileRegs<E, D>& r, typename E
   const int col = (lane % T::kLanesPerRow) * T::kEpl, r0 = lane / T::kLanesPerRow;
 #pragma unroll
   for (int i = 0; i < T::kLoads; ++i) {
-    typename E::storage* dst = lds + (T::kRowsPerLoad * i + r0) * T::kRowStride + col;
-    uint2* d2 = reinterpret_cast<uint2*>(dst);
-    d2[0] = make_uint2(r.vf[i][0], r.vf[i][1]);
-    d2[1] = make_uint2(r.vf[i][2], r.vf[i][3]);
+    st16(lds + (T::kRowsPerLoad * i + r0) * T::kRowStride + col, r.vf[i]);    // 16-byte aligned rows
   }
 }
 
@@ -159,18 +158,22 @@ __device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, f
       pb[1] = f32_to_bf16_bits(acc_s[2 * s][2]) | (f32_to_bf16_bits(acc_s[2 * s][3]) << 16);
       pb[2] = f32_to_bf16_bits(acc_s[2 * s + 1][0]) | (f32_to_bf16_bits(acc_s[2 * s + 1][1]) << 16);
       pb[3] = f32_to_bf16_bits(acc_s[2 * s + 1][2]) | (f32_to_bf16_bits(acc_s[2 * s + 1][3]) << 16);
+      // A operand of lane (n, g): V[kb + j][16 dt + n], kb = 32s + 16h + 4g, j = 0..3.
+      // ds_read_b64_tr_b16 over 16 lanes returns to lane 4a + b the b-th 16-bit
+      // element of the rows read by lanes a, a + 4, a + 8, a + 12, so lane (n, g)
+      // reads row kb + n/4, columns 16 dt + 4(n%4) .. +3.
       const uint16_t* vl = reinterpret_cast<const uint16_t*>(lds);
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #pragma unroll
       for (int dt = 0; dt < T::kDt; ++dt) {
-        const int col = 16 * dt + n;
         u32x4 va;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int kb = 32 * s + 16 * h + 4 * g;
-          const uint32_t v0 = vl[(kb + 0) * SV + col], v1 = vl[(kb + 1) * SV + col];
-          const uint32_t v2 = vl[(kb + 2) * SV + col], v3 = vl[(kb + 3) * SV + col];
-          va[2 * h] = v0 | (v1 << 16);
-          va[2 * h + 1] = v2 | (v3 << 16);
+          const uint16_t* src = vl + (32 * s + 16 * h + 4 * g + (n >> 2)) * SV + 16 * dt + 4 * (n & 3);
+          const uint2 w = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)src));
+          va[2 * h] = w.x;
+          va[2 * h + 1] = w.y;
         }
         acc_o[dt] = mfma_bf16_16x16x32(va, pb, acc_o[dt]);
       }

@@ -104,7 +104,7 @@ Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
   if (wc_tiles <= 2048) {
     pl.tpw_wc = 4; pl.tpw_slc = 1;
   } else if (wc_tiles <= 6144) {
-    pl.tpw_wc = 8; pl.tpw_slc = 4;
+    pl.tpw_wc = 11; pl.tpw_slc = 4;
   } else {
     pl.tpw_wc = 4; pl.tpw_slc = 2;
   }
