@@ -117,27 +117,36 @@ __device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, f
   constexpr int SV = T::kRowStride;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
+  // max of the raw scores over the tile's valid keys (no mask on a full tile); the
+  // softmax runs in log2 units, x = s * scale_log2
   float mt = -INFINITY;
+  if (nvalid == kBlock) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = 16 * t + 4 * g + i;
-      const float x = (key < nvalid) ? acc_s[t][i] * scale_log2 : -INFINITY;
-      acc_s[t][i] = x;
-      mt = fmaxf(mt, x);
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, acc_s[t][i]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * t + 4 * g + i;
+        const float x = (key < nvalid) ? acc_s[t][i] : -INFINITY;
+        acc_s[t][i] = x;
+        mt = fmaxf(mt, x);
+      }
     }
   }
   mt = fmaxf(mt, shfl_xor_f(mt, 16));
   mt = fmaxf(mt, shfl_xor_f(mt, 32));
-  const float m_new = fmaxf(m_run, mt);
+  const float m_new = fmaxf(m_run, mt * scale_log2);
   const float corr = fast_exp2(m_run - m_new);     // 0 when m_run = -inf
   float psum = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pv = fast_exp2(acc_s[t][i] - m_new);
+      const float pv = fast_exp2(fmaf(acc_s[t][i], scale_log2, -m_new));
       acc_s[t][i] = pv;
       psum += pv;
     }
@@ -154,10 +163,10 @@ __device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, f
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 pb;
-      pb[0] = f32_to_bf16_bits(acc_s[2 * s][0]) | (f32_to_bf16_bits(acc_s[2 * s][1]) << 16);
-      pb[1] = f32_to_bf16_bits(acc_s[2 * s][2]) | (f32_to_bf16_bits(acc_s[2 * s][3]) << 16);
-      pb[2] = f32_to_bf16_bits(acc_s[2 * s + 1][0]) | (f32_to_bf16_bits(acc_s[2 * s + 1][1]) << 16);
-      pb[3] = f32_to_bf16_bits(acc_s[2 * s + 1][2]) | (f32_to_bf16_bits(acc_s[2 * s + 1][3]) << 16);
+      pb[0] = pack_bf16x2(acc_s[2 * s][0], acc_s[2 * s][1]);
+      pb[1] = pack_bf16x2(acc_s[2 * s][2], acc_s[2 * s][3]);
+      pb[2] = pack_bf16x2(acc_s[2 * s + 1][0], acc_s[2 * s + 1][1]);
+      pb[3] = pack_bf16x2(acc_s[2 * s + 1][2], acc_s[2 * s + 1][3]);
       // A operand of lane (n, g): V[kb + j][16 dt + n], kb = 32s + 16h + 4g, j = 0..3.
       // ds_read_b64_tr_b16 over 16 lanes returns to lane 4a + b the b-th 16-bit
       // element of the rows read by lanes a, a + 4, a + 8, a + 12, so lane (n, g)
