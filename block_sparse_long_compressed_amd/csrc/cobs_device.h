@@ -80,6 +80,7 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLnBlock = 4.1588830833596715f;   // ln 64: a full block's ln n_b
 
 // Order-preserving map of a float to uint32 (larger float -> larger key); -0 maps as +0.
 __device__ __forceinline__ uint32_t orderable(float f) {

@@ -104,17 +104,23 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
   float run_m = -INFINITY, run_s = 0.f;        // LSE partial of head n over this lane's blocks
   // scores s4[i] of blocks tile*16 + 4g + i for head n: running LSE and block-major hand-off
   auto post = [&](int tile, const f32x4& s4, bool add_ln_n) {
+    float sv[4];
+    float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = tile * 16 + 4 * g + i;
       const int nbk = min(kBlock, L - b * kBlock);
-      const float s = (b < ncand) ? s4[i] + (add_ln_n ? __logf((float)nbk) : 0.f) : -INFINITY;
-      const float mx = fmaxf(run_m, s);
-      if (mx != -INFINITY) {
-        run_s = run_s * __expf(run_m - mx) + __expf(s - mx);
-        run_m = mx;
-      }
-      if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), s);
+      const float ln_n = !add_ln_n ? 0.f : (nbk == kBlock ? kLnBlock : __logf((float)nbk));
+      sv[i] = (b < ncand) ? s4[i] + ln_n : -INFINITY;
+      mt = fmaxf(mt, sv[i]);
+      if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), sv[i]);
+    }
+    const float mx = fmaxf(run_m, mt);          // one rescale per tile
+    if (mx != -INFINITY) {
+      run_s *= __expf(run_m - mx);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) run_s += __expf(sv[i] - mx);
+      run_m = mx;
     }
   };
   if constexpr (KIND == 2) {

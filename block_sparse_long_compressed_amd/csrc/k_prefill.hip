@@ -251,16 +251,22 @@ __global__ __launch_bounds__(256, (KIND == 1 || KIND == 4) ? 2 : 3) void k_prefi
           rows_of(tile + 4 * RING, mrow, vrow[r]);
           sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
         }
+        float sv[4];
+        float mt = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int b = tile * 16 + 4 * g + i;
-          const float sv = (b < ncand) ? s4[i] + __logf((float)min(kBlock, L - b * kBlock)) : -INFINITY;
-          const float mx = fmaxf(run_m, sv);
-          if (mx != -INFINITY) {
-            run_s = run_s * __expf(run_m - mx) + __expf(sv - mx);
-            run_m = mx;
-          }
-          s_sc[b * 16 + n] = sv;
+          const int nbk = min(kBlock, L - b * kBlock);
+          sv[i] = (b < ncand) ? s4[i] + (nbk == kBlock ? kLnBlock : __logf((float)nbk)) : -INFINITY;
+          mt = fmaxf(mt, sv[i]);
+          s_sc[b * 16 + n] = sv[i];
+        }
+        const float mx = fmaxf(run_m, mt);      // one rescale per tile
+        if (mx != -INFINITY) {
+          run_s *= __expf(run_m - mx);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) run_s += __expf(sv[i] - mx);
+          run_m = mx;
         }
       }
     }
