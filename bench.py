@@ -80,10 +80,14 @@ def calibrated_subspace(w, g):
     return B.cobs_query_subspace(U.params_for(w), g["Qcal"], w.subspace)
 
 
-def counter_traffic(workload):
+def counter_traffic(workload, alpha=None):
     """HBM bytes per launch of the decode kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (copy-calibrated), or None when there is no
-    summary for this workload or the kernel sources changed since it was taken."""
+    summary for this workload, the kernel sources changed since it was taken, or
+    alpha is not the workload's own (the counters were taken at that alpha)."""
+    from block_sparse_long_compressed_amd import synth
+    if alpha is not None and workload in synth.WORKLOADS and alpha != synth.WORKLOADS[workload].alpha:
+        return None
     import hashlib
     path = os.path.join(ROOT, "profiles", f"k_decode_{workload}_hbm_bytes.md")
     if not os.path.exists(path):
@@ -304,7 +308,7 @@ def main():
                    "alpha": alpha, "step_bytes": step_bytes, "replicas": R, "graph_replay": not args.eager},
         "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": counter_traffic(w.name), "bytes_per_launch": step_bytes,
+                     "traffic": counter_traffic(w.name, alpha), "bytes_per_launch": step_bytes,
                      "avg_launch_us": ms_step * 1e3,
                      "attention_only": {"avg_launch_us": attn_us, "bytes_per_launch": attn_bytes,
                                         "achieved": attn_gbps}},
