@@ -166,10 +166,20 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
     }
     mt = fmaxf(mt, shfl_xor_f(mt, 16));
     mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    const float m_new = fmaxf(m[u], mt * scale_log2);
-    // a token with no visible key yet keeps (m, l, acc) = (-inf, 0, 0); its P is all zero
-    const float corr = (m_new == -INFINITY) ? 1.f : fast_exp2(m[u] - m_new);
-    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+    // Rescale l and the output only when some lane's running max (log2 units) moved:
+    // the factor is exactly 1 otherwise.  (Letting the max lag behind, so that P may
+    // exceed 1, skips more rescales but loses the exact P = 1 at the maximum and
+    // measured 3x the output error.)  A token with no visible key yet keeps
+    // (m, l, acc) = (-inf, 0, 0); its P is all zero.
+    const float m_cand = fmaxf(m[u], mt * scale_log2);
+    if (__builtin_amdgcn_ballot_w64(m_cand > m[u])) {
+      const float corr = (m_cand == -INFINITY) ? 1.f : fast_exp2(m[u] - m_cand);
+      l[u] *= corr;
+#pragma unroll
+      for (int dt = 0; dt < S::kDt; ++dt) acc[u][dt] *= corr;
+      m[u] = m_cand;
+    }
+    const float mref = (m[u] == -INFINITY) ? 0.f : m[u];
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -180,10 +190,7 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
         psum += pv;
       }
     }
-    l[u] = l[u] * corr + psum;
-    m[u] = m_new;
-#pragma unroll
-    for (int dt = 0; dt < S::kDt; ++dt) acc[u][dt] *= corr;
+    l[u] += psum;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       pb[u][h][0] = pack_bf16x2(s[u][2 * h][0], s[u][2 * h][1]);
