@@ -326,22 +326,25 @@ __global__ __launch_bounds__(256, (KIND == 1 || KIND == 4) ? 2 : 3) void k_prefi
   for (int i = total + (int)threadIdx.x; i < p.top_k; i += 256) sel_u[i] = -1;
 }
 
-// Diagonal summaries, up to kPairMaxBlocks candidate blocks: one workgroup per two
+// Diagonal summaries, up to kPairMaxBlocks candidate blocks: one workgroup per T
 // consecutive tokens of a kv-head group.  Each summary tile is loaded once and
-// scored for both tokens (their query weights sit in LDS in the B-operand layout,
-// read 16 bytes at a time), so a tile's load serves twice the MFMA work.  Every
+// scored for all T tokens (their query weights sit in LDS in the B-operand layout,
+// read 16 bytes at a time), so a tile's load serves T times the MFMA work.  Every
 // lane keeps its tiles' scores in registers; the group score of a block is formed
 // across the 16 lanes of a row (one head each) with DPP row rotations, so no
 // per-head score array is staged.  Then the workgroup radix select, per token.
 constexpr int kPairTiles = 8;                         // tiles per wave (4 waves)
 constexpr int kPairMaxBlocks = 4 * kPairTiles * 16;   // 512
+constexpr int kPairTMax = 4;                          // tokens per workgroup, at most
+constexpr int kPairTokens = 2;   // measured: 4 tokens (two waves per SIMD, four serial selects) is slower
 
 struct PsPairLds {
-  float red_m[2][4][16], red_s[2][4][16];
-  float lse_sh[2][16];
+  float red_m[kPairTMax][4][16], red_s[kPairTMax][4][16];
+  float lse_sh[kPairTMax][16];
   uint32_t hist2[2][4][256];
   int scan_w[4];
-  // followed by the weights [2][2D/16][64][4] floats and the keys [2][kPairMaxBlocks]
+  int ncand[kPairTMax];
+  // followed by the weights [T][2D/16][64][4] floats and the keys [T][kPairMaxBlocks]
 };
 
 // Full reduction over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1).
@@ -360,43 +363,45 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-template <typename E, int D>
-__global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
+template <typename E, int D, int T>
+__global__ __launch_bounds__(256, T <= 2 ? 3 : 2) void k_prefill_select_pair(PsParams p) {
   constexpr int NU = D / 16;
   constexpr int NQ = 2 * NU;                          // 16-byte weight groups per token: lin, then quad
   extern __shared__ __align__(16) unsigned char smem[];
   PsPairLds& sl = *reinterpret_cast<PsPairLds*>(smem);
-  float* wB = reinterpret_cast<float*>(smem + sizeof(PsPairLds));        // [2][NQ][64][4]
-  uint32_t* keys = reinterpret_cast<uint32_t*>(wB + 2 * NQ * 64 * 4);   // [2][kPairMaxBlocks]
+  float* wB = reinterpret_cast<float*>(smem + sizeof(PsPairLds));        // [T][NQ][64][4]
+  uint32_t* keys = reinterpret_cast<uint32_t*>(wB + T * NQ * 64 * 4);   // [T][kPairMaxBlocks]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int tok0 = 2 * blockIdx.x, head = blockIdx.y, seq = blockIdx.z;
+  const int tok0 = T * blockIdx.x, head = blockIdx.y, seq = blockIdx.z;
   const int L = p.seq_lens ? p.seq_lens[seq] : p.L_fixed;
   const int G = p.group;
-  bool live[2];
-  int ncand[2];
+  bool live[T];
+  int ncand[T], nmax = 0;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < T; ++u) {
     live[u] = tok0 + u < p.tokens;
     ncand[u] = live[u] ? candidate_blocks(L, p.q_pos0 + tok0 + u) : 0;
+    nmax = max(nmax, ncand[u]);
   }
-  const int tiles = (max(ncand[0], ncand[1]) + 15) / 16;
+  if (threadIdx.x < T) sl.ncand[threadIdx.x] = candidate_blocks(L, p.q_pos0 + tok0 + threadIdx.x);
+  const int tiles = (nmax + 15) / 16;
   const size_t sum_base = ((size_t)seq * p.hkv + head) * p.nb_max;
   const bool use_quad = p.alpha != 0.f;
 
   // the first tile's summary rows go out before the weights are formed
   SumTile<D, 0> st;
   auto load_tile = [&](int tile) {
-    const int brow = min(tile * 16 + n, max(ncand[0], ncand[1]) - 1);
+    const int brow = min(tile * 16 + n, nmax - 1);
     const void *mrow, *vrow;
     summary_rows<D, 0>(p.mu, p.so, sum_base + brow, 0, D, mrow, vrow);
     sum_tile_load<D, 0>(mrow, vrow, 0, D, g, use_quad, st);
   };
   if (wave < tiles) load_tile(wave);
 
-  // weights of both tokens: lane (n, g) of 16-byte group j holds feature 16(j % NU) + 4g + c,
+  // weights of the T tokens: lane (n, g) of 16-byte group j holds feature 16(j % NU) + 4g + c,
   // c = 0..3: scale q (j < NU), then alpha/2 (scale q)^2; zero for columns n >= G
-  for (int idx = threadIdx.x; idx < 2 * NU * 64; idx += 256) {
+  for (int idx = threadIdx.x; idx < T * NU * 64; idx += 256) {
     const int u = idx / (NU * 64), r = idx % (NU * 64), j = r / 64, l = r % 64;
     const int ln = l & 15, lg = l >> 4;
     float q4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -414,25 +419,27 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
   }
   __syncthreads();
 
-  // ---- scores of tiles wave, wave + 4, ... for both tokens, kept in registers
-  f32x4 sreg[2][kPairTiles];
-  float run_m[2] = {-INFINITY, -INFINITY}, run_s[2] = {0.f, 0.f};
+  // ---- scores of tiles wave, wave + 4, ... for the T tokens, kept in registers
+  f32x4 sreg[T][kPairTiles];
+  float run_m[T], run_s[T];
+#pragma unroll
+  for (int u = 0; u < T; ++u) { run_m[u] = -INFINITY; run_s[u] = 0.f; }
 #pragma unroll
   for (int i = 0; i < kPairTiles; ++i) {
     const int tile = wave + 4 * i;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) sreg[u][i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int u = 0; u < T; ++u) sreg[u][i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (tile < tiles) {
-      f32x4 acc[2], acc2[2];
+      f32x4 acc[T], acc2[T];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < T; ++u) {
         acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc2[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int j = 0; j < NU; ++j) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < T; ++u) {
           const f32x4 w = *reinterpret_cast<const f32x4*>(&wB[(((size_t)u * NQ + j) * 64 + lane) * 4]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) acc[u] = mfma_f32_16x16x4(st.m4[j][c], w[c], acc[u]);
@@ -442,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int u = 0; u < T; ++u) {
             const f32x4 w = *reinterpret_cast<const f32x4*>(&wB[(((size_t)u * NQ + NU + j) * 64 + lane) * 4]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc2[u] = mfma_f32_16x16x4(st.v4[0][j][c], w[c], acc2[u]);
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
       }
       if (tile + 4 < tiles) load_tile(tile + 4);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < T; ++u) {
         const f32x4 s4 = acc[u] + acc2[u];
         float mt = -INFINITY;
 #pragma unroll
@@ -474,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
   }
   // per-head log-sum-exp over the candidates, per token
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < T; ++u) {
 #pragma unroll
     for (int m = 16; m < 64; m <<= 1) {
       const float om = shfl_xor_f(run_m[u], m), os = shfl_xor_f(run_s[u], m);
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
     if (g == 0) { sl.red_m[u][wave][n] = run_m[u]; sl.red_s[u][wave][n] = run_s[u]; }
   }
   __syncthreads();
-  if (threadIdx.x < 32) {
+  if (threadIdx.x < 16 * T) {
     const int u = threadIdx.x >> 4, h = threadIdx.x & 15;
     float M = -INFINITY, S = 0.f;
     for (int w = 0; w < 4; ++w) {
@@ -502,7 +509,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
   // ---- group scores shat_b = ln sum_h exp(s_hb - LSE_h): the 16 lanes of a row hold
   // the 16 heads of blocks 4g + k; lane n = k of the row writes block 4g + k's key
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < T; ++u) {
     const float lse_n = sl.lse_sh[u][n];
     const bool head_ok = n < G && lse_n != -INFINITY;
 #pragma unroll
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
   }
   if (p.sel_score) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < T; ++u) {
       if (!live[u]) continue;
       float* ss = p.sel_score + (((size_t)seq * p.tokens + tok0 + u) * p.hkv + head) * p.nb_max;
       for (int b = ncand[u] + threadIdx.x; b < p.nb_max; b += 256) ss[b] = -INFINITY;
@@ -537,9 +544,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_select_pair(PsParams p) {
   __syncthreads();
 
 #pragma unroll 1
-  for (int u = 0; u < 2; ++u) {
-    if (u == 1 && !live[1]) break;
-    const int nc = u == 0 ? ncand[0] : ncand[1];
+  for (int u = 0; u < T; ++u) {
+    if (tok0 + u >= p.tokens) break;
+    const int nc = sl.ncand[u];
     int32_t* sel_u = p.sel + (((size_t)seq * p.tokens + tok0 + u) * p.hkv + head) * p.top_k;
     const int per = (nc + 255) / 256;
     const int total = wg_select_topk(keys + u * kPairMaxBlocks, nc, per, p.top_k, &sl.hist2[0][0][0],
@@ -654,10 +661,11 @@ __global__ __launch_bounds__(256) void k_attn_unit(AuParams p) {
 template <typename E, int D, int KIND>
 static hipError_t launch_ps(const PrefillArgs& a, const PsParams& sp) {
   if (KIND == 0 && sp.nb_pad <= kPairMaxBlocks) {
-    dim3 grid((a.tokens + 1) / 2, a.hkv, a.batch);
-    const size_t lds = sizeof(PsPairLds) + (size_t)2 * (D / 8) * 64 * 4 * sizeof(float) +
-                       (size_t)2 * kPairMaxBlocks * sizeof(uint32_t);
-    hipLaunchKernelGGL((k_prefill_select_pair<E, D>), grid, dim3(256), lds, a.stream, sp);
+    constexpr int T = kPairTokens;
+    dim3 grid((a.tokens + T - 1) / T, a.hkv, a.batch);
+    const size_t lds = sizeof(PsPairLds) + (size_t)T * (D / 8) * 64 * 4 * sizeof(float) +
+                       (size_t)T * kPairMaxBlocks * sizeof(uint32_t);
+    hipLaunchKernelGGL((k_prefill_select_pair<E, D, T>), grid, dim3(256), lds, a.stream, sp);
     return hipGetLastError();
   }
   if (sp.nb_pad <= kPsWgMaxBlocks) {
