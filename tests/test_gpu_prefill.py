@@ -45,8 +45,11 @@ BASE = dict(batch=1, n_q_heads=32, n_kv_heads=2, head_dim=128, top_k=8, window=3
             so_kind="diag", rank=0, alpha=1.0, dtype="bf16", needles=3)
 
 
-def test_prefill_ragged_tail():
-    L, T = 1500, 200
+@pytest.mark.parametrize("T", [200, 37])
+def test_prefill_ragged_tail(T):
+    """Chunks that are not a multiple of the attention kernel's 16 tokens per
+    workgroup (37 = 2 x 16 + 5) nor of the scoring kernel's two (odd)."""
+    L = 1500
     w = synth.Workload("pf", max_len=L, min_len=L, n_q_tokens=T, q_pos0=L - T, **BASE)
     x = synth.make_inputs(w, 11)
     check_prefill(w, x, tokens=list(range(T)))
