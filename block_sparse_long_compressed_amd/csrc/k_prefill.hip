@@ -1,21 +1,26 @@
-// Chunked causal prefill (gfx950): per-token block selection and per-token
-// three-branch attention for queries at positions t = q_pos0 .. q_pos0+T-1 of a
-// sequence whose block summaries were built once over the whole prefix.
+// Chunked causal prefill (gfx950): per-token block selection, and the per-token
+// attention path for fp32 inputs, for queries at positions t = q_pos0 .. q_pos0+T-1
+// of a sequence whose block summaries were built once over the whole prefix.
 //
 // Selection (COBS explainer, Technisches Resuemee 2.1-2.3; skill card "Method")
 // is the decode rule applied to each token's causal candidate set (blocks whose
-// keys all lie at positions <= t).  One wave owns one (token, kv-head group):
-// pass 1 runs the fp32-MFMA block scores over the candidates and keeps an online
-// per-head log-sum-exp; pass 2 recomputes the scores, normalises each head by its
-// LSE and reduces over the group's 16 heads with lane shuffles into an LDS key per
-// block; a single-wave MSB-first radix select (DPP scans, ballots, no barriers)
-// then keeps the top-k, ties to the lower block index.
+// keys all lie at positions <= t).  Three kernels, by kind and context length:
+//   k_prefill_select_pair  diagonal summaries, up to 512 blocks: two tokens per
+//                          workgroup share each summary tile load; scores stay in
+//                          registers and the group score is a DPP row reduction;
+//   k_prefill_select_wg    other kinds, up to 2048 blocks: one workgroup per
+//                          (token, group), per-head scores staged in LDS;
+//   k_prefill_select       longer contexts: one wave per (token, group) scoring
+//                          twice (online log-sum-exp, then the group scores) and a
+//                          single-wave radix select (DPP scans, ballots, no barriers).
+// All keep the top-k with ties to the lower block index.
 //
-// Attention (NSA branches, Janus issue #181): one workgroup per (token, group);
-// wave 0 runs the selected blocks, wave 1 the window [t-W+1, t], waves 2-3 the
-// two halves of the visible pooled tokens, each with the shared 64-key tile
-// routine; the waves' (max, sum, O) are merged in LDS and the gated sum is
-// written directly (no workspace, no second pass).
+// Attention for fp32 inputs (NSA branches, Janus issue #181): one workgroup per
+// (token, group); wave 0 runs the selected blocks, wave 1 the window [t-W+1, t],
+// waves 2-3 the two halves of the visible pooled tokens, each with the shared
+// 64-key tile routine; the waves' (max, sum, O) are merged in LDS and the gated
+// sum is written directly.  bf16 inputs use the token-blocked kernel in
+// k_prefill_attn.hip.
 #include "attn_tile.h"
 #include "cobs_device.h"
 #include "cobs_launch.h"
