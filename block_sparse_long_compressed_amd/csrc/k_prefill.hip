@@ -343,6 +343,11 @@ constexpr int kPairMaxBlocks = 4 * kPairTiles * 16;   // 512
 constexpr int kPairTMax = 4;                          // tokens per workgroup, at most
 constexpr int kPairTokens = 2;   // measured: 4 tokens (two waves per SIMD, four serial selects) is slower
 
+template <typename E, int D>
+constexpr size_t pair_weight_bytes(int T) {       // query weights of a workgroup's tokens in LDS
+  return E::kBytes == 2 ? (size_t)T * 3 * (D / 32) * 64 * 16 : (size_t)T * (D / 8) * 64 * 16;
+}
+
 struct PsPairLds {
   float red_m[kPairTMax][4][16], red_s[kPairTMax][4][16];
   float lse_sh[kPairTMax][16];
@@ -369,13 +374,15 @@ __device__ __forceinline__ float row_sum16(float x) {
 }
 
 template <typename E, int D, int T>
-__global__ __launch_bounds__(256, T <= 2 ? 3 : 2) void k_prefill_select_pair(PsParams p) {
-  constexpr int NU = D / 16;
-  constexpr int NQ = 2 * NU;                          // 16-byte weight groups per token: lin, then quad
+__global__ __launch_bounds__(256, (T <= 2 && E::kBytes == 4) ? 3 : 2) void k_prefill_select_pair(PsParams p) {
+  constexpr int NU = D / 16, NJ = D / 32;
+  constexpr int NQ = 2 * NU;                          // fp32: 16-byte weight groups per token, lin then quad
+  constexpr bool kSplit = E::kBytes == 2;             // bf16 queries: split-bf16 contraction
   extern __shared__ __align__(16) unsigned char smem[];
   PsPairLds& sl = *reinterpret_cast<PsPairLds*>(smem);
-  float* wB = reinterpret_cast<float*>(smem + sizeof(PsPairLds));        // [T][NQ][64][4]
-  uint32_t* keys = reinterpret_cast<uint32_t*>(wB + T * NQ * 64 * 4);   // [T][kPairMaxBlocks]
+  float* wB = reinterpret_cast<float*>(smem + sizeof(PsPairLds));        // fp32: [T][NQ][64][4]
+  u32x4* wS = reinterpret_cast<u32x4*>(wB);                              // bf16: [T][3][NJ][64]
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem + sizeof(PsPairLds) + pair_weight_bytes<E, D>(T));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int tok0 = T * blockIdx.x, head = blockIdx.y, seq = blockIdx.z;
@@ -404,23 +411,54 @@ __global__ __launch_bounds__(256, T <= 2 ? 3 : 2) void k_prefill_select_pair(PsP
   };
   if (wave < tiles) load_tile(wave);
 
-  // weights of the T tokens: lane (n, g) of 16-byte group j holds feature 16(j % NU) + 4g + c,
-  // c = 0..3: scale q (j < NU), then alpha/2 (scale q)^2; zero for columns n >= G
-  for (int idx = threadIdx.x; idx < T * NU * 64; idx += 256) {
-    const int u = idx / (NU * 64), r = idx % (NU * 64), j = r / 64, l = r % 64;
-    const int ln = l & 15, lg = l >> 4;
-    float q4[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ln < G && live[u])
-      load_q4<E>(p.Q, (((size_t)seq * p.tokens + tok0 + u) * (size_t)(p.hkv * G) + (size_t)head * G + ln) * D +
-                          16 * j + 4 * lg, q4);
-    f32x4 wl, wq;
+  if constexpr (kSplit) {
+    // bf16 queries: the contraction runs on v_mfma_f32_16x16x32_bf16 with exact
+    // products.  Lane (n, g)'s eight k-slots of chunk j are features 16u + 4g + c for
+    // u = 2j, 2j+1 (the order its fp32 summary loads hold); per token and chunk: q
+    // (bf16, exact), and q^2 (exact in fp32, 16 significant bits) as hi + lo bf16 parts
+    // whose sum is exact.  Zero for columns n >= G.
+    for (int idx = threadIdx.x; idx < T * NJ * 64; idx += 256) {
+      const int u = idx / (NJ * 64), r = idx % (NJ * 64), j = r / 64, l = r % 64;
+      const int ln = l & 15, lg = l >> 4;
+      u32x4 qw = {0u, 0u, 0u, 0u};
+      if (ln < G && live[u]) {
+        const uint16_t* qh = static_cast<const uint16_t*>(p.Q) +
+            (((size_t)seq * p.tokens + tok0 + u) * (size_t)(p.hkv * G) + (size_t)head * G + ln) * D;
+        const uint2 x0 = *reinterpret_cast<const uint2*>(qh + 32 * j + 4 * lg);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(qh + 32 * j + 16 + 4 * lg);
+        qw = u32x4{x0.x, x0.y, x1.x, x1.y};
+      }
+      u32x4 hi, lo;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      wl[c] = p.scale * q4[c];
-      wq[c] = 0.5f * p.alpha * wl[c] * wl[c];
+      for (int e = 0; e < 4; ++e) {
+        const float a = __uint_as_float(qw[e] << 16), b = __uint_as_float(qw[e] & 0xFFFF0000u);
+        const float a2 = a * a, b2 = b * b;
+        hi[e] = pack_bf16x2(a2, b2);
+        lo[e] = pack_bf16x2(a2 - __uint_as_float(hi[e] << 16), b2 - __uint_as_float(hi[e] & 0xFFFF0000u));
+      }
+      wS[(((size_t)u * 3 + 0) * NJ + j) * 64 + l] = qw;
+      wS[(((size_t)u * 3 + 1) * NJ + j) * 64 + l] = hi;
+      wS[(((size_t)u * 3 + 2) * NJ + j) * 64 + l] = lo;
     }
-    *reinterpret_cast<f32x4*>(&wB[(((size_t)u * NQ + j) * 64 + l) * 4]) = wl;
-    *reinterpret_cast<f32x4*>(&wB[(((size_t)u * NQ + NU + j) * 64 + l) * 4]) = wq;
+  } else {
+    // weights of the T tokens: lane (n, g) of 16-byte group j holds feature 16(j % NU) + 4g + c,
+    // c = 0..3: scale q (j < NU), then alpha/2 (scale q)^2; zero for columns n >= G
+    for (int idx = threadIdx.x; idx < T * NU * 64; idx += 256) {
+      const int u = idx / (NU * 64), r = idx % (NU * 64), j = r / 64, l = r % 64;
+      const int ln = l & 15, lg = l >> 4;
+      float q4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (ln < G && live[u])
+        load_q4<E>(p.Q, (((size_t)seq * p.tokens + tok0 + u) * (size_t)(p.hkv * G) + (size_t)head * G + ln) * D +
+                            16 * j + 4 * lg, q4);
+      f32x4 wl, wq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        wl[c] = p.scale * q4[c];
+        wq[c] = 0.5f * p.alpha * wl[c] * wl[c];
+      }
+      *reinterpret_cast<f32x4*>(&wB[(((size_t)u * NQ + j) * 64 + l) * 4]) = wl;
+      *reinterpret_cast<f32x4*>(&wB[(((size_t)u * NQ + NU + j) * 64 + l) * 4]) = wq;
+    }
   }
   __syncthreads();
 
@@ -441,23 +479,63 @@ __global__ __launch_bounds__(256, T <= 2 ? 3 : 2) void k_prefill_select_pair(PsP
         acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc2[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      if constexpr (kSplit) {
+        // the tile's fp32 means and variances as hi + lo bf16 parts (16 of their 24
+        // significand bits), in the chunk order of the weights
+        u32x4 mh[NJ], ml[NJ], vh[NJ], vl[NJ];
+        auto split8 = [&](const f32x4& x, const f32x4& y, u32x4& h, u32x4& lw) {
+          h = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+          const float xs[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
 #pragma unroll
-      for (int j = 0; j < NU; ++j) {
+          for (int e = 0; e < 4; ++e)
+            lw[e] = pack_bf16x2(xs[2 * e] - __uint_as_float(h[e] << 16), xs[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
+        };
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          split8(st.m4[2 * j], st.m4[2 * j + 1], mh[j], ml[j]);
+          if (use_quad) split8(st.v4[0][2 * j], st.v4[0][2 * j + 1], vh[j], vl[j]);
+        }
 #pragma unroll
         for (int u = 0; u < T; ++u) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(&wB[(((size_t)u * NQ + j) * 64 + lane) * 4]);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) acc[u] = mfma_f32_16x16x4(st.m4[j][c], w[c], acc[u]);
+          for (int j = 0; j < NJ; ++j) {
+            const u32x4 qw = wS[(((size_t)u * 3 + 0) * NJ + j) * 64 + lane];
+            acc[u] = mfma_bf16_16x16x32(mh[j], qw, acc[u]);
+            acc[u] = mfma_bf16_16x16x32(ml[j], qw, acc[u]);
+          }
+          if (use_quad) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const u32x4 q2h = wS[(((size_t)u * 3 + 1) * NJ + j) * 64 + lane];
+              const u32x4 q2l = wS[(((size_t)u * 3 + 2) * NJ + j) * 64 + lane];
+              acc2[u] = mfma_bf16_16x16x32(vh[j], q2h, acc2[u]);
+              acc2[u] = mfma_bf16_16x16x32(vh[j], q2l, acc2[u]);
+              acc2[u] = mfma_bf16_16x16x32(vl[j], q2h, acc2[u]);
+              acc2[u] = mfma_bf16_16x16x32(vl[j], q2l, acc2[u]);
+            }
+          }
+          acc[u] = p.scale * acc[u] + (0.5f * p.alpha * p.scale * p.scale) * acc2[u];
+          acc2[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      }
-      if (use_quad) {
+      } else {
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
 #pragma unroll
           for (int u = 0; u < T; ++u) {
-            const f32x4 w = *reinterpret_cast<const f32x4*>(&wB[(((size_t)u * NQ + NU + j) * 64 + lane) * 4]);
+            const f32x4 w = *reinterpret_cast<const f32x4*>(&wB[(((size_t)u * NQ + j) * 64 + lane) * 4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc2[u] = mfma_f32_16x16x4(st.v4[0][j][c], w[c], acc2[u]);
+            for (int c = 0; c < 4; ++c) acc[u] = mfma_f32_16x16x4(st.m4[j][c], w[c], acc[u]);
+          }
+        }
+        if (use_quad) {
+#pragma unroll
+          for (int j = 0; j < NU; ++j) {
+#pragma unroll
+            for (int u = 0; u < T; ++u) {
+              const f32x4 w = *reinterpret_cast<const f32x4*>(&wB[(((size_t)u * NQ + NU + j) * 64 + lane) * 4]);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) acc2[u] = mfma_f32_16x16x4(st.v4[0][j][c], w[c], acc2[u]);
+            }
           }
         }
       }
@@ -668,8 +746,7 @@ static hipError_t launch_ps(const PrefillArgs& a, const PsParams& sp) {
   if (KIND == 0 && sp.nb_pad <= kPairMaxBlocks) {
     constexpr int T = kPairTokens;
     dim3 grid((a.tokens + T - 1) / T, a.hkv, a.batch);
-    const size_t lds = sizeof(PsPairLds) + (size_t)T * (D / 8) * 64 * 4 * sizeof(float) +
-                       (size_t)T * kPairMaxBlocks * sizeof(uint32_t);
+    const size_t lds = sizeof(PsPairLds) + pair_weight_bytes<E, D>(T) + (size_t)T * kPairMaxBlocks * sizeof(uint32_t);
     hipLaunchKernelGGL((k_prefill_select_pair<E, D, T>), grid, dim3(256), lds, a.stream, sp);
     return hipGetLastError();
   }
