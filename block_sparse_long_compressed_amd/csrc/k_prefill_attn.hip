@@ -8,9 +8,9 @@
 // A workgroup of 8 waves owns 16 consecutive tokens of one kv-head group (two per
 // wave, so a wave's B operand covers 2 x 16 query heads) and runs the three
 // branches one after the other over 64-key tiles staged once in LDS for all 16
-// tokens (two LDS buffers; the global loads of the next two tiles are in flight
-// in registers while the current tile is consumed); every token masks its own
-// keys:
+// tokens, two tiles per barrier (two LDS buffer pairs; the global loads of the
+// next two tiles are in flight in registers while the current pair is consumed);
+// every token masks its own keys:
 //   window and pooled tokens: consecutive tokens' key ranges nearly coincide, so
 //   each tile of the union range is staged once and a token masks positions
 //   outside its range;
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_prefill_shared(PaParams p) {
   constexpr int NCH = S::kNch, NDT = S::kDt;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* bufs = reinterpret_cast<uint16_t*>(smem);
-  PfSel& ps = *reinterpret_cast<PfSel*>(smem + (size_t)2 * S::kBufElems * sizeof(uint16_t));
+  PfSel& ps = *reinterpret_cast<PfSel*>(smem + (size_t)4 * S::kBufElems * sizeof(uint16_t));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int head = blockIdx.y, G = p.group, L = p.seq_len;
@@ -342,22 +342,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_prefill_shared(PaParams p) {
       for (int dt = 0; dt < NDT; ++dt) acc[u][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (ntiles > 0) {
-      // Tile j is computed from LDS buffer j&1 while the global loads of tiles j+1
-      // and j+2 are in flight in the two register sets (tile j+1's are stored to
-      // the other buffer after the compute, then that set loads tile j+3).
+      // Tiles go in pairs (stages): stage s, tiles 2s and 2s+1, is computed from LDS
+      // buffer pair s&1 after one barrier, while the global loads of the next stage
+      // are in flight in the two register sets; after the compute those are stored
+      // to the other buffer pair and the sets load the stage after.
       StageRegs<D> sr0, sr1;
       auto load_tile = [&](int j, StageRegs<D>& r) {
         const int st = tile_start(j);
         stage_load<D>(Ksrc + (size_t)st * D, Vsrc + (size_t)st * D, min(kBlock, lim - st), r);
       };
-      load_tile(0, sr0);
-      if (ntiles > 1) load_tile(1, sr1);
-      __syncthreads();                         // the previous branch is done with the buffers
-      stage_store<D>(sr0, bufs);
-      if (ntiles > 2) load_tile(2, sr0);
-#pragma unroll 1
-      for (int j = 0; j < ntiles; ++j) {
-        __syncthreads();                       // tile j staged by every thread
+      auto tile_buf = [&](int j) { return bufs + ((j >> 1) & 1) * 2 * S::kBufElems + (j & 1) * S::kBufElems; };
+      auto compute_tile = [&](int j) {
         const int tstart = tile_start(j);
         const int nvj = min(kBlock, lim - tstart);
         bool any = true;
@@ -372,16 +367,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_prefill_shared(PaParams p) {
             any |= mine;
           }
         }
-        if (any) shared_tile<D>(bufs + (j & 1) * S::kBufElems, tstart, lo, hi, qf, p.scale_log2, m, l, acc);
-        // the register set holding tile j+1 (sr1 for even j) goes to the other
-        // buffer and then loads tile j+3
-        if (j & 1) {
-          if (j + 1 < ntiles) stage_store<D>(sr0, bufs);
-          if (j + 3 < ntiles) load_tile(j + 3, sr0);
-        } else {
-          if (j + 1 < ntiles) stage_store<D>(sr1, bufs + S::kBufElems);
-          if (j + 3 < ntiles) load_tile(j + 3, sr1);
-        }
+        if (any) shared_tile<D>(tile_buf(j), tstart, lo, hi, qf, p.scale_log2, m, l, acc);
+      };
+      load_tile(0, sr0);
+      if (ntiles > 1) load_tile(1, sr1);
+      __syncthreads();                         // the previous branch is done with the buffers
+      stage_store<D>(sr0, tile_buf(0));
+      if (ntiles > 1) stage_store<D>(sr1, tile_buf(1));
+      if (ntiles > 2) load_tile(2, sr0);
+      if (ntiles > 3) load_tile(3, sr1);
+#pragma unroll 1
+      for (int j = 0; j < ntiles; j += 2) {
+        __syncthreads();                       // stage j/2 staged by every thread
+        compute_tile(j);
+        if (j + 1 < ntiles) compute_tile(j + 1);
+        if (j + 2 < ntiles) stage_store<D>(sr0, tile_buf(j + 2));
+        if (j + 3 < ntiles) stage_store<D>(sr1, tile_buf(j + 3));
+        if (j + 4 < ntiles) load_tile(j + 4, sr0);
+        if (j + 5 < ntiles) load_tile(j + 5, sr1);
       }
     }
     // this branch's gated, normalised output goes straight to (or onto) the outputs
@@ -418,7 +421,7 @@ static hipError_t launch_pa(const PrefillArgs& a) {
   p.vc = static_cast<const uint16_t*>(a.vc); p.gates = a.gates; p.sel = a.sel; p.out = a.out;
   if ((a.max_len + kBlock - 1) / kBlock > kPfMaxBlocks || a.top_k > 64) return hipErrorInvalidValue;
   dim3 g1((a.tokens + kPfTokens - 1) / kPfTokens, a.hkv, 1);
-  const size_t lds = (size_t)2 * PfShape<D>::kBufElems * sizeof(uint16_t) + sizeof(PfSel);
+  const size_t lds = (size_t)4 * PfShape<D>::kBufElems * sizeof(uint16_t) + sizeof(PfSel);
   hipLaunchKernelGGL((k_prefill_shared<D>), g1, dim3(kPfThreads), lds, a.stream, p);
   return hipGetLastError();
 }
