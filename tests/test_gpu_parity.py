@@ -133,6 +133,16 @@ def run_and_check(w, x, alpha=None, out_tol=1e-2, seqs=None):
     return worst
 
 
+@pytest.mark.parametrize("lens", [[5000, 3333], [2000, 700]])
+def test_decode_max_top_k(lens):
+    """The largest top-k the library accepts (64): most candidates selected at 5000
+    keys, all of them (and -1 padding) at 700 keys (11 blocks)."""
+    w = W("k64", batch=2, max_len=5000, min_len=700, n_q_heads=32, n_kv_heads=2, head_dim=128, top_k=64,
+          window=256, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0, dtype="bf16", needles=3)
+    x = synth.make_inputs(w, 21, lens=np.array(lens))
+    run_and_check(w, x)
+
+
 @pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0, 2.0])
 def test_decode_g16_alpha_sweep(alpha):
     w, x = small("g16_d128_bf16")

@@ -74,6 +74,15 @@ def test_prefill_variants(kind, d, G):
     check_prefill(w, x, tokens=list(range(T)))
 
 
+def test_prefill_max_top_k():
+    """top-k 64 over 78 blocks: the selected-block union of a 16-token workgroup
+    covers most of the prefix."""
+    L, T = 5000, 40
+    w = synth.Workload("pfk", max_len=L, min_len=L, n_q_tokens=T, q_pos0=L - T, **dict(BASE, top_k=64))
+    x = synth.make_inputs(w, 17)
+    check_prefill(w, x, tokens=list(range(T)))
+
+
 def test_prefill_f32_inputs():
     # fp32 Q/K/V take the one-workgroup-per-(token, group) attention path
     L, T = 700, 40
