@@ -124,7 +124,7 @@ __device__ __forceinline__ void stage_store(const StageRegs<D>& r, uint16_t* buf
 template <int D>
 __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start, const int (&lo)[2], const int (&hi)[2],
                                             const u32x4 (&qf)[2][PfShape<D>::kNch], float scale_log2,
-                                            float (&m)[2], float (&l)[2], f32x4 (&acc)[2][PfShape<D>::kDt]) {
+                                            float (&m)[2], f32x4 (&lsum)[2], f32x4 (&acc)[2][PfShape<D>::kDt]) {
   using S = PfShape<D>;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, g = lane >> 4;
@@ -174,23 +174,20 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
     const float m_cand = fmaxf(m[u], mt * scale_log2);
     if (__builtin_amdgcn_ballot_w64(m_cand > m[u])) {
       const float corr = (m_cand == -INFINITY) ? 1.f : fast_exp2(m[u] - m_cand);
-      l[u] *= corr;
+      lsum[u] *= corr;
 #pragma unroll
       for (int dt = 0; dt < S::kDt; ++dt) acc[u][dt] *= corr;
       m[u] = m_cand;
     }
     const float mref = (m[u] == -INFINITY) ? 0.f : m[u];
-    float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pv = fast_exp2(fmaf(s[u][t][i], scale_log2, -mref));
         s[u][t][i] = pv;
-        psum += pv;
       }
     }
-    l[u] += psum;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       pb[u][h][0] = pack_bf16x2(s[u][2 * h][0], s[u][2 * h][1]);
@@ -222,6 +219,12 @@ __device__ __forceinline__ void shared_tile(const uint16_t* buf, int tile_start,
       acc[0][dt] = mfma_bf16_16x16x32(vop, pb[0][h], acc[0][dt]);
       acc[1][dt] = mfma_bf16_16x16x32(vop, pb[1][h], acc[1][dt]);
     }
+    // the softmax denominator as one more output tile with an all-ones A operand:
+    // every row is sum_k P[k][n] over the tile's keys, from the same bf16 P as the
+    // numerator
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    lsum[0] = mfma_bf16_16x16x32(ones, pb[0][h], lsum[0]);
+    lsum[1] = mfma_bf16_16x16x32(ones, pb[1][h], lsum[1]);
   }
 }
 
@@ -334,7 +337,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_prefill_shared(PaParams p) {
     const int lim = (br == 2) ? L : base + count;
     auto tile_start = [&](int j) -> int { return (br == 2) ? ps.list[j] * kBlock : base + j * kBlock; };
     const int ntiles = (count + kBlock - 1) / kBlock;
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY};
+    f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     f32x4 acc[2][NDT];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_prefill_shared(PaParams p) {
             any |= mine;
           }
         }
-        if (any) shared_tile<D>(tile_buf(j), tstart, lo, hi, qf, p.scale_log2, m, l, acc);
+        if (any) shared_tile<D>(tile_buf(j), tstart, lo, hi, qf, p.scale_log2, m, lsum, acc);
       };
       load_tile(0, sr0);
       if (ntiles > 1) load_tile(1, sr1);
@@ -390,9 +394,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_prefill_shared(PaParams p) {
     // this branch's gated, normalised output goes straight to (or onto) the outputs
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      float lt = l[u];
-      lt += shfl_xor_f(lt, 16);
-      lt += shfl_xor_f(lt, 32);
+      const float lt = lsum[u][0];                 // every row of the ones tile holds the sum
       if (live[u] && n < G) {
         const size_t row = (size_t)tok[u] * p.hkv * G + (size_t)head * G + n;
         // (cmp, slc, win); without gates the selected branch alone, weight 1
