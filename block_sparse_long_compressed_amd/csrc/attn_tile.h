@@ -108,7 +108,9 @@ __device__ __forceinline__ void tile_stage_v(const TileRegs<E, D>& r, typename E
 }
 
 // Online softmax of the tile's scores (log2 domain; lane owns head n) and
-// O^T += V^T P^T from the staged V.
+// O^T += V^T P^T from the staged V.  l_run is the head's whole running sum in
+// every lane of its column (bf16: from the same rounded P as the numerator, as one
+// more MFMA output tile with an all-ones A operand).
 template <typename E, int D>
 __device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, float scale_log2,
                                                 const typename E::storage* lds, float& m_run, float& l_run,
@@ -141,17 +143,12 @@ __device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, f
   mt = fmaxf(mt, shfl_xor_f(mt, 32));
   const float m_new = fmaxf(m_run, mt * scale_log2);
   const float corr = fast_exp2(m_run - m_new);     // 0 when m_run = -inf
-  float psum = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pv = fast_exp2(fmaf(acc_s[t][i], scale_log2, -m_new));
-      acc_s[t][i] = pv;
-      psum += pv;
-    }
+    for (int i = 0; i < 4; ++i) acc_s[t][i] = fast_exp2(fmaf(acc_s[t][i], scale_log2, -m_new));
   }
-  l_run = l_run * corr + psum;
+  l_run *= corr;
   m_run = m_new;
 #pragma unroll
   for (int dt = 0; dt < T::kDt; ++dt) acc_o[dt] *= corr;
@@ -160,6 +157,8 @@ __device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, f
   __builtin_amdgcn_wave_barrier();
 
   if constexpr (E::kBytes == 2) {
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    f32x4 lt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 pb;
@@ -186,8 +185,18 @@ __device__ __forceinline__ void tile_softmax_pv(f32x4 (&acc_s)[4], int nvalid, f
         }
         acc_o[dt] = mfma_bf16_16x16x32(va, pb, acc_o[dt]);
       }
+      lt = mfma_bf16_16x16x32(ones, pb, lt);
     }
+    l_run += lt[0];
   } else {
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) psum += acc_s[t][i];
+    psum += shfl_xor_f(psum, 16);
+    psum += shfl_xor_f(psum, 32);
+    l_run += psum;
     const float* vl = reinterpret_cast<const float*>(lds);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {

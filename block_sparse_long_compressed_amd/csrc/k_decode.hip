@@ -435,8 +435,6 @@ __device__ void attn_role(const DecodeParams& p, int unit, int branch, int local
     if (nv_next > 0) tile_load_v<E, D>(Vn, nv_next, tr);
     nv = nv_next;
   }
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
 
   // ---- merge the waves of this workgroup in LDS ----------------------------
   __syncthreads();

@@ -704,8 +704,6 @@ __global__ __launch_bounds__(256) void k_attn_unit(AuParams p) {
     if (nvalid <= 0) continue;
     attend_tile<E, D>(Kt, Vt, nvalid, qf, p.scale_log2, lds, m_run, l_run, acc_o);
   }
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
 
   __syncthreads();
   float* mo = reinterpret_cast<float*>(smem);        // [4][16][D]
