@@ -190,7 +190,8 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
   a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len);
   a.head_dim = p->head_dim; a.rank = p->rank; a.bf16 = p->kv_dtype == COBS_BF16;
   const int units = batch * p->n_kv_heads;
-  a.blocks_per_wave = std::min(8, std::max(2, cdiv(units * a.nb_max, 4 * 256 * 4)));
+  // one block per wave (two for a few thousand blocks, which all fit in the resident waves at once)
+  a.blocks_per_wave = units * a.nb_max <= 4096 ? 2 : 1;
   a.seq_lens = seq_lens; a.K = K; a.V = pool ? V : K;
   a.mu = mu;
   a.var = p->so_kind == COBS_SO_DIAG ? static_cast<float*>(so) : nullptr;

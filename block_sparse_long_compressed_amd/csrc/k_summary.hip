@@ -7,8 +7,10 @@
 // (Janus issue #181, compression path) attends over mean-pooled tokens: the mean
 // of 32 consecutive keys (values) every 16 positions.
 //
-// One wavefront streams a run of consecutive blocks of one (sequence, kv-head):
-// every 16-byte load instruction reads 1 KiB of contiguous rows, the block stays
+// One wavefront streams a short run of consecutive blocks of one (sequence,
+// kv-head) and one tensor (keys: mean, variance, pooled keys; values: pooled
+// values), so a block's rows take 64 registers and three waves share a SIMD.
+// Every 16-byte load instruction reads 1 KiB of contiguous rows, the block stays
 // in registers for the two-pass variance, and row sums are reduced with lane
 // shuffles.  Pooled token j = (chunk_j + chunk_{j+1}) / 32 where chunk_c is the
 // sum of rows [16c, 16c+16); the chunk after the run (the halo) is read once.
@@ -70,8 +72,24 @@ __device__ __forceinline__ void store_mean(void* mu_u, bool mu_bf16, int b, int 
   }
 }
 
+// Lane partial sums of chunk q = rows [16q, 16q+16) of a block held as loaded.
 template <typename E, int D>
-__global__ __launch_bounds__(64) void k_build_diag(
+__device__ __forceinline__ void chunk_partials(const u32x4 (&x)[RowTiling<E, D>::kLoads], float (&part)[4][E::kPer16]) {
+  using T = RowTiling<E, D>;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int e = 0; e < T::kEpl; ++e) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = q * 16 / T::kRowsPerLoad; i < (q + 1) * 16 / T::kRowsPerLoad; ++i) a += E::get(x[i], e);
+      part[q][e] = a;
+    }
+  }
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(64, 2) void k_build_diag(
     const int32_t* __restrict__ seq_lens, int max_len, int nb_max, int nc_max,
     const typename E::storage* __restrict__ K, const typename E::storage* __restrict__ V,
     void* __restrict__ mu, float* __restrict__ var,
@@ -84,109 +102,99 @@ __global__ __launch_bounds__(64) void k_build_diag(
   const int rg = lane / LPR;          // row group: rows rg, rg+RPL, ...
   const int hkv = gridDim.y;
   const int head = blockIdx.y, seq = blockIdx.z;
+  // With pooled tokens, even workgroups take the keys (mean, variance, pooled keys)
+  // and odd ones the values (pooled values) of the same run of blocks.
+  const bool is_v = want_pool && (blockIdx.x & 1);
+  const int run = want_pool ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
   const int L = seq_lens[seq];
   const int nb = (L + kBlock - 1) / kBlock;
-  const int b_begin = blockIdx.x * blocks_per_wave;
+  const int b_begin = run * blocks_per_wave;
   const int b_end = min(b_begin + blocks_per_wave, nb);
   if (b_begin >= b_end) return;
   const int nc = (want_pool && L >= 32) ? (L - 32) / 16 + 1 : 0;
 
   const size_t unit = (size_t)seq * hkv + head;
-  const typename E::storage* Ku = K + unit * (size_t)max_len * D;
-  const typename E::storage* Vu = V + unit * (size_t)max_len * D;
+  const typename E::storage* X = (is_v ? V : K) + unit * (size_t)max_len * D;
   void* mu_u = mu_bf16 ? (void*)(static_cast<uint16_t*>(mu) + unit * (size_t)nb_max * D)
                        : (void*)(static_cast<float*>(mu) + unit * (size_t)nb_max * D);
   float* var_u = var ? var + unit * (size_t)nb_max * D : nullptr;
-  typename E::storage* kc_u = want_pool ? kc + unit * (size_t)nc_max * D : nullptr;
-  typename E::storage* vc_u = want_pool ? vc + unit * (size_t)nc_max * D : nullptr;
+  typename E::storage* xc_u = want_pool ? (is_v ? vc : kc) + unit * (size_t)nc_max * D : nullptr;
 
-  float carry_k[EPL], carry_v[EPL];   // chunk 3 of the previous block
+  auto load_block = [&](int b, u32x4 (&x)[NL]) {
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) carry_k[e] = carry_v[e] = 0.f;
+    for (int i = 0; i < NL; ++i) {
+      const int r = min(b * kBlock + i * RPL + rg, L - 1);
+      x[i] = ld16(X + (size_t)r * D + cc * EPL);
+    }
+  };
+
+  float carry[EPL];                   // chunk 3 of the previous block
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) carry[e] = 0.f;
 
   for (int b = b_begin; b < b_end; ++b) {
-    const int row0 = b * kBlock;
-    const int nrows = min(kBlock, L - row0);
-    u32x4 xk[NL], xv[NL];
+    u32x4 x[NL];
+    load_block(b, x);
+    const int nrows = min(kBlock, L - b * kBlock);
+    if (nrows < kBlock) {             // the last block of a sequence: rows past its end count as zero
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int r = min(row0 + i * RPL + rg, L - 1);
-      xk[i] = ld16(Ku + (size_t)r * D + cc * EPL);
-      if (want_pool) xv[i] = ld16(Vu + (size_t)r * D + cc * EPL);
+      for (int i = 0; i < NL; ++i)
+        if (i * RPL + rg >= nrows) x[i] = u32x4{0u, 0u, 0u, 0u};
     }
-    float sum[EPL];
+    float part[4][EPL];
+    chunk_partials<E, D>(x, part);
+    if (!is_v) {
+      float mean[EPL];
+      const float inv_n = 1.0f / (float)nrows;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) sum[e] = 0.f;
+      for (int e = 0; e < EPL; ++e)
+        mean[e] = reduce_rows<LPR>((part[0][e] + part[1][e]) + (part[2][e] + part[3][e])) * inv_n;
+      if (rg == 0) store_mean<EPL>(mu_u, mu_bf16 != 0, b, D, cc * EPL, mean);
+      if (want_var) {
+        // unpack the raw rows again (keeping all 64 rows unpacked since the sums
+        // would double the registers this wave holds)
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
+        for (int i = 0; i < NL; ++i) asm volatile("" : "+v"(x[i]));
+        float sq[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sum[e] += ok * E::get(xk[i], e);
-    }
-    float mean[EPL];
-    const float inv_n = 1.0f / (float)nrows;
+        for (int e = 0; e < EPL; ++e) sq[e] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) mean[e] = reduce_rows<LPR>(sum[e]) * inv_n;
-    if (rg == 0) store_mean<EPL>(mu_u, mu_bf16 != 0, b, D, cc * EPL, mean);
-    if (want_var) {
-      float sq[EPL];
+        for (int i = 0; i < NL; ++i) {
+          const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sq[e] = 0.f;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float dlt = E::get(xk[i], e) - mean[e];
-          sq[e] += ok * dlt * dlt;
+          for (int e = 0; e < EPL; ++e) {
+            const float dlt = (E::get(x[i], e) - mean[e]) * ok;
+            sq[e] = fmaf(dlt, dlt, sq[e]);
+          }
         }
-      }
-      float v[EPL];
+        float v[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) v[e] = reduce_rows<LPR>(sq[e]) * inv_n;
-      if (rg == 1 % RPL) {
-        float* dst = var_u + (size_t)b * D + cc * EPL;
+        for (int e = 0; e < EPL; ++e) v[e] = reduce_rows<LPR>(sq[e]) * inv_n;
+        if (rg == 1 % RPL) {
+          float* dst = var_u + (size_t)b * D + cc * EPL;
 #pragma unroll
-        for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]});
+          for (int e = 0; e < EPL; e += 4) st_f32x4(dst + e, f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]});
+        }
       }
     }
     if (want_pool) {
-      // chunk sums (rows [16q, 16q+16) of this block), masked to valid rows
-      float ck[4][EPL], cv[4][EPL];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          float a = 0.f, c = 0.f;
-#pragma unroll
-          for (int i = q * 16 / RPL; i < (q + 1) * 16 / RPL; ++i) {
-            const float ok = (i * RPL + rg < nrows) ? 1.f : 0.f;
-            a += ok * E::get(xk[i], e);
-            c += ok * E::get(xv[i], e);
-          }
-          ck[q][e] = reduce_rows<LPR>(a);
-          cv[q][e] = reduce_rows<LPR>(c);
-        }
-      }
       // pooled token c = 4b + q - 1 spans chunk (4b+q-1) and chunk (4b+q)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        float ch[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ch[e] = reduce_rows<LPR>(part[q][e]);
         const int c = 4 * b + q - 1;
-        if (c < 0 || c >= nc) continue;
-        if (q == 0 && b == b_begin) continue;   // emitted by the wave that owns block b-1
-        float tk[EPL], tv[EPL];
+        // token 4b - 1 is emitted by the wave that owns block b - 1
+        if (c >= 0 && c < nc && !(q == 0 && b == b_begin)) {
+          float t[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float pk = (q == 0) ? carry_k[e] : ck[q - 1][e];
-          const float pv = (q == 0) ? carry_v[e] : cv[q - 1][e];
-          tk[e] = (pk + ck[q][e]) * (1.0f / 32.0f);
-          tv[e] = (pv + cv[q][e]) * (1.0f / 32.0f);
+          for (int e = 0; e < EPL; ++e) t[e] = (carry[e] + ch[e]) * (1.0f / 32.0f);
+          if (rg == q % RPL) store_pooled<E, D>(xc_u + (size_t)c * D + cc * EPL, t);
         }
-        if (rg == 2 % RPL) store_pooled<E, D>(kc_u + (size_t)c * D + cc * EPL, tk);
-        if (rg == 3 % RPL) store_pooled<E, D>(vc_u + (size_t)c * D + cc * EPL, tv);
-      }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) { carry_k[e] = ck[3][e]; carry_v[e] = cv[3][e]; }
+        for (int e = 0; e < EPL; ++e) carry[e] = ch[e];
+      }
     }
   }
   // halo: pooled token 4*b_end - 1 needs chunk 0 of block b_end
@@ -194,25 +202,19 @@ __global__ __launch_bounds__(64) void k_build_diag(
     const int c = 4 * b_end - 1;
     if (c < nc) {   // then rows [64*b_end, 64*b_end + 16) are all < L
       const int row0 = b_end * kBlock;
-      float a[EPL], v[EPL];
+      float a[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) a[e] = v[e] = 0.f;
+      for (int e = 0; e < EPL; ++e) a[e] = 0.f;
 #pragma unroll
       for (int i = 0; i < 16 / RPL; ++i) {
-        const int r = row0 + i * RPL + rg;
-        const u32x4 xk = ld16(Ku + (size_t)r * D + cc * EPL);
-        const u32x4 xv = ld16(Vu + (size_t)r * D + cc * EPL);
+        const u32x4 xh = ld16(X + (size_t)(row0 + i * RPL + rg) * D + cc * EPL);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) { a[e] += E::get(xk, e); v[e] += E::get(xv, e); }
+        for (int e = 0; e < EPL; ++e) a[e] += E::get(xh, e);
       }
-      float tk[EPL], tv[EPL];
+      float t[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        tk[e] = (carry_k[e] + reduce_rows<LPR>(a[e])) * (1.0f / 32.0f);
-        tv[e] = (carry_v[e] + reduce_rows<LPR>(v[e])) * (1.0f / 32.0f);
-      }
-      if (rg == 2 % RPL) store_pooled<E, D>(kc_u + (size_t)c * D + cc * EPL, tk);
-      if (rg == 3 % RPL) store_pooled<E, D>(vc_u + (size_t)c * D + cc * EPL, tv);
+      for (int e = 0; e < EPL; ++e) t[e] = (carry[e] + reduce_rows<LPR>(a[e])) * (1.0f / 32.0f);
+      if (rg == 0) store_pooled<E, D>(xc_u + (size_t)c * D + cc * EPL, t);
     }
   }
 }
@@ -321,7 +323,8 @@ __global__ __launch_bounds__(64) void k_append_diag(
 template <typename E, int D>
 static hipError_t launch_diag(const BuildArgs& a) {
   const int bpw = a.blocks_per_wave;
-  dim3 grid((a.nb_max + bpw - 1) / bpw, a.hkv, a.batch);
+  const int runs = (a.nb_max + bpw - 1) / bpw;
+  dim3 grid(a.kc != nullptr ? 2 * runs : runs, a.hkv, a.batch);
   hipLaunchKernelGGL((k_build_diag<E, D>), grid, dim3(64), 0, a.stream,
                      a.seq_lens, a.max_len, a.nb_max, a.nc_max,
                      (const typename E::storage*)a.K, (const typename E::storage*)a.V,
