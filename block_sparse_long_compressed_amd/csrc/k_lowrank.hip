@@ -9,11 +9,14 @@
 // A block holds n <= 64 keys of dimension d = 64 or 128 > n, so the work is
 // done on the n x n Gram matrix G = X X^T / n of the centred keys X (same
 // non-zero eigenvalues as C_b): if G w = lambda w with |w| = 1, then
-// X^T w / sqrt(n) = sqrt(lambda) u.  G is diagonalised by a parallel cyclic
-// Jacobi method in fp64 (32 disjoint rotations per round, round-robin pairing,
-// rotations accumulated in V), which agrees with a reference fp64 symmetric
-// eigensolver to rounding.  One 256-thread workgroup per block; G and V live in
-// LDS (2 x 32 KiB).  Eigenvalues <= 0 give v = 0; each v is signed so that its
+// X^T w / sqrt(n) = sqrt(lambda) u.  One 256-thread workgroup per block, G in
+// LDS, in fp64: G is reduced to a tridiagonal T = Q^T G Q by 62 Householder
+// reflections; the r largest eigenvalues of T come from bisection on Sturm counts
+// (one half-wave per eigenvalue, 32 shifts per step); each eigenvector of T from
+// the twisted factorisation T - lambda I = L+ D+ L+^T = U- D- U-^T (one solve, no
+// iteration), made orthogonal to the earlier ones; then w = Q z.  This agrees
+// with a reference fp64 symmetric eigensolver to rounding wherever the eigenvalue
+// is not repeated.  Eigenvalues <= 0 give v = 0; each v is signed so that its
 // largest-magnitude entry is positive.
 //
 // Query-subspace projection (Technisches Resuemee 2.3, "Subraum-Projektion"):
@@ -30,11 +33,74 @@ namespace cobs {
 
 constexpr int kLrThreads = 256;
 constexpr int kN = 64;              // Gram size (keys per block)
-constexpr int kMaxSweeps = 16;
+constexpr double kEps = 0x1p-52;          // fp64 unit roundoff (2^-53) times 2
+constexpr double kSafeMin = 0x1p-1021;    // safe minimum (1 / it does not overflow)
 
-// Round-robin pairing: round r (0..62), pair k (0..31) -> (p, q), p != q; every
-// unordered pair of 0..63 occurs exactly once in 63 rounds.
-__device__ __forceinline__ int rr_index(int pos, int r) { return pos == 0 ? 0 : 1 + (pos - 1 + r) % (kN - 1); }
+// A double moved between lanes by a DPP pattern (two 32-bit moves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Reductions over the 16 lanes of a row with DPP: lane pairs i^1, i^2 within a
+// quad, then the mirrored quads and half-rows, so every lane adds the same two
+// partial results (a + b and b + a) and ends with the same bits.
+template <typename Op>
+__device__ __forceinline__ double row_reduce(double v, Op op) {
+  v = op(v, dpp_f64<0xB1>(v));      // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_f64<0x4E>(v));      // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_f64<0x141>(v));     // row_half_mirror
+  v = op(v, dpp_f64<0x140>(v));     // row_mirror
+  return v;
+}
+struct AddOp { __device__ double operator()(double a, double b) const { return a + b; } };
+struct MaxOp { __device__ double operator()(double a, double b) const { return fmax(a, b); } };
+struct MinOp { __device__ double operator()(double a, double b) const { return fmin(a, b); } };
+
+// Sum, maximum and minimum over the 32 lanes of a half-wave, and the sum over the wave.
+__device__ __forceinline__ double half_sum(double v) {
+  v = row_reduce(v, AddOp{});
+  return v + __shfl_xor(v, 16, 64);
+}
+__device__ __forceinline__ double half_max(double v) {
+  v = row_reduce(v, MaxOp{});
+  return fmax(v, __shfl_xor(v, 16, 64));
+}
+__device__ __forceinline__ double half_min(double v) {
+  v = row_reduce(v, MinOp{});
+  return fmin(v, __shfl_xor(v, 16, 64));
+}
+// The value of lane i (i the same in every lane).
+__device__ __forceinline__ double readlane_f64(double v, int i) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, i);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), i);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum(double v) {
+  v = half_sum(v);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+// Number of eigenvalues below sig of the symmetric tridiagonal matrix with
+// diagonal d and squared off-diagonal e2 (Sturm sequence of the LDL^T pivots of
+// T - sig I; a pivot smaller in magnitude than pivmin is replaced by -pivmin).
+__device__ __forceinline__ int sturm_count(const double* d, const double* e2, double sig, double pivmin) {
+  double q = d[0] - sig;
+  if (fabs(q) < pivmin) q = -pivmin;
+  int c = q < 0.0 ? 1 : 0;
+  for (int i = 1; i < kN; ++i) {
+    double r = __builtin_amdgcn_rcp(q);           // 1 / q: hardware estimate and one Newton step
+    r = fma(r, fma(-q, r, 1.0), r);
+    q = (d[i] - sig) - e2[i - 1] * r;
+    if (fabs(q) < pivmin) q = -pivmin;
+    c += q < 0.0 ? 1 : 0;
+  }
+  return c;
+}
 
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -120,16 +186,19 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
                                                               void* __restrict__ lowrank, int fp4,
                                                               const float* __restrict__ Psub, int sub_s,
                                                               int vlen) {
-  __shared__ double A[kN][kN + 1];      // Gram matrix, diagonalised in place (+1: bank spread)
-  // the block's keys (fp32, exact for bf16) until G is built, then the rotations
+  __shared__ double A[kN][kN + 1];      // Gram matrix, reduced in place (+1: bank spread)
+  // the block's keys (fp32, exact for bf16) until G is built, then the Householder vectors
   __shared__ union { float k[kN][D + 1]; double v[kN][kN + 1]; } kv;
   __shared__ double mu[D];
-  __shared__ double cs[kN / 2][2];
-  __shared__ int pq[kN / 2][2];
   __shared__ double red[4];
-  __shared__ int order[8];
+  __shared__ int hh_skip[2];
   __shared__ double lam_sel[8];
-  __shared__ double vout[8][D];
+  // the output vectors, and before them the eigensolver's vectors (8 * D >= 512 doubles)
+  __shared__ union {
+    double vout[8][D];
+    struct { double u[kN], part[4][kN], d[kN], e[kN], e2[kN]; } ev;
+  } ov;
+  auto& vout = ov.vout;
   __shared__ int gexp[8][D / 32];
   __shared__ __align__(16) uint8_t rec[8 * (D / 2 + D / 32) + 16];
   auto& Vm = kv.v;
@@ -219,90 +288,178 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
       for (int j = 0; j < 4; ++j) A[4 * ta + i][4 * tb + j] = acc[i][j] * inv_n;
   }
   __syncthreads();
-  for (int idx = tid; idx < kN * kN; idx += kLrThreads) Vm[idx / kN][idx % kN] = (idx / kN == idx % kN) ? 1.0 : 0.0;
-  __syncthreads();
-
-  // cyclic Jacobi sweeps
+  // ---- top-r eigenpairs of G ------------------------------------------------
+  // (1) Householder tridiagonalisation G = Q T Q^T, Q = H_0 ... H_61, H_k = I - u_k u_k^T
+  //     (|u_k|^2 = 2, zero in entries 0..k); u_k is kept in row k of Vm.
   double fro2 = 0.0;
   for (int idx = tid; idx < kN * kN; idx += kLrThreads) fro2 += A[idx / kN][idx % kN] * A[idx / kN][idx % kN];
   fro2 = block_sum_f64(fro2, red);
-  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    double off2 = 0.0;
-    for (int idx = tid; idx < kN * kN; idx += kLrThreads) {
-      const int i = idx / kN, j = idx % kN;
-      if (i != j) off2 += A[i][j] * A[i][j];
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int k = 0; k < kN - 2; ++k) {
+    if (wv == 0) {                                  // reflector of column k below the diagonal
+      const double xi = (lane > k) ? A[lane][k] : 0.0;
+      const double sigma = wave_sum(xi * xi);
+      const double x0 = A[k + 1][k];
+      double ui = 0.0;
+      const bool refl = sigma > 1e-40 * fro2;       // else the column is negligible: H_k = I
+      if (refl) {
+        const double alpha = -copysign(sqrt(sigma), x0);
+        const double sc = sqrt(1.0 / (sigma - alpha * x0));
+        ui = (lane > k) ? (xi - (lane == k + 1 ? alpha : 0.0)) * sc : 0.0;
+      }
+      Vm[k][lane] = ui;
+      ov.ev.u[lane] = ui;
+      if (lane == 0) hh_skip[k & 1] = refl ? 0 : 1;
     }
-    off2 = block_sum_f64(off2, red);
-    if (!(off2 > 1e-30 * fro2)) break;            // converged (also stops on an all-zero block)
-    for (int r = 0; r < kN - 1; ++r) {
-      if (tid < kN / 2) {
-        const int p = rr_index(tid, r), q = rr_index(kN - 1 - tid, r);
-        const double app = A[p][p], aqq = A[q][q], apq = A[p][q];
-        double c = 1.0, s = 0.0;
-        if (apq != 0.0 && fabs(apq) > 1e-300) {
-          const double theta = (aqq - app) / (2.0 * apq);
-          double t;
-          if (fabs(theta) > 1e150) t = 0.5 / theta;
-          else t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-          c = 1.0 / sqrt(t * t + 1.0);
-          s = t * c;
-        }
-        cs[tid][0] = c; cs[tid][1] = s;
-        pq[tid][0] = p; pq[tid][1] = q;
+    __syncthreads();
+    if (hh_skip[k & 1]) continue;
+    // p = G u: wave w sums rows 16w..16w+15 (G is symmetric, so its columns are read)
+    {
+      double sp = 0.0;
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) sp += A[16 * wv + ii][lane] * ov.ev.u[16 * wv + ii];
+      ov.ev.part[wv][lane] = sp;
+    }
+    __syncthreads();
+    // w = p - (u^T p / 2) u;  G <- G - u w^T - w u^T  (wave w: rows 16w..16w+15)
+    {
+      const double uj = ov.ev.u[lane];
+      const double pj = (ov.ev.part[0][lane] + ov.ev.part[1][lane]) + (ov.ev.part[2][lane] + ov.ev.part[3][lane]);
+      const double K = 0.5 * wave_sum(uj * pj);
+      const double wj = pj - K * uj;
+      const int row0 = __builtin_amdgcn_readfirstlane(16 * wv);
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int i = row0 + ii;
+        const double ui = readlane_f64(uj, i), wi = readlane_f64(wj, i);
+        A[i][lane] -= ui * wj + wi * uj;
       }
-      __syncthreads();
-      // rows: A <- J^T A
-      for (int idx = tid; idx < (kN / 2) * kN; idx += kLrThreads) {
-        const int k = idx / kN, j = idx % kN;
-        const int p = pq[k][0], q = pq[k][1];
-        const double c = cs[k][0], s = cs[k][1];
-        const double ap = A[p][j], aq = A[q][j];
-        A[p][j] = c * ap - s * aq;
-        A[q][j] = s * ap + c * aq;
+    }
+    __syncthreads();
+  }
+  if (tid < kN) {
+    const double ee = (tid < kN - 1) ? A[tid + 1][tid] : 0.0;
+    ov.ev.d[tid] = A[tid][tid];
+    ov.ev.e[tid] = ee;
+    ov.ev.e2[tid] = ee * ee;
+  }
+  __syncthreads();
+  // (2) the j-th largest eigenvalue of T by bisection, one half-wave per eigenvalue:
+  //     32 Sturm counts per step narrow the bracket 33-fold
+  double* const Af = &A[0][0];                      // G is no longer needed: scratch
+  double* const Wv = Af + 24 * kN;                  // eigenvectors, [j][kN]
+  const int jv = tid >> 5, g = tid & 31;
+  if (jv < rank) {
+    const double* d = ov.ev.d;
+    const double* e = ov.ev.e;
+    const double* e2 = ov.ev.e2;
+    double lo = INFINITY, hi = -INFINITY, emax2 = 0.0;
+    for (int i = 0; i < kN; ++i) {
+      const double r = fabs(e[i]) + (i > 0 ? fabs(e[i - 1]) : 0.0);
+      lo = fmin(lo, d[i] - r);
+      hi = fmax(hi, d[i] + r);
+      emax2 = fmax(emax2, e2[i]);
+    }
+    const double pivmin = kSafeMin * fmax(1.0, emax2);
+    const double tnorm = fmax(fabs(lo), fabs(hi));
+    lo -= 2.0 * kEps * tnorm + 2.0 * pivmin;
+    hi += 2.0 * kEps * tnorm + 2.0 * pivmin;
+    const int target = kN - 1 - jv;                 // its index in ascending order
+    for (int it = 0; it < 64; ++it) {
+      if (hi - lo <= 2.0 * kEps * fmax(fabs(lo), fabs(hi)) + kEps * tnorm + pivmin) break;
+      const double sig = lo + (hi - lo) * ((double)(g + 1) / 33.0);
+      const int c = sturm_count(d, e2, sig, pivmin);
+      const double nlo = half_max(c <= target ? sig : -INFINITY);
+      const double nhi = half_min(c > target ? sig : INFINITY);
+      if (nlo > -INFINITY) lo = nlo;
+      if (nhi < INFINITY) hi = nhi;
+    }
+    // (3) its eigenvector of T from the twisted factorisation of T - lam I:
+    //     T - lam I = L+ D+ L+^T = U- D- U-^T; at the twist k where
+    //     |gamma_k| = |D+_k + D-_k - (d_k - lam)| is smallest, z_k = 1 and
+    //     z_i = -L+_i z_i+1 above, z_i+1 = -U-_i z_i below
+    if (g == 0) {
+      const double lam = 0.5 * (lo + hi);
+      lam_sel[jv] = lam;
+      const double tiny = kSafeMin * 0x1p14;
+      double* Lp = Af + jv * 3 * kN;
+      double* Um = Lp + kN;
+      double* Dp = Um + kN;
+      double dp = d[0] - lam;
+      for (int i = 0; i < kN - 1; ++i) {
+        if (fabs(dp) < tiny) dp = -tiny;
+        Dp[i] = dp;
+        Lp[i] = e[i] / dp;
+        dp = (d[i + 1] - lam) - Lp[i] * e[i];
       }
-      __syncthreads();
-      // columns: A <- A J, V <- V J
-      for (int idx = tid; idx < (kN / 2) * kN; idx += kLrThreads) {
-        const int k = idx / kN, i = idx % kN;
-        const int p = pq[k][0], q = pq[k][1];
-        const double c = cs[k][0], s = cs[k][1];
-        const double ap = A[i][p], aq = A[i][q];
-        A[i][p] = c * ap - s * aq;
-        A[i][q] = s * ap + c * aq;
-        const double vp = Vm[i][p], vq = Vm[i][q];
-        Vm[i][p] = c * vp - s * vq;
-        Vm[i][q] = s * vp + c * vq;
+      Dp[kN - 1] = dp;
+      double dm = d[kN - 1] - lam;
+      double best = fabs(Dp[kN - 1] + dm - (d[kN - 1] - lam));
+      int kt = kN - 1;
+      for (int i = kN - 2; i >= 0; --i) {
+        if (fabs(dm) < tiny) dm = -tiny;
+        Um[i] = e[i] / dm;
+        dm = (d[i] - lam) - Um[i] * e[i];
+        const double gam = fabs(Dp[i] + dm - (d[i] - lam));
+        if (gam < best) { best = gam; kt = i; }
       }
-      __syncthreads();
+      double* z = Wv + jv * kN;
+      z[kt] = 1.0;
+      double zc = 1.0;
+      for (int i = kt - 1; i >= 0; --i) { zc = -Lp[i] * zc; z[i] = zc; }
+      zc = 1.0;
+      for (int i = kt; i < kN - 1; ++i) { zc = -Um[i] * zc; z[i + 1] = zc; }
     }
   }
-
-  // top-r eigenvalues (ties to the lower index), by one wave
-  if (tid < 64) {
-    double lam = A[tid][tid];
-    bool taken = false;
-    for (int i = 0; i < rank; ++i) {
-      double best = taken ? -INFINITY : lam;
-      int bi = tid;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const double ob = __shfl_xor(best, m, 64);
-        const int oi = __shfl_xor(bi, m, 64);
-        if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+  __syncthreads();
+  // (4) normalise, orthogonal to the earlier vectors (a repeated eigenvalue gives the
+  //     same twisted vector again: then the first unit vector not yet spanned)
+  if (wv == 0) {
+    for (int jj = 0; jj < rank; ++jj) {
+      double z = Wv[jj * kN + lane];
+      double nz = 0.0;
+      for (int attempt = -1; attempt < kN; ++attempt) {
+        if (attempt >= 0) z = (lane == attempt) ? 1.0 : 0.0;
+        nz = sqrt(wave_sum(z * z));
+        if (!(nz > 0.0)) continue;
+        z /= nz;
+        for (int pv = 0; pv < jj; ++pv) {
+          const double v = Wv[pv * kN + lane];
+          z -= wave_sum(v * z) * v;
+        }
+        nz = sqrt(wave_sum(z * z));
+        if (nz > 0.5) break;
       }
-      if (tid == bi) taken = true;
-      if (tid == 0) { order[i] = bi; lam_sel[i] = best; }
+      Wv[jj * kN + lane] = z / nz;
     }
+  }
+  __syncthreads();
+  // (5) back to G's basis: w = H_0 ... H_61 z, one half-wave per vector
+  if (jv < rank) {
+    double z0 = Wv[jv * kN + g], z1 = Wv[jv * kN + g + 32];
+    for (int k = kN - 3; k >= 0; --k) {
+      const double u0 = Vm[k][g], u1 = Vm[k][g + 32];
+      const double dot = half_sum(u0 * z0 + u1 * z1);
+      z0 -= dot * u0;
+      z1 -= dot * u1;
+    }
+    Wv[jv * kN + g] = z0;
+    Wv[jv * kN + g + 32] = z1;
+  }
+  __syncthreads();
+  // the keys again (the Householder vectors took their space)
+  for (int idx = tid; idx < kN * D; idx += kLrThreads) {
+    const int r = idx / D, c = idx % D;
+    kv.k[r][c] = (r < n) ? (float)kval(r, c) : 0.f;
   }
   __syncthreads();
   // v_i = X^T w_i / sqrt(n)
   const double inv_sqrt_n = 1.0 / sqrt((double)n);
   for (int idx = tid; idx < rank * D; idx += kLrThreads) {
     const int i = idx / D, c = idx % D;
-    const int j = order[i];
     double s = 0.0;
     if (lam_sel[i] > 0.0) {
-      for (int r = 0; r < n; ++r) s += (kval(r, c) - mu[c]) * Vm[r][j];
+      for (int r = 0; r < n; ++r) s += ((double)kv.k[r][c] - mu[c]) * Wv[i * kN + r];
       s *= inv_sqrt_n;
     }
     vout[i][c] = s;
