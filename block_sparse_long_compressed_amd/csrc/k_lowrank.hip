@@ -191,12 +191,11 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
   __shared__ union { float k[kN][D + 1]; double v[kN][kN + 1]; } kv;
   __shared__ double mu[D];
   __shared__ double red[4];
-  __shared__ int hh_skip[2];
   __shared__ double lam_sel[8];
   // the output vectors, and before them the eigensolver's vectors (8 * D >= 512 doubles)
   __shared__ union {
     double vout[8][D];
-    struct { double u[kN], part[4][kN], d[kN], e[kN], e2[kN]; } ev;
+    struct { double part[4][kN], d[kN], e[kN], e2[kN]; } ev;
   } ov;
   auto& vout = ov.vout;
   __shared__ int gexp[8][D / 32];
@@ -296,38 +295,33 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
   fro2 = block_sum_f64(fro2, red);
   const int lane = tid & 63, wv = tid >> 6;
   for (int k = 0; k < kN - 2; ++k) {
-    if (wv == 0) {                                  // reflector of column k below the diagonal
-      const double xi = (lane > k) ? A[lane][k] : 0.0;
-      const double sigma = wave_sum(xi * xi);
-      const double x0 = A[k + 1][k];
-      double ui = 0.0;
-      const bool refl = sigma > 1e-40 * fro2;       // else the column is negligible: H_k = I
-      if (refl) {
-        const double alpha = -copysign(sqrt(sigma), x0);
-        const double sc = sqrt(1.0 / (sigma - alpha * x0));
-        ui = (lane > k) ? (xi - (lane == k + 1 ? alpha : 0.0)) * sc : 0.0;
-      }
-      Vm[k][lane] = ui;
-      ov.ev.u[lane] = ui;
-      if (lane == 0) hh_skip[k & 1] = refl ? 0 : 1;
+    // the reflector of column k below the diagonal, formed by every wave from the
+    // same LDS values with bit-identical reductions (so all take the same branch)
+    const double xi = (lane > k) ? A[lane][k] : 0.0;
+    const double sigma = wave_sum(xi * xi);
+    if (!(sigma > 1e-40 * fro2)) {                  // the column is negligible: H_k = I
+      if (wv == 0) Vm[k][lane] = 0.0;
+      continue;
     }
-    __syncthreads();
-    if (hh_skip[k & 1]) continue;
+    const double x0 = A[k + 1][k];
+    const double alpha = -copysign(sqrt(sigma), x0);
+    const double sc = sqrt(1.0 / (sigma - alpha * x0));
+    const double uj = (lane > k) ? (xi - (lane == k + 1 ? alpha : 0.0)) * sc : 0.0;
+    if (wv == 0) Vm[k][lane] = uj;
     // p = G u: wave w sums rows 16w..16w+15 (G is symmetric, so its columns are read)
+    const int row0 = __builtin_amdgcn_readfirstlane(16 * wv);
     {
       double sp = 0.0;
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) sp += A[16 * wv + ii][lane] * ov.ev.u[16 * wv + ii];
+      for (int ii = 0; ii < 16; ++ii) sp += A[row0 + ii][lane] * readlane_f64(uj, row0 + ii);
       ov.ev.part[wv][lane] = sp;
     }
     __syncthreads();
     // w = p - (u^T p / 2) u;  G <- G - u w^T - w u^T  (wave w: rows 16w..16w+15)
     {
-      const double uj = ov.ev.u[lane];
       const double pj = (ov.ev.part[0][lane] + ov.ev.part[1][lane]) + (ov.ev.part[2][lane] + ov.ev.part[3][lane]);
       const double K = 0.5 * wave_sum(uj * pj);
       const double wj = pj - K * uj;
-      const int row0 = __builtin_amdgcn_readfirstlane(16 * wv);
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
         const int i = row0 + ii;
