@@ -14,7 +14,8 @@
 // reflections; the r largest eigenvalues of T come from bisection on Sturm counts
 // (one half-wave per eigenvalue, 32 shifts per step); each eigenvector of T from
 // the twisted factorisation T - lambda I = L+ D+ L+^T = U- D- U-^T (one solve, no
-// iteration), made orthogonal to the earlier ones; then w = Q z.  This agrees
+// iteration), made orthogonal to the earlier ones (a repeated eigenvalue takes one
+// inverse-iteration step for each further direction); then w = Q z.  This agrees
 // with a reference fp64 symmetric eigensolver to rounding wherever the eigenvalue
 // is not repeated.  Eigenvalues <= 0 give v = 0; each v is signed so that its
 // largest-magnitude entry is positive.
@@ -79,6 +80,10 @@ __device__ __forceinline__ double readlane_f64(double v, int i) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, i);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), i);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_max(double v) {
+  v = half_max(v);
+  return fmax(v, __shfl_xor(v, 32, 64));
 }
 __device__ __forceinline__ double wave_sum(double v) {
   v = half_sum(v);
@@ -406,16 +411,46 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
     }
   }
   __syncthreads();
-  // (4) normalise, orthogonal to the earlier vectors (a repeated eigenvalue gives the
-  //     same twisted vector again: then the first unit vector not yet spanned)
+  // (4) normalise, orthogonal to the earlier vectors.  A repeated eigenvalue gives
+  //     the same twisted vector again; then one inverse-iteration step from the
+  //     first unit vector (made orthogonal to the earlier vectors) that leaves a
+  //     new direction: (T - lam I) y = b solved with the forward factorisation,
+  //     pivots held at least eps |T| away from zero.
   if (wv == 0) {
+    const double tn = wave_max(fabs(ov.ev.d[lane])) + 2.0 * wave_max(fabs(ov.ev.e[lane]));
+    const double pfloor = kEps * tn;
     for (int jj = 0; jj < rank; ++jj) {
       double z = Wv[jj * kN + lane];
       double nz = 0.0;
       for (int attempt = -1; attempt < kN; ++attempt) {
-        if (attempt >= 0) z = (lane == attempt) ? 1.0 : 0.0;
+        if (attempt >= 0) {
+          double bv = (lane == attempt) ? 1.0 : 0.0;
+          for (int pv = 0; pv < jj; ++pv) {
+            const double v = Wv[pv * kN + lane];
+            bv -= wave_sum(v * bv) * v;
+          }
+          Wv[jj * kN + lane] = bv;
+          __builtin_amdgcn_wave_barrier();
+          if (lane == 0) {
+            const double* Lp = Af + jj * 3 * kN;
+            const double* Dp = Lp + 2 * kN;
+            double* y = Wv + jj * kN;
+            for (int t = 1; t < kN; ++t) y[t] -= Lp[t - 1] * y[t - 1];
+            for (int t = 0; t < kN; ++t) {
+              double dd = Dp[t];
+              if (fabs(dd) < pfloor) dd = dd < 0.0 ? -pfloor : pfloor;
+              y[t] /= dd;
+            }
+            for (int t = kN - 2; t >= 0; --t) y[t] -= Lp[t] * y[t + 1];
+          }
+          __builtin_amdgcn_wave_barrier();
+          z = Wv[jj * kN + lane];
+          const double zm = wave_max(fabs(z));
+          if (!(zm > 0.0 && zm < INFINITY)) continue;
+          z /= zm;
+        }
         nz = sqrt(wave_sum(z * z));
-        if (!(nz > 0.0)) continue;
+        if (!(nz > 0.0 && nz < INFINITY)) continue;
         z /= nz;
         for (int pv = 0; pv < jj; ++pv) {
           const double v = Wv[pv * kN + lane];
@@ -424,7 +459,7 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
         nz = sqrt(wave_sum(z * z));
         if (nz > 0.5) break;
       }
-      Wv[jj * kN + lane] = z / nz;
+      Wv[jj * kN + lane] = (nz > 0.5) ? z / nz : 0.0;
     }
   }
   __syncthreads();

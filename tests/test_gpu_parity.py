@@ -296,6 +296,33 @@ def test_summaries_lowrank(rank):
     check_lowrank(w, x, s)
 
 
+def test_summaries_lowrank_repeated_eigenvalues():
+    """Blocks whose covariance has an exactly repeated eigenvalue (keys on m
+    coordinate axes with equal weight, bf16-exact), a block of identical keys and a
+    block whose covariance has rank 2: the rank-4 projector must match the oracle's
+    wherever it is well defined, and the quadratic form elsewhere."""
+    w = W("lowrank", **dict(LOWRANK, rank=4))
+    x = synth.make_inputs(w, 7, lens=np.array([1500, 700]))
+    K = x["K"]
+
+    def axes_block(m, a, off):
+        blk = np.zeros((64, w.head_dim), dtype=K.dtype)
+        for j in range(64):
+            blk[j, j % m] = a if (j // m) % 2 == 0 else -a
+        return blk + off
+
+    K[0, 0, 64:128] = axes_block(4, 0.75, 0.25)      # four equal eigenvalues, the rest zero
+    K[0, 0, 128:192] = axes_block(2, 1.5, 0.0)       # two equal
+    K[0, 0, 192:256] = axes_block(3, 0.5, -0.5)      # three equal
+    K[0, 0, 256:320] = 0.375                         # identical keys: zero covariance
+    K[0, 1, 320:384] = axes_block(4, 1.0, 0.0)
+    p = U.params_for(w)
+    g = U.to_device(x)
+    s = U.build(p, g)
+    checked, loose = check_lowrank(w, x, s)
+    assert checked > 0 and loose > 0
+
+
 @pytest.mark.parametrize("alpha", [0.0, 1.0, 2.0])
 def test_decode_lowrank_small(alpha):
     w = W("lowrank", **LOWRANK)
