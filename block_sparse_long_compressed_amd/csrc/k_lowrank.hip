@@ -197,10 +197,10 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
   __shared__ double mu[D];
   __shared__ double red[4];
   __shared__ double lam_sel[8];
-  // the output vectors, and before them the eigensolver's vectors (8 * D >= 512 doubles)
+  // the output vectors, and before them the eigensolver's scratch
   __shared__ union {
     double vout[8][D];
-    struct { double part[4][kN], d[kN], e[kN], e2[kN]; } ev;
+    struct { double part[4][kN], col[2][kN], d[kN], e[kN], e2[kN]; } ev;
   } ov;
   auto& vout = ov.vout;
   __shared__ int gexp[8][D / 32];
@@ -299,49 +299,69 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
   for (int idx = tid; idx < kN * kN; idx += kLrThreads) fro2 += A[idx / kN][idx % kN] * A[idx / kN][idx % kN];
   fro2 = block_sum_f64(fro2, red);
   const int lane = tid & 63, wv = tid >> 6;
+  // wave w keeps rows 16w..16w+15 of G in registers (lane = column); the column a
+  // step reduces is row k of the symmetric G, published through LDS by its wave
+  const int grow0 = __builtin_amdgcn_readfirstlane(16 * wv);
+  double arow[16];
+#pragma unroll
+  for (int ii = 0; ii < 16; ++ii) arow[ii] = A[grow0 + ii][lane];
+  auto own_row = [&](int r) {                        // arow[r - grow0] (r in this wave's rows)
+    double v = 0.0;
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) v = (grow0 + ii == r) ? arow[ii] : v;
+    return v;
+  };
+  if (wv == 0) ov.ev.col[0][lane] = arow[0];
+  __syncthreads();
   for (int k = 0; k < kN - 2; ++k) {
+    const double* colk = ov.ev.col[k & 1];
+    double* coln = ov.ev.col[(k + 1) & 1];
+    const bool owner_next = wv == (k + 1) / 16;
     // the reflector of column k below the diagonal, formed by every wave from the
     // same LDS values with bit-identical reductions (so all take the same branch)
-    const double xi = (lane > k) ? A[lane][k] : 0.0;
+    const double xi = (lane > k) ? colk[lane] : 0.0;
     const double sigma = wave_sum(xi * xi);
     if (!(sigma > 1e-40 * fro2)) {                  // the column is negligible: H_k = I
       if (wv == 0) Vm[k][lane] = 0.0;
+      if (owner_next) coln[lane] = own_row(k + 1);
+      __syncthreads();
       continue;
     }
-    const double x0 = A[k + 1][k];
+    const double x0 = colk[k + 1];
     const double alpha = -copysign(sqrt(sigma), x0);
     const double sc = sqrt(1.0 / (sigma - alpha * x0));
     const double uj = (lane > k) ? (xi - (lane == k + 1 ? alpha : 0.0)) * sc : 0.0;
     if (wv == 0) Vm[k][lane] = uj;
-    // p = G u: wave w sums rows 16w..16w+15 (G is symmetric, so its columns are read)
-    const int row0 = __builtin_amdgcn_readfirstlane(16 * wv);
+    // p = G u: wave w sums its rows (G is symmetric, so a row serves as a column)
     {
       double sp = 0.0;
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) sp += A[row0 + ii][lane] * readlane_f64(uj, row0 + ii);
+      for (int ii = 0; ii < 16; ++ii) sp += arow[ii] * readlane_f64(uj, grow0 + ii);
       ov.ev.part[wv][lane] = sp;
     }
     __syncthreads();
-    // w = p - (u^T p / 2) u;  G <- G - u w^T - w u^T  (wave w: rows 16w..16w+15)
+    // w = p - (u^T p / 2) u;  G <- G - u w^T - w u^T on this wave's rows
     {
       const double pj = (ov.ev.part[0][lane] + ov.ev.part[1][lane]) + (ov.ev.part[2][lane] + ov.ev.part[3][lane]);
       const double K = 0.5 * wave_sum(uj * pj);
       const double wj = pj - K * uj;
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
-        const int i = row0 + ii;
-        const double ui = readlane_f64(uj, i), wi = readlane_f64(wj, i);
-        A[i][lane] -= ui * wj + wi * uj;
+        const double ui = readlane_f64(uj, grow0 + ii), wi = readlane_f64(wj, grow0 + ii);
+        arow[ii] -= ui * wj + wi * uj;
       }
     }
+    if (owner_next) coln[lane] = own_row(k + 1);
     __syncthreads();
   }
-  if (tid < kN) {
-    const double ee = (tid < kN - 1) ? A[tid + 1][tid] : 0.0;
-    ov.ev.d[tid] = A[tid][tid];
-    ov.ev.e[tid] = ee;
-    ov.ev.e2[tid] = ee * ee;
+  // T: the diagonal, and the subdiagonal e_i = G[i+1][i] (row i + 1, lane i)
+#pragma unroll
+  for (int ii = 0; ii < 16; ++ii) {
+    const int r = grow0 + ii;
+    if (lane == r) ov.ev.d[r] = arow[ii];
+    if (r >= 1 && lane == r - 1) { ov.ev.e[r - 1] = arow[ii]; ov.ev.e2[r - 1] = arow[ii] * arow[ii]; }
   }
+  if (tid == 0) { ov.ev.e[kN - 1] = 0.0; ov.ev.e2[kN - 1] = 0.0; }
   __syncthreads();
   // (2) the j-th largest eigenvalue of T by bisection, one half-wave per eigenvalue:
   //     32 Sturm counts per step narrow the bracket 33-fold
