@@ -90,14 +90,14 @@ def test_summaries_small(name):
     check_summaries(w, x, U.build(p, g))
 
 
-@pytest.mark.parametrize("d", [128, 64])
-def test_summaries_short_and_ragged(d):
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (128, "f32"), (64, "f32")])
+def test_summaries_short_and_ragged(d, dtype):
     """Sequences of 1, 31, 33, 64, 65 and 80 keys: a lone partial block, no pooled
     token, a pooled token whose second chunk is the next block's first, and runs of
     blocks that end past the sequence."""
     lens = [1, 31, 33, 64, 65, 80]
     w = W("short", batch=len(lens), max_len=96, min_len=1, n_q_heads=8, n_kv_heads=2, head_dim=d, top_k=2,
-          window=64, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0, dtype="bf16", needles=0)
+          window=64, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0, dtype=dtype, needles=0)
     x = synth.make_inputs(w, 11, lens=np.array(lens))
     p = U.params_for(w)
     check_summaries(w, x, U.build(p, U.to_device(x)))
