@@ -189,9 +189,6 @@ cobs_status cobs_build_summaries(const cobs_params* p, int32_t batch, int32_t ma
   a.batch = batch; a.hkv = p->n_kv_heads; a.max_len = max_len;
   a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len);
   a.head_dim = p->head_dim; a.rank = p->rank; a.bf16 = p->kv_dtype == COBS_BF16;
-  const int units = batch * p->n_kv_heads;
-  // one block per wave (two for a few thousand blocks, which all fit in the resident waves at once)
-  a.blocks_per_wave = units * a.nb_max <= 4096 ? 2 : 1;
   a.seq_lens = seq_lens; a.K = K; a.V = pool ? V : K;
   a.mu = mu;
   a.var = p->so_kind == COBS_SO_DIAG ? static_cast<float*>(so) : nullptr;
@@ -220,7 +217,6 @@ cobs_status cobs_update_summaries(const cobs_params* p, int32_t batch, int32_t m
   a.batch = batch; a.hkv = p->n_kv_heads; a.max_len = max_len;
   a.nb_max = (int)nb_of(max_len); a.nc_max = (int)nc_of(p, max_len);
   a.head_dim = p->head_dim; a.rank = p->rank; a.bf16 = p->kv_dtype == COBS_BF16;
-  a.blocks_per_wave = 1;
   a.seq_lens = new_lens; a.old_lens = old_lens;
   a.touch_blocks = std::min((int)a.nb_max, cdiv(max_append - 1, 64) + 2);   // blocks a run of new positions can touch
   a.K = K; a.V = pool ? V : K;

@@ -9,7 +9,6 @@ namespace cobs {
 struct BuildArgs {
   int batch, hkv, max_len, nb_max, nc_max, head_dim, rank;
   bool bf16;
-  int blocks_per_wave;
   const int32_t* seq_lens;     // lengths the summaries are built for
   const int32_t* old_lens;     // incremental update: lengths they were valid for (else null)
   int touch_blocks;            // incremental update: workgroups per (sequence, kv-head)

@@ -7,13 +7,15 @@
 // (Janus issue #181, compression path) attends over mean-pooled tokens: the mean
 // of 32 consecutive keys (values) every 16 positions.
 //
-// One wavefront streams a short run of consecutive blocks of one (sequence,
-// kv-head) and one tensor (keys: mean, variance, pooled keys; values: pooled
-// values), so a block's rows take 64 registers and three waves share a SIMD.
-// Every 16-byte load instruction reads 1 KiB of contiguous rows, the block stays
-// in registers for the two-pass variance, and row sums are reduced with lane
-// shuffles.  Pooled token j = (chunk_j + chunk_{j+1}) / 32 where chunk_c is the
-// sum of rows [16c, 16c+16); the chunk after the run (the halo) is read once.
+// One wavefront reduces one block of one (sequence, kv-head) and one tensor (keys:
+// mean, variance, pooled keys; values: pooled values), so a block's rows take 64
+// registers and three waves share a SIMD; a workgroup takes four consecutive
+// blocks.  Every 16-byte load instruction reads 1 KiB of contiguous rows, the
+// block stays in registers for the two-pass variance, and row sums are reduced
+// with lane shuffles.  Pooled token j = (chunk_j + chunk_{j+1}) / 32 where chunk_c
+// is the sum of rows [16c, 16c+16): a token across two blocks of the workgroup
+// takes the first block's last chunk from LDS; the one after the workgroup's last
+// block reads that block's first chunk again (the halo, 1/16 of the rows).
 #include "cobs_device.h"
 #include "cobs_launch.h"
 
@@ -88,16 +90,19 @@ __device__ __forceinline__ void chunk_partials(const u32x4 (&x)[RowTiling<E, D>:
   }
 }
 
+constexpr int kDiagWaves = 4;        // consecutive blocks per build workgroup, one per wave
+
 template <typename E, int D>
-__global__ __launch_bounds__(64, 2) void k_build_diag(
+__global__ __launch_bounds__(64 * kDiagWaves, 2) void k_build_diag(
     const int32_t* __restrict__ seq_lens, int max_len, int nb_max, int nc_max,
     const typename E::storage* __restrict__ K, const typename E::storage* __restrict__ V,
     void* __restrict__ mu, float* __restrict__ var,
     typename E::storage* __restrict__ kc, typename E::storage* __restrict__ vc,
-    int blocks_per_wave, int want_var, int want_pool, int mu_bf16) {
+    int want_var, int want_pool, int mu_bf16) {
   using T = RowTiling<E, D>;
   constexpr int LPR = T::kLanesPerRow, RPL = T::kRowsPerLoad, NL = T::kLoads, EPL = T::kEpl;
-  const int lane = threadIdx.x;
+  __shared__ float last_chunk[kDiagWaves][D];   // each wave's rows [48, 64) summed, for its neighbour
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cc = lane % LPR;          // column chunk: columns [cc*EPL, cc*EPL+EPL)
   const int rg = lane / LPR;          // row group: rows rg, rg+RPL, ...
   const int hkv = gridDim.y;
@@ -108,9 +113,9 @@ __global__ __launch_bounds__(64, 2) void k_build_diag(
   const int run = want_pool ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
   const int L = seq_lens[seq];
   const int nb = (L + kBlock - 1) / kBlock;
-  const int b_begin = run * blocks_per_wave;
-  const int b_end = min(b_begin + blocks_per_wave, nb);
-  if (b_begin >= b_end) return;
+  if (run * kDiagWaves >= nb) return;           // the whole workgroup
+  const int b = run * kDiagWaves + wave;
+  const bool active = b < nb;
   const int nc = (want_pool && L >= 32) ? (L - 32) / 16 + 1 : 0;
 
   const size_t unit = (size_t)seq * hkv + head;
@@ -120,21 +125,14 @@ __global__ __launch_bounds__(64, 2) void k_build_diag(
   float* var_u = var ? var + unit * (size_t)nb_max * D : nullptr;
   typename E::storage* xc_u = want_pool ? (is_v ? vc : kc) + unit * (size_t)nc_max * D : nullptr;
 
-  auto load_block = [&](int b, u32x4 (&x)[NL]) {
+  float ch[4][EPL];                   // sums of the block's four 16-row chunks
+  if (active) {
+    u32x4 x[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int r = min(b * kBlock + i * RPL + rg, L - 1);
       x[i] = ld16(X + (size_t)r * D + cc * EPL);
     }
-  };
-
-  float carry[EPL];                   // chunk 3 of the previous block
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) carry[e] = 0.f;
-
-  for (int b = b_begin; b < b_end; ++b) {
-    u32x4 x[NL];
-    load_block(b, x);
     const int nrows = min(kBlock, L - b * kBlock);
     if (nrows < kBlock) {             // the last block of a sequence: rows past its end count as zero
 #pragma unroll
@@ -178,30 +176,47 @@ __global__ __launch_bounds__(64, 2) void k_build_diag(
       }
     }
     if (want_pool) {
-      // pooled token c = 4b + q - 1 spans chunk (4b+q-1) and chunk (4b+q)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float ch[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) ch[e] = reduce_rows<LPR>(part[q][e]);
+        for (int e = 0; e < EPL; ++e) ch[q][e] = reduce_rows<LPR>(part[q][e]);
+      }
+      // pooled token c = 4b + q - 1 spans chunk q - 1 and chunk q of this block (q = 1..3)
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
         const int c = 4 * b + q - 1;
-        // token 4b - 1 is emitted by the wave that owns block b - 1
-        if (c >= 0 && c < nc && !(q == 0 && b == b_begin)) {
+        if (c < nc) {
           float t[EPL];
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) t[e] = (carry[e] + ch[e]) * (1.0f / 32.0f);
+          for (int e = 0; e < EPL; ++e) t[e] = (ch[q - 1][e] + ch[q][e]) * (1.0f / 32.0f);
           if (rg == q % RPL) store_pooled<E, D>(xc_u + (size_t)c * D + cc * EPL, t);
         }
+      }
+      if (rg == 0) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) carry[e] = ch[e];
+        for (int e = 0; e < EPL; ++e) last_chunk[wave][cc * EPL + e] = ch[3][e];
       }
     }
   }
-  // halo: pooled token 4*b_end - 1 needs chunk 0 of block b_end
-  if (want_pool) {
-    const int c = 4 * b_end - 1;
-    if (c < nc) {   // then rows [64*b_end, 64*b_end + 16) are all < L
-      const int row0 = b_end * kBlock;
+  if (!want_pool) return;
+  __syncthreads();
+  if (!active) return;
+  // token 4b - 1 spans the previous block's last chunk and this block's first: the
+  // previous wave's sums from LDS; the first wave's is emitted by the workgroup
+  // before, whose last wave reads this block's first 16 rows once more (the halo)
+  if (wave > 0) {
+    const int c = 4 * b - 1;
+    if (c < nc) {
+      float t[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) t[e] = (last_chunk[wave - 1][cc * EPL + e] + ch[0][e]) * (1.0f / 32.0f);
+      if (rg == 0) store_pooled<E, D>(xc_u + (size_t)c * D + cc * EPL, t);
+    }
+  }
+  if (wave == kDiagWaves - 1) {
+    const int c = 4 * b + 3;
+    if (c < nc) {   // then rows [64(b+1), 64(b+1) + 16) are all < L
+      const int row0 = (b + 1) * kBlock;
       float a[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) a[e] = 0.f;
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(64, 2) void k_build_diag(
       }
       float t[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) t[e] = (carry[e] + reduce_rows<LPR>(a[e])) * (1.0f / 32.0f);
+      for (int e = 0; e < EPL; ++e) t[e] = (ch[3][e] + reduce_rows<LPR>(a[e])) * (1.0f / 32.0f);
       if (rg == 0) store_pooled<E, D>(xc_u + (size_t)c * D + cc * EPL, t);
     }
   }
@@ -322,14 +337,13 @@ __global__ __launch_bounds__(64) void k_append_diag(
 
 template <typename E, int D>
 static hipError_t launch_diag(const BuildArgs& a) {
-  const int bpw = a.blocks_per_wave;
-  const int runs = (a.nb_max + bpw - 1) / bpw;
+  const int runs = (a.nb_max + kDiagWaves - 1) / kDiagWaves;
   dim3 grid(a.kc != nullptr ? 2 * runs : runs, a.hkv, a.batch);
-  hipLaunchKernelGGL((k_build_diag<E, D>), grid, dim3(64), 0, a.stream,
+  hipLaunchKernelGGL((k_build_diag<E, D>), grid, dim3(64 * kDiagWaves), 0, a.stream,
                      a.seq_lens, a.max_len, a.nb_max, a.nc_max,
                      (const typename E::storage*)a.K, (const typename E::storage*)a.V,
                      a.mu, a.var, (typename E::storage*)a.kc, (typename E::storage*)a.vc,
-                     bpw, a.var != nullptr ? 1 : 0, a.kc != nullptr ? 1 : 0, a.fp4 ? 1 : 0);
+                     a.var != nullptr ? 1 : 0, a.kc != nullptr ? 1 : 0, a.fp4 ? 1 : 0);
   return hipGetLastError();
 }
 
