@@ -76,7 +76,7 @@ def calibrated_subspace(w, g):
     if not w.subspace:
         return None
     from block_sparse_long_compressed_amd import binding as B
-    from tests import gpu_util as U
+    from block_sparse_long_compressed_amd import runtime as U
     return B.cobs_query_subspace(U.params_for(w), g["Qcal"], w.subspace)
 
 
@@ -108,107 +108,107 @@ def counter_traffic(workload, alpha=None):
     return data.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, x, seconds):
-    """The fp64 oracle timed on the host for a bounded sample of decode queries."""
+def dense_bytes(w, lens):
+    """Bytes a dense decode step reads for the same queries: every key and value of
+    every (sequence, kv-head), plus the same Q, gates and output traffic."""
+    es = 2 if w.dtype == "bf16" else 4
+    kv = int(np.asarray(lens, dtype=np.int64).sum()) * w.n_kv_heads * w.head_dim * 2 * es
+    return kv + w.batch * w.n_q_heads * (w.head_dim * es + 3 * 4 + w.head_dim * 4)
+
+
+def _cpu_worker(w, x, units, seconds, ready, start, results):
+    """One host core of the CPU baseline: prebuild the oracle's summaries of its
+    (sequence, kv-head) units (untimed, as on the GPU side), then run whole
+    group queries round-robin over them until `seconds` have passed."""
     from threadpoolctl import threadpool_limits
     from oracle import cobs_oracle as O
     p = O.params_of(w)
     G = w.group
-    # summaries are per-prefix state, built once (untimed) as on the GPU side
-    units = {}
-    seqs = list(range(w.batch))
-    for s in seqs[:4]:
-        L = int(x["lens"][s])
-        for h in range(w.n_kv_heads):
+    with threadpool_limits(limits=1):
+        prepared = []
+        for s, h in units:
+            L = int(x["lens"][s])
             keys = x["K"][s, h, :L].astype(np.float64)
             vals = x["V"][s, h, :L].astype(np.float64)
-            units[(s, h)] = (keys, vals, L) + O.build_unit(p, keys, vals, L)
-    done = 0
-    with threadpool_limits(limits=1):
+            qg = x["Q"][s, 0, h * G:(h + 1) * G].astype(np.float64)
+            gt = x["gates"][s, 0, h * G:(h + 1) * G].astype(np.float64) if x["gates"] is not None else None
+            prepared.append((qg, keys, vals, L, gt) + tuple(O.build_unit(p, keys, vals, L)))
+        ready.put(1)
+        start.wait()
+        done = 0
         t0 = time.perf_counter()
         while True:
-            s = seqs[done % min(4, len(seqs))]
-            for h in range(w.n_kv_heads):
-                keys, vals, L, summ, kc, vc = units[(s, h)]
-                qg = x["Q"][s, 0, h * G:(h + 1) * G].astype(np.float64)
-                gt = x["gates"][s, 0, h * G:(h + 1) * G].astype(np.float64) if x["gates"] is not None else None
-                O.query_group(p, qg, keys, vals, L, L - 1, summ, kc, vc, gt)
+            qg, keys, vals, L, gt, summ, kc, vc = prepared[done % len(prepared)]
+            O.query_group(p, qg, keys, vals, L, L - 1, summ, kc, vc, gt)
             done += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-    return {"value": done / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} decode queries (all {w.n_kv_heads} kv-head groups each) over sequences "
-                      f"{seqs[:4]} of {w.name}, {el:.1f} s, summaries prebuilt"}
+    results.put((done, el))
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="decode_b1_L32k")
-    ap.add_argument("--alpha", type=float, default=None)
-    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the last-level cache")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--eager", action="store_true", help="launch steps directly instead of graph replays")
-    ap.add_argument("--mode", choices=["decode", "prefill", "build", "update", "recall", "copy"], default="decode",
-                    help="decode (the metric), prefill (MFMA utilisation), build (summary GB/s), "
-                         "update (one appended token per sequence: incremental summaries), "
-                         "recall (cumulant selections against the exact-mass selection), "
-                         "copy (plain copy of known size, to calibrate HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
-              "(multi-GPU sharding is a design note only)", file=sys.stderr)
-        sys.exit(2)
+class CpuBaseline:
+    """The fp64 oracle timed on the host cores: one forked process per core, each
+    owning a few (sequence, kv-head) units of the workload.  The processes are forked
+    before the GPU is touched and prebuild their summaries while the GPU part runs;
+    the timed region starts with finish()."""
 
+    def __init__(self, w, x, seconds):
+        import multiprocessing as mp
+        self.w, self.seconds = w, seconds
+        self.cores = max(1, min(16, len(os.sched_getaffinity(0))))   # one GPU's share of host cores
+        nseq = min(w.batch, -(-self.cores // w.n_kv_heads))
+        units = [(s, h) for s in range(nseq) for h in range(w.n_kv_heads)]
+        self.cores = min(self.cores, len(units))
+        self.seqs = list(range(nseq))
+        ctx = mp.get_context("fork")
+        self.ready, self.results, self.start = ctx.Queue(), ctx.Queue(), ctx.Event()
+        self.procs = [ctx.Process(target=_cpu_worker, args=(w, x, units[i::self.cores], seconds, self.ready,
+                                                            self.start, self.results), daemon=True)
+                      for i in range(self.cores)]
+        for pr in self.procs:
+            pr.start()
+
+    def finish(self):
+        for _ in self.procs:
+            self.ready.get()
+        self.start.set()
+        res = [self.results.get() for _ in self.procs]
+        for pr in self.procs:
+            pr.join()
+        group_queries = sum(r[0] for r in res)
+        el = max(r[1] for r in res)
+        w = self.w
+        return {"value": group_queries / w.n_kv_heads / el, "unit": "queries/s", "cores": self.cores,
+                "kind": "oracle",
+                "sample": f"{group_queries} kv-head group queries (a query = all {w.n_kv_heads} groups of one "
+                          f"sequence) over sequences {self.seqs} of {w.name}, {self.cores} processes of one "
+                          f"BLAS thread each for {el:.1f} s, summaries prebuilt"}
+
+
+def time_decode(w, x, g0, P, alpha, steps, warmup, replicas=0, eager=False, attention_only=True):
+    """Time one decode step (one launch of k_decode) on the uploaded batch g0: graph
+    replays over R input replicas, HIP events on the launch stream.  Returns a dict
+    with the step time and the algorithmic bytes of the selection actually made."""
     import torch
     from block_sparse_long_compressed_amd import binding as B
-    from block_sparse_long_compressed_amd import synth
-    from tests import gpu_util as U
-
-    if args.mode == "copy":
-        return bench_copy(args)
-    if args.mode == "prefill":
-        return bench_prefill(args)
-    if args.mode == "build":
-        return bench_build(args)
-    if args.mode == "update":
-        return bench_update(args)
-    if args.mode == "recall":
-        return bench_recall(args)
-    w = synth.WORKLOADS[args.workload]
-    if w.prefill:
-        raise SystemExit("use --mode prefill for prefill workloads")
-    alpha = w.alpha if args.alpha is None else args.alpha
-    log(f"[bench] workload {w.name} alpha {alpha}: generating inputs")
-    x = synth.make_inputs(w, args.seed)
-    B.lib()
-    g0 = U.to_device(x)
-    P = calibrated_subspace(w, g0)
+    from block_sparse_long_compressed_amd import runtime as U
     p = U.params_for(w, alpha=alpha, P=P)
     s0 = U.build(p, g0)
     torch.cuda.synchronize()
-
     # one untimed step to get the selection for the byte model
     out0, sel0 = U.decode(p, g0, s0)
     attn_bytes, sel_bytes = algorithmic_bytes(w, x["lens"], sel0, alpha)
     step_bytes = attn_bytes + sel_bytes
-    R = args.replicas or max(3, math.ceil(2 * MALL_BYTES / step_bytes))
-    log(f"[bench] step bytes {step_bytes / 2**20:.2f} MiB, replicas {R}")
-
+    R = replicas or max(3, math.ceil(2 * MALL_BYTES / step_bytes))
     reps = []
     for r in range(R):
-        g = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in g0.items()}
-        s = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in s0.items()}
+        g = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in g0.items()} if r else g0
+        s = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in s0.items()} if r else s0
         ws = B.alloc_workspace(p, w.batch, w.max_len)
         out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
         sel = torch.empty((w.batch, w.n_kv_heads, w.top_k), dtype=torch.int32, device="cuda")
         reps.append((g, s, ws, out, sel))
-    del g0, s0
     torch.cuda.synchronize()
 
     def step(i, with_sel_in=False):
@@ -237,55 +237,130 @@ def main():
 
     full = capture([lambda i=i: step(i) for i in range(R)])
     singles = [capture([lambda i=i: step(i)]) for i in range(R)]
-    attn_only = capture([lambda i=i: step(i, with_sel_in=True) for i in range(R)])
 
-    def run_steps(n):
-        if args.eager:
+    def run_steps(n, with_sel_in=False, graph=None):
+        if eager:
             for i in range(n):
-                step(i)
+                step(i, with_sel_in)
             return
         for _ in range(n // R):
-            full.replay()
+            (graph or full).replay()
         for i in range(n % R):
             singles[i].replay()
 
-    log(f"[bench] warmup {args.warmup}")
-    run_steps(args.warmup)
+    run_steps(warmup)
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    run_steps(args.steps)
+    run_steps(steps)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {ms_step * 1e3:.2f} us/step (host wall {wall / args.steps * 1e6:.2f} us/step)")
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    res = {"us_per_step": us, "host_wall_us_per_step": wall / steps * 1e6, "step_bytes": step_bytes,
+           "attn_bytes": attn_bytes, "replicas": R, "sel0": sel0}
+    if attention_only:
+        # the same kernel with the caller's selection (attention roles only), for reference
+        attn = capture([lambda i=i: step(i, with_sel_in=True) for i in range(R)])
+        n_attn = max(R, (steps // R) * R)
+        for _ in range(2):
+            attn.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(n_attn // R):
+            if eager:
+                for i in range(R):
+                    step(i, with_sel_in=True)
+            else:
+                attn.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        res["attn_us"] = ev0.elapsed_time(ev1) * 1e3 / n_attn
+        del attn
+    del full, singles, reps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
-    # the same kernel with the caller's selection (attention roles only), for reference
-    n_attn = max(R, (args.steps // R) * R)
-    for _ in range(2):
-        attn_only.replay()
-    torch.cuda.synchronize()
-    ev0.record()
-    for r in range(n_attn // R):
-        if args.eager:
-            for i in range(R):
-                step(i, with_sel_in=True)
-        else:
-            attn_only.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    attn_us = ev0.elapsed_time(ev1) * 1e3 / n_attn
-    attn_gbps = attn_bytes / (attn_us * 1e-6) / 1e9
-    log(f"[bench] attention roles alone {attn_us:.2f} us, {attn_gbps:.0f} GB/s")
+
+def line_of(w, alpha, r):
+    """Per-workload summary: step time, queries/s, algorithmic GB/s and fraction of HBM peak."""
+    gbps = r["step_bytes"] / (r["us_per_step"] * 1e-6) / 1e9
+    return {"workload": w.name, "alpha": alpha, "us_per_step": r["us_per_step"],
+            "queries_per_s": w.batch / (r["us_per_step"] * 1e-6), "step_bytes": r["step_bytes"],
+            "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS}
+
+
+EXTRA_WORKLOADS = ["decode_b1_L32k", "decode_b8_L128k_rank4", "decode_b8_L128k_rank4_fp4",
+                   "decode_b8_L128k_sub85_fp4"]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="decode_b32_L16k32k")
+    ap.add_argument("--alpha", type=float, default=None)
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the last-level cache")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the alpha sweep and the other decode workloads reported beside the headline")
+    ap.add_argument("--extras", default=",".join(EXTRA_WORKLOADS),
+                    help="comma-separated decode workloads timed after the headline (latency, long context)")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--eager", action="store_true", help="launch steps directly instead of graph replays")
+    ap.add_argument("--mode", choices=["decode", "prefill", "build", "update", "recall", "copy"], default="decode",
+                    help="decode (the metric), prefill (MFMA utilisation), build (summary GB/s), "
+                         "update (one appended token per sequence: incremental summaries), "
+                         "recall (cumulant selections against the exact-mass selection), "
+                         "copy (plain copy of known size, to calibrate HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+              "(multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_compressed_amd import binding as B
+    from block_sparse_long_compressed_amd import synth
+    from block_sparse_long_compressed_amd import runtime as U
+
+    if args.mode == "copy":
+        return bench_copy(args)
+    if args.mode == "prefill":
+        return bench_prefill(args)
+    if args.mode == "build":
+        return bench_build(args)
+    if args.mode == "update":
+        return bench_update(args)
+    if args.mode == "recall":
+        return bench_recall(args)
+    w = synth.WORKLOADS[args.workload]
+    if w.prefill:
+        raise SystemExit("use --mode prefill for prefill workloads")
+    alpha = w.alpha if args.alpha is None else args.alpha
+    log(f"[bench] workload {w.name} alpha {alpha}: generating inputs")
+    x = synth.make_inputs(w, args.seed)
+    # the CPU baseline's processes are forked before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else CpuBaseline(w, x, args.cpu_seconds)
+    B.lib()
+    g0 = U.to_device(x)
+    P = calibrated_subspace(w, g0)
+    log(f"[bench] timing {args.steps} steps (warmup {args.warmup})")
+    r = time_decode(w, x, g0, P, alpha, args.steps, args.warmup, args.replicas, args.eager)
+    ms_step = r["us_per_step"] * 1e-3
+    step_bytes, attn_bytes = r["step_bytes"], r["attn_bytes"]
+    log(f"[bench] {r['us_per_step']:.2f} us/step (host wall {r['host_wall_us_per_step']:.2f} us/step), "
+        f"step bytes {step_bytes / 2**20:.2f} MiB, replicas {r['replicas']}")
+    attn_gbps = attn_bytes / (r["attn_us"] * 1e-6) / 1e9
+    log(f"[bench] attention roles alone {r['attn_us']:.2f} us, {attn_gbps:.0f} GB/s")
     # the step is one launch of k_decode: its algorithmic bytes over its duration
     achieved = step_bytes / (ms_step * 1e-3) / 1e9
-
     qps = w.batch / (ms_step * 1e-3)
-    kv_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    dense = dense_bytes(w, x["lens"])
     result = {
         "metric": "sparse-decode queries/s and achieved HBM GB/s (% of peak) at 32k ctx, top-k=16",
         "value": qps,
@@ -299,23 +374,70 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "achieved_GBps": kv_gbps,
-        "pct_of_hbm_peak": 100.0 * kv_gbps / HBM_PEAK_GBPS,
+        "achieved_GBps": achieved,
+        "pct_of_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.max_len,
                    "seq_len_min": w.min_len, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "block": 64, "top_k": w.top_k, "window": w.window,
                    "cmp": [w.cmp_len, w.cmp_stride], "second_order": w.so_kind, "rank": w.rank,
-                   "alpha": alpha, "step_bytes": step_bytes, "replicas": R, "graph_replay": not args.eager},
+                   "alpha": alpha, "step_bytes": step_bytes, "replicas": r["replicas"],
+                   "graph_replay": not args.eager},
         "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic(w.name, alpha), "bytes_per_launch": step_bytes,
-                     "avg_launch_us": ms_step * 1e3,
-                     "attention_only": {"avg_launch_us": attn_us, "bytes_per_launch": attn_bytes,
+                     "avg_launch_us": r["us_per_step"],
+                     "attention_only": {"avg_launch_us": r["attn_us"], "bytes_per_launch": attn_bytes,
                                         "achieved": attn_gbps}},
+        # KV read traffic of this step against dense attention over the same queries
+        "kv_traffic_dense_over_cobs": dense / step_bytes,
     }
-    if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    if not args.no_extras:
+        # the alpha sweep of the batched workload on the same inputs (alpha = 0 is the
+        # first-order mean-pool selector of NSA: its bytes give the COBS / NSA ratio)
+        sweep = {}
+        for a in (0.0, 0.5, 1.0, 2.0):
+            if a == alpha:
+                sweep[str(a)] = line_of(w, a, r)
+                continue
+            log(f"[bench] alpha {a}")
+            ra = time_decode(w, x, g0, P, a, max(60, args.steps // 3), 10, args.replicas, args.eager,
+                             attention_only=False)
+            sweep[str(a)] = line_of(w, a, ra)
+        result["alpha_sweep"] = sweep
+        if alpha == 1.0:
+            result["kv_traffic_cobs_over_alpha0"] = step_bytes / sweep["0.0"]["step_bytes"]
+        result["pages_reported_kv_traffic"] = {"cobs_over_nsa": 1.21, "dense_over_cobs": 15.15,
+                                               "note": "context only: the pages' own ratios, on a 32k "
+                                                       "retrieval suite with unstated block size, top-k "
+                                                       "and hardware"}
+    del g0
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        extras = {}
+        inputs = {}
+        for name in [e for e in args.extras.split(",") if e]:
+            we = synth.WORKLOADS[name]
+            log(f"[bench] extra workload {name}: generating inputs")
+            # the rank-4 storages share one draw (the recipe does not depend on the storage)
+            key = (we.batch, we.max_len, we.min_len, we.n_q_heads, we.n_kv_heads, we.head_dim, we.dtype,
+                   we.needles, we.subspace)
+            if key not in inputs:
+                inputs.clear()
+                inputs[key] = synth.make_inputs(we, args.seed)
+            xe = inputs[key]
+            ge = U.to_device(xe)
+            Pe = calibrated_subspace(we, ge)
+            re_ = time_decode(we, xe, ge, Pe, we.alpha, max(60, args.steps // 3), 10, args.replicas, args.eager,
+                              attention_only=False)
+            extras[name] = line_of(we, we.alpha, re_)
+            extras[name]["kv_traffic_dense_over_cobs"] = dense_bytes(we, xe["lens"]) / re_["step_bytes"]
+            log(f"[bench]   {name}: {re_['us_per_step']:.2f} us/step")
+            del ge, Pe
+            torch.cuda.empty_cache()
+        result["extra_workloads"] = extras
+    if cpu is not None:
+        log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s on {cpu.cores} processes)")
+        result["cpu_baseline"] = cpu.finish()
     print(json.dumps(result), flush=True)
 
 
@@ -351,7 +473,7 @@ def bench_build(args):
     import torch
     from block_sparse_long_compressed_amd import binding as B
     from block_sparse_long_compressed_amd import synth
-    from tests import gpu_util as U
+    from block_sparse_long_compressed_amd import runtime as U
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w, args.seed)
     g = U.to_device(x)
@@ -373,7 +495,7 @@ def bench_update(args):
     import torch
     from block_sparse_long_compressed_amd import binding as B
     from block_sparse_long_compressed_amd import synth
-    from tests import gpu_util as U
+    from block_sparse_long_compressed_amd import runtime as U
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w, args.seed)
     g = U.to_device(x)
@@ -394,7 +516,7 @@ def bench_recall(args):
     import torch
     from block_sparse_long_compressed_amd import binding as B
     from block_sparse_long_compressed_amd import synth
-    from tests import gpu_util as U
+    from block_sparse_long_compressed_amd import runtime as U
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w, args.seed)
     g = U.to_device(x)
@@ -476,7 +598,7 @@ def bench_prefill(args):
     import torch
     from block_sparse_long_compressed_amd import binding as B
     from block_sparse_long_compressed_amd import synth
-    from tests import gpu_util as U
+    from block_sparse_long_compressed_amd import runtime as U
     w = synth.WORKLOADS[args.workload if args.workload.startswith("prefill") else "prefill_T8k_L32k"]
     x = synth.make_inputs(w, args.seed)
     p = U.params_for(w)
