@@ -65,6 +65,8 @@ _SIGNATURES = {
                                        _vp, _vp, _sz, _vp]),
     "cobs_sparse_attn_prefill": (_i32, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _vp, _sz, _vp]),
+    "cobs_decode_status": (_i32, [_P, _i32, _i32, _vp, _sz, ctypes.POINTER(ctypes.c_uint32), _vp]),
+    "cobs_set_poll_limit": (None, [ctypes.c_uint32]),
     "cobs_query_subspace_workspace_bytes": (_sz, [_P]),
     "cobs_query_subspace": (_i32, [_P, _i32, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -187,6 +189,23 @@ def cobs_sparse_attn_decode(p: cobs_params, seq_lens, Q, K, V, mu, so, kc, vc, g
         ctypes.byref(p), batch, max_len, _ptr(seq_lens), _ptr(Q), _ptr(K), _ptr(V), _ptr(mu), _ptr(so),
         _ptr(kc), _ptr(vc), _ptr(gates), _ptr(sel_in), _ptr(sel_out), _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+COBS_STATUS_WAIT_GAVE_UP = 1
+
+
+def cobs_decode_status(p: cobs_params, batch: int, max_len: int, ws, stream=None) -> int:
+    """Status bits of the decode steps run on ws since the last query (synchronises)."""
+    flags = ctypes.c_uint32()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("cobs_decode_status", lib().cobs_decode_status(ctypes.byref(p), batch, max_len, _ptr(ws), nbytes,
+                                                          ctypes.byref(flags), _stream(stream)))
+    return flags.value
+
+
+def cobs_set_poll_limit(polls: int) -> None:
+    """Test hook: polls of a published selection code before a wave gives up."""
+    lib().cobs_set_poll_limit(polls & 0xFFFFFFFF)
 
 
 def cobs_sparse_attn_prefill(p: cobs_params, q_pos0: int, Q, K, V, mu, so, kc, vc, gates, out, ws,

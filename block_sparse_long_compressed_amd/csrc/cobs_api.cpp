@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "cobs_launch.h"
 
@@ -14,7 +15,6 @@ namespace {
 
 using namespace cobs;
 
-constexpr int kSelWaves = 1024;         // scoring waves (each keeps up to two summary tiles in flight)
 constexpr size_t kAlign = 256;
 constexpr int kMaxBlocks = 4096;        // per sequence (selection keeps <= 16 keys per thread)
 
@@ -69,64 +69,76 @@ cobs_status check_sizes(int batch, int max_len, int tokens) {
 }
 
 // Launch shapes and the workspace carve-up; a pure function of the sizes so that
-// cobs_workspace_bytes and every call agree.
+// cobs_workspace_bytes and every call agree.  Decode workgroups have NW waves (8, or 4
+// for fp32 keys at d = 128, whose attention tile needs a SIMD's whole register file).
+constexpr int kLeadTilesPerWave = 2;    // selected tiles each wave of the selecting workgroup runs
+constexpr int kSlcTilesPerWave = 2;     // selected tiles per wave of the other selected-branch workgroups
+constexpr int kScoreTilesPerWave = 4;   // 16-block summary tiles per scoring wave
+constexpr int kWcTilesPerWave = 5;      // target window/pooled tiles per wave
+constexpr int kFillWorkgroups = 256;    // workgroups that fill the chip once (one per CU)
+constexpr size_t kDecodeLdsBudget = 150 * 1024;
+
 struct Plan {
-  int units_sel, units_attn;
-  int sel_tpw, sel_splits;
-  int attn_waves, tpw_wc, tpw_slc, wg_slc, wg_win, wg_cmp, attn_P;
-  size_t off_cnt_sel, off_cnt_attn, off_ready, off_scores, off_lse, off_sel, off_ml, off_o, total;
+  int nw, splits, sel_tpw;
+  int lead_tiles, wg_slc, wg_wc;         // with a selecting workgroup (the fused step)
+  int wg_slc_in;                         // with the caller's selection (attention only)
+  size_t off_cnt_sel, off_cnt_attn, off_ready, off_status, off_scores, off_lse, off_sel, off_ml, off_o, total;
 };
 
 Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
   Plan pl;
   const int hkv = p->n_kv_heads, G = group_of(p), d = p->head_dim;
+  const bool bf16 = p->kv_dtype == COBS_BF16;
   const int nb = (int)nb_of(max_len);
   const int nb_pad = (nb + 15) / 16 * 16;
-  pl.units_sel = batch * tokens * hkv;
-  pl.units_attn = batch * hkv;
-  // scoring: 16-block tiles, 4 waves per workgroup
+  const int units_sel = batch * tokens * hkv;
+  const int units = batch * hkv;
+  pl.nw = decode_waves(bf16, d);
+  // scoring: one workgroup per unit keeps the raw scores in LDS when the unit's tiles
+  // fit its waves; longer contexts split the tiles and hand the scores off
   const int tiles = cdiv(nb, 16);
-  pl.sel_tpw = std::min(8, std::max(1, cdiv(pl.units_sel * tiles, kSelWaves)));
-  pl.sel_splits = cdiv(tiles, 4 * pl.sel_tpw);
-  // attention: 64-key tiles of the three branches
-  const int t_slc = p->top_k;
+  if (tiles <= pl.nw * kScoreTilesPerWave &&
+      decode_select_lds_bytes(bf16, d, nb_pad, true) <= kDecodeLdsBudget) {
+    pl.splits = 1;
+    pl.sel_tpw = cdiv(tiles, pl.nw);
+  } else {
+    pl.splits = cdiv(tiles, pl.nw * kScoreTilesPerWave);
+    pl.sel_tpw = cdiv(tiles, pl.nw * pl.splits);
+  }
+  // selected branch: the lead's share, then workgroups that wait for the rest
+  pl.lead_tiles = std::min(p->top_k, pl.nw * kLeadTilesPerWave);
+  pl.wg_slc = cdiv(p->top_k - pl.lead_tiles, pl.nw * kSlcTilesPerWave);
+  pl.wg_slc_in = cdiv(p->top_k, pl.nw * kSlcTilesPerWave);
+  // window and pooled tiles: about kWcTilesPerWave per wave, spread wider when the
+  // units are too few to fill the chip
   const int t_win = p->window > 0 ? cdiv(std::min(p->window, max_len), 64) : 0;
   const int t_cmp = cdiv((int)nc_of(p, max_len), 64);
-  pl.attn_waves = 4;
-  // Tiles per wave of each branch (chosen by measurement on MI355X).  The window and
-  // pooled branches take long waves when there is a moderate amount of them (a few
-  // thousand tiles: fewer workgroups and hand-offs, and a thinner stream of loads
-  // beside the scoring) and shorter ones when there is much more (the selection
-  // then runs long and short waves fill it better) or very little (latency-bound).
-  // The selected branch starts last, after its unit's selection: few, full
-  // workgroups.
-  const int wc_tiles = pl.units_attn * (t_win + t_cmp);
-  if (wc_tiles <= 2048) {
-    pl.tpw_wc = 4; pl.tpw_slc = 1;
-  } else if (wc_tiles <= 6144) {
-    pl.tpw_wc = 11; pl.tpw_slc = 4;
-  } else {
-    pl.tpw_wc = 4; pl.tpw_slc = 2;
-  }
-  pl.wg_slc = cdiv(t_slc, pl.attn_waves * pl.tpw_slc);
-  pl.wg_win = cdiv(t_win, pl.attn_waves * pl.tpw_wc);
-  pl.wg_cmp = cdiv(t_cmp, pl.attn_waves * pl.tpw_wc);
-  pl.attn_P = pl.wg_slc + pl.wg_win + pl.wg_cmp;
+  const int t_wc = t_win + t_cmp;
+  pl.wg_wc = t_wc == 0 ? 0 : std::max(cdiv(t_wc, pl.nw * kWcTilesPerWave),
+                                      std::min(cdiv(t_wc, pl.nw), cdiv(kFillWorkgroups, std::max(units, 1)) - 1));
+  if (t_wc > 0) pl.wg_wc = std::max(pl.wg_wc, 1);
+  const int P = std::max(1 + pl.wg_slc, pl.wg_slc_in) + 2 * pl.wg_wc;   // partial slots, either mode
 
   // with several query tokens only the selection buffer is used (prefill path)
   const bool decode = tokens == 1;
   size_t off = 0;
-  pl.off_cnt_sel = off;  off = align_up(off + sizeof(uint32_t) * pl.units_sel);
-  pl.off_cnt_attn = off; off = align_up(off + sizeof(uint32_t) * pl.units_attn);
-  pl.off_ready = off;    off = align_up(off + sizeof(uint32_t) * (size_t)pl.units_attn * p->top_k);
-  pl.off_scores = off;   off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_sel * 16 * nb_pad : 0));
-  pl.off_lse = off;      off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_sel * pl.sel_splits * 32 : 0));
-  pl.off_sel = off;      off = align_up(off + sizeof(int32_t) * (size_t)pl.units_sel * p->top_k);
-  pl.off_ml = off;       off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_attn * pl.attn_P * 32 : 0));
-  pl.off_o = off;        off = align_up(off + (decode ? sizeof(float) * (size_t)pl.units_attn * pl.attn_P * G * d : 0));
+  pl.off_cnt_sel = off;  off = align_up(off + sizeof(uint32_t) * units_sel);
+  pl.off_cnt_attn = off; off = align_up(off + sizeof(uint32_t) * units);
+  pl.off_ready = off;    off = align_up(off + sizeof(uint32_t) * (size_t)units * p->top_k);
+  pl.off_status = off;   off = align_up(off + sizeof(uint32_t));
+  pl.off_scores = off;   off = align_up(off + (decode && pl.splits > 1 ? sizeof(float) * (size_t)units_sel * 16 * nb_pad : 0));
+  pl.off_lse = off;      off = align_up(off + (decode && pl.splits > 1 ? sizeof(float) * (size_t)units_sel * pl.splits * 32 : 0));
+  pl.off_sel = off;      off = align_up(off + sizeof(int32_t) * (size_t)units_sel * p->top_k);
+  pl.off_ml = off;       off = align_up(off + (decode ? sizeof(float) * (size_t)units * P * 32 : 0));
+  pl.off_o = off;        off = align_up(off + (decode ? sizeof(float) * (size_t)units * P * G * d : 0));
   pl.total = off;
   return pl;
 }
+
+// Polls of one published selection code before a selected-branch wave gives up
+// (about 0.1 s); lowered only by tests, through cobs_set_poll_limit.
+constexpr uint32_t kDefaultPollCap = 1u << 21;
+std::atomic<uint32_t> g_poll_cap{kDefaultPollCap};
 
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
@@ -253,18 +265,20 @@ static DecodeArgs decode_args(const cobs_params* p, const Plan& pl, int32_t batc
   a.window = p->window; a.cmp_on = (p->cmp_len > 0 && nc_of(p, max_len) > 0) ? 1 : 0; a.rank = p->rank;
   a.so_kind = kernel_kind(p); a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha; a.scale = scale_of(p);
   a.do_select = a.do_attn = false;
-  a.splits = pl.sel_splits; a.sel_tpw = pl.sel_tpw;
-  a.tpw_wc = pl.tpw_wc; a.tpw_slc = pl.tpw_slc; a.wg_slc = pl.wg_slc; a.wg_win = pl.wg_win; a.wg_cmp = pl.wg_cmp;
+  a.splits = pl.splits; a.sel_tpw = pl.sel_tpw;
+  a.lead_tiles = pl.lead_tiles; a.wg_slc = pl.wg_slc; a.tpw_slc = kSlcTilesPerWave; a.wg_wc = pl.wg_wc;
   a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr; a.mu = a.so = a.gates = nullptr;
   a.sel = nullptr; a.sel_in = nullptr; a.sel_score = nullptr; a.out = nullptr;
   a.P = p->subspace_dim > 0 ? p->subspace : nullptr; a.sub_s = p->subspace_dim; a.vlen = vec_len(p);
   a.sel_counters = at<uint32_t>(ws, pl.off_cnt_sel);
   a.attn_counters = at<uint32_t>(ws, pl.off_cnt_attn);
   a.ready = at<uint32_t>(ws, pl.off_ready);
+  a.status = at<uint32_t>(ws, pl.off_status);
   a.scores = at<float>(ws, pl.off_scores);
   a.lse_part = at<float>(ws, pl.off_lse);
   a.part_ml = at<float>(ws, pl.off_ml);
   a.part_o = at<float>(ws, pl.off_o);
+  a.poll_cap = g_poll_cap.load(std::memory_order_relaxed);
   a.stream = stream;
   return a;
 }
@@ -329,6 +343,7 @@ cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t
   DecodeArgs a = decode_args(p, pl, batch, max_len, seq_lens, ws, s);
   a.do_select = sel_in == nullptr;
   a.do_attn = true;
+  if (sel_in) { a.lead_tiles = 0; a.wg_slc = pl.wg_slc_in; }
   a.Q = Q; a.K = K; a.V = V; a.kc = kc; a.vc = vc; a.mu = mu; a.so = so; a.gates = gates; a.out = out;
   a.sel = sel_out ? sel_out : at<int32_t>(ws, pl.off_sel);
   a.sel_in = sel_in;
@@ -355,6 +370,27 @@ cobs_status cobs_sparse_attn_prefill(const cobs_params* p, int32_t seq_len, int3
   if (st2 != COBS_OK) return st2;
   return hip_status(launch_prefill_attn(a));
 }
+
+cobs_status cobs_decode_status(const cobs_params* p, int32_t batch, int32_t max_len, void* ws, size_t ws_bytes,
+                               uint32_t* flags, void* stream) {
+  cobs_status st = check_params(p);
+  if (st != COBS_OK) return st;
+  if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
+  if (!flags || !ws) return COBS_ERR_INVALID_ARG;
+  const Plan pl = make_plan(p, batch, max_len, 1);
+  if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* dev = at<uint32_t>(ws, pl.off_status);
+  if (hipMemcpyAsync(flags, dev, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return COBS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return COBS_ERR_HIP;
+  if (*flags != 0u) {
+    if (hipMemsetAsync(dev, 0, sizeof(uint32_t), s) != hipSuccess) return COBS_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return COBS_ERR_HIP;
+  }
+  return COBS_OK;
+}
+
+void cobs_set_poll_limit(uint32_t polls) { g_poll_cap.store(polls == 0xFFFFFFFFu ? kDefaultPollCap : polls); }
 
 size_t cobs_query_subspace_workspace_bytes(const cobs_params* p) {
   if (!p || p->n_kv_heads < 1 || (p->head_dim != 64 && p->head_dim != 128)) return 0;

@@ -30,8 +30,9 @@ struct DecodeArgs {
   float alpha, scale;
   bool do_select, do_attn;
   int splits, sel_tpw;         // scoring workgroups per (sequence, kv-head), 16-block tiles per wave
-  int tpw_wc, tpw_slc;             // attention: 64-key tiles per wave (window and pooled; selected)
-  int wg_slc, wg_win, wg_cmp;      // attention workgroups per branch and unit
+  int lead_tiles;              // selected tiles the selecting workgroup attends to itself
+  int wg_slc, tpw_slc;         // further selected-branch workgroups per unit, tiles per wave
+  int wg_wc;                   // window/pooled workgroups per unit
   const int32_t* seq_lens;
   const void *Q, *K, *V, *kc, *vc;
   const void *mu, *so;         // summaries in the layout of so_kind (3, 5: compressed storage)
@@ -43,8 +44,9 @@ struct DecodeArgs {
   float* sel_score;
   float* out;
   // workspace
-  uint32_t *sel_counters, *attn_counters, *ready;
+  uint32_t *sel_counters, *attn_counters, *ready, *status;
   float *scores, *lse_part, *part_ml, *part_o;
+  uint32_t poll_cap;           // polls of one selection code before a wave gives up
   hipStream_t stream;
 };
 
@@ -80,6 +82,8 @@ hipError_t launch_build_diag(const BuildArgs& a);
 hipError_t launch_build_lowrank(const BuildArgs& a);
 hipError_t launch_append_diag(const BuildArgs& a);     // mean, diagonal, pooled tokens of touched blocks
 hipError_t launch_decode(const DecodeArgs& a);
+int decode_waves(bool bf16, int head_dim);      // waves per decode workgroup
+size_t decode_select_lds_bytes(bool bf16, int head_dim, int nb_pad, bool raw_in_lds);
 hipError_t launch_prefill_select(const PrefillArgs& a);
 hipError_t launch_prefill_attn(const PrefillArgs& a);
 hipError_t launch_prefill_attn_bf16(const PrefillArgs& a);   // token-blocked, bf16 K/V

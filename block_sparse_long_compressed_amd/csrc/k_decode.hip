@@ -11,21 +11,31 @@
 // paths, each an exact softmax over its own keys, combined with gates:
 // out = g_cmp o_cmp + g_slc o_slc + g_win o_win.
 //
-// Workgroups take one of three roles, in linear index order:
-//   [0, S)          scoring: 16-block tiles on the fp32 MFMA, per-head LSE partials;
-//                   the last scoring workgroup of a (sequence, kv-head) runs the
-//                   radix select and publishes each entry of the selection as a
-//                   code (0 = not yet, 1 = no block, b + 2 = block b);
-//   [S, S+WC)       window and pooled-token attention: independent of the
-//                   selection, so they overlap scoring;
-//   [S+WC, total)   selected-block attention: each wave polls (bounded) the codes
-//                   of its own tiles, so it starts as soon as they are published.
-// Workgroups are dispatched in index order on each XCD, so every scoring
-// workgroup is resident before any waiter behind it and the wait cannot deadlock;
-// the wait is capped regardless, and every address a waiter derives from the
-// selection is bounds-checked.  The last attention workgroup of a unit merges the
-// per-workgroup partials of each branch by log-sum-exp rescaling, applies the
-// gates and resets the unit's counters and codes for the next call.
+// A unit is one (sequence, kv-head).  Workgroups of NW waves take one of three
+// roles, in linear index order:
+//   scoring   `splits` per unit.  Each scores a share of the unit's 16-block summary
+//             tiles.  With one scoring workgroup per unit the raw block scores stay in
+//             LDS; otherwise they travel block-major through the workspace and the
+//             last workgroup to arrive collects them.  The workgroup that holds all
+//             the scores (the lead) forms shat, runs the radix select, writes the
+//             selection and then attends to the first `lead_tiles` selected blocks
+//             itself, straight from the selection in LDS.  The remaining selected
+//             blocks are published as codes (0 = not yet, 1 = no block, b + 2 = block
+//             b) for the selected-branch workgroups.
+//   window /  `wg_wc` per unit; their waves split the unit's window tiles and pooled
+//   pooled    tiles evenly (independent of the selection, so they overlap scoring).
+//   selected  `wg_slc` per unit: the selected blocks beyond the lead's share.  Each
+//             wave polls (bounded) the codes of its own tiles; with the caller's
+//             selection they read it directly.
+// Workgroups are dispatched in index order on each XCD, so a unit's lead is resident
+// before any workgroup that waits on it.  The wait is capped regardless: a wave that
+// gives up treats the tile as empty and sets bit 0 of the workspace status word,
+// which the host reads with cobs_decode_status.  Every address derived from a
+// selection is bounds-checked.  Each attention workgroup merges its waves per branch
+// into one partial per branch slot; the last one of a unit merges the partials of
+// each branch by log-sum-exp rescaling, applies the gates and resets the unit's
+// counters and codes for the next call.  The lead arrives there too, so the codes are
+// reset only after they were published.
 //
 // Data one workgroup leaves for another travels with sc1 (device-coherent)
 // stores and loads; see the hand-off helpers in cobs_device.h.
@@ -38,9 +48,7 @@
 
 namespace cobs {
 
-constexpr int kThreads = 256;
-constexpr int kSelMaxSplits = 64;              // scoring workgroups per (sequence, kv-head)
-constexpr uint32_t kSpinCap = 1u << 21;        // ~0.1 s of polling before a waiter gives up
+constexpr int kSelMaxSplits = 64;              // scoring workgroups per unit
 
 struct DecodeParams {
   int hkv, group, max_len, nb_max, nb_pad, top_k;
@@ -52,43 +60,257 @@ struct DecodeParams {
   const void *mu, *so;
   const float* P;               // query subspaces [hkv][sub_s][d] (subspace score kinds)
   int sub_s, vlen;              // subspace dimension; length of a rank-r vector
-  int32_t* sel;                 // selection written by the scoring role
+  int32_t* sel;                 // selection written by the lead
   float* sel_score;
   uint32_t* sel_counters;
-  float* scores;                // [unit][nb_pad][16]
-  float* lse_part;              // [unit][splits][16][2]
+  float* scores;                // [unit][nb_pad][16] (splits > 1)
+  float* lse_part;              // [unit][splits][16][2] (splits > 1)
   uint32_t* pub;                // [unit][top_k] published selection codes (null: nobody waits)
   // attention
-  int wc_wgs, slc_wgs, nc_max, window, cmp_on, tpw, tpw_slc, wg_slc, wg_win, wg_cmp;
+  int do_attn, has_lead, lead_tiles;
+  int wc_wgs, slc_wgs, nc_max, window, cmp_on, wg_wc, wg_slc, tpw_slc;
   float scale_log2;
   const void *K, *V, *kc, *vc;
   const float* gates;
-  const int32_t* sel_attn;      // selection the attention reads (sel or the caller's)
-  int wait_ready;
+  const int32_t* sel_in;        // the caller's selection (no lead)
   float* out;
   uint32_t* attn_counters;
   float* part_ml;               // [unit][P][16][2]
   float* part_o;                // [unit][P][G][d]
+  uint32_t* status;             // bit 0: a selected-branch wait gave up
+  uint32_t poll_cap;            // polls of one code before a wave gives up
 };
 
+// Partial slots of a unit: selected [0, ns), window [ns, ns + wg_wc), pooled
+// [ns + wg_wc, ns + 2 wg_wc), with ns = has_lead + wg_slc.
+__device__ __forceinline__ int slc_slots(const DecodeParams& p) { return p.has_lead + p.wg_slc; }
+__device__ __forceinline__ int n_slots(const DecodeParams& p) { return slc_slots(p) + 2 * p.wg_wc; }
+
 // LDS of the scoring role (inside the launch's dynamic buffer).
+template <int NW>
 struct SelLds {
-  float red_m[4][16], red_s[4][16];
-  uint32_t hist2[2][4][256];
-  int scan_w[4];
+  float red_m[NW][16], red_s[NW][16];
+  uint32_t hist2[2][NW][256];
+  int scan_w[NW];
   int bcast[4];
   float lse_sh[16];
   float red_part[kSelMaxSplits * 32];
   f32x4 wsub_x[8 * 64];          // subspace weights exchanged between the waves
-  // followed by [nb_pad] keys and [nb_pad] group scores
+  // followed by [nb_pad] keys, [nb_pad] group scores and, with one scoring
+  // workgroup per unit, [nb_pad][16] raw scores
 };
 
-template <typename E, int D, int KIND, int HV>
-__device__ void select_role(const DecodeParams& p, int unit, int split, unsigned char* smem) {
-  constexpr int NU = D / 16;
-  SelLds& sl = *reinterpret_cast<SelLds*>(smem);
-  uint32_t* s_key = reinterpret_cast<uint32_t*>(smem + sizeof(SelLds));
+template <int NW>
+__host__ __device__ constexpr size_t select_lds_bytes(int nb_pad, bool raw_in_lds) {
+  return sizeof(SelLds<NW>) + (size_t)nb_pad * 8 + (raw_in_lds ? (size_t)nb_pad * 64 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// One wave's run over its 64-key tiles.  src(j, Kt, Vt) returns the number of valid
+// keys of the wave's j-th tile (0: no more tiles; valid tiles form a prefix).  The
+// next tile's K loads go out once this tile's scores are formed (overlapping the
+// softmax and P V), its V loads after P V (overlapping the next scores).  The
+// group's queries (the B operand of S = K Q^T) are requested after the first tile,
+// so no round trip precedes the tile loads; columns n >= G repeat head G-1, whose
+// scores and outputs stay in their own columns and are never merged or written.
+// ---------------------------------------------------------------------------
+template <typename E, int D, typename Src>
+__device__ __forceinline__ void wave_tiles(Src&& src, const typename E::storage* Qg, int G, float scale_log2,
+                                           typename E::storage* lds, float& m_run, float& l_run,
+                                           f32x4 (&acc_o)[AttnTiling<E, D>::kDt]) {
+  using T = AttnTiling<E, D>;
+  constexpr int NCH = T::kChunks, EPL = T::kEpl, NDT = T::kDt;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  m_run = -INFINITY;
+  l_run = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  TileRegs<E, D> tr;
+  const typename E::storage *Kt = nullptr, *Vt = nullptr;
+  int nv = src(0, Kt, Vt);
+  if (nv <= 0) return;
+  tile_load_k<E, D>(Kt, nv, tr);
+  tile_load_v<E, D>(Vt, nv, tr);
+  u32x4 qf[NCH];
+  {
+    const typename E::storage* Qh = Qg + (size_t)min(n, G - 1) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
+  }
+  for (int j = 0; nv > 0; ++j) {
+    f32x4 sc4[4];
+    tile_scores<E, D>(tr, qf, sc4);
+    const typename E::storage *Kn = nullptr, *Vn = nullptr;
+    const int nv_next = src(j + 1, Kn, Vn);
+    if (nv_next > 0) tile_load_k<E, D>(Kn, nv_next, tr);
+    tile_stage_v<E, D>(tr, lds);
+    tile_softmax_pv<E, D>(sc4, nv, scale_log2, lds, m_run, l_run, acc_o);
+    if (nv_next > 0) tile_load_v<E, D>(Vn, nv_next, tr);
+    nv = nv_next;
+  }
+}
+
+template <typename E, int D, int NW>
+__host__ __device__ constexpr size_t attn_stage_bytes() {
+  return (size_t)NW * kBlock * AttnTiling<E, D>::kRowStride * E::kBytes;
+}
+
+// ---------------------------------------------------------------------------
+// Merge the workgroup's waves per branch slot in LDS and store one partial
+// (max, sum, O) per slot with sc1 stores; then the unit's last attention
+// workgroup combines every slot and writes the output.  wave_slot: the partial
+// slot this wave contributes to (-1: none).  my_slots[0..nmine): the slots this
+// workgroup owns (each is written, empty when no wave contributed).
+// ---------------------------------------------------------------------------
+template <typename E, int D, int NW>
+__device__ void merge_and_finish(const DecodeParams& p, int unit, int wave_slot, const int (&my_slots)[2], int nmine,
+                                 float m_run, float l_run, const f32x4 (&acc_o)[D / 16], unsigned char* smem,
+                                 int* flag) {
+  constexpr int NT = 64 * NW, NDT = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int seq = unit / p.hkv, head = unit % p.hkv;
+  const int G = p.group;
+  const int P = n_slots(p);
+
+  __syncthreads();                                   // every wave is done with its LDS slice
+  float* mo = reinterpret_cast<float*>(smem);        // [NW][16][D] then [NW][16][2], [NW] slots
+  float* mml = mo + (size_t)NW * 16 * D;
+  int* wslot = reinterpret_cast<int*>(mml + NW * 32);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mo[((size_t)wave * 16 + n) * D + 16 * dt + 4 * g + i] = acc_o[dt][i];
+  }
+  if (g == 0) { mml[(wave * 16 + n) * 2] = m_run; mml[(wave * 16 + n) * 2 + 1] = l_run; }
+  if (lane == 0) wslot[wave] = wave_slot;
+  __syncthreads();
+  const Coherent po(p.part_o + (size_t)unit * P * G * D, (uint32_t)(P * G * D * 4));
+  const Coherent pm(p.part_ml + (size_t)unit * P * 32, (uint32_t)(P * 32 * 4));
+  const int items = G * (D / 4);
+  for (int idx = threadIdx.x; idx < nmine * items; idx += NT) {
+    const int which = idx / items, r = idx % items;
+    const int slot = my_slots[which];
+    const int h = r / (D / 4), d4 = (r % (D / 4)) * 4;
+    float M = -INFINITY;
+    for (int w = 0; w < NW; ++w)
+      if (wslot[w] == slot) M = fmaxf(M, mml[(w * 16 + h) * 2]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float Ls = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < NW; ++w) {
+        const float mw = mml[(w * 16 + h) * 2];
+        if (wslot[w] != slot || mw == -INFINITY) continue;
+        const float f = fast_exp2(mw - M);
+        Ls += f * mml[(w * 16 + h) * 2 + 1];
+        const float* src = mo + ((size_t)w * 16 + h) * D + d4;
+        o[0] += f * src[0]; o[1] += f * src[1]; o[2] += f * src[2]; o[3] += f * src[3];
+      }
+    }
+    po.st4((uint32_t)(((slot * G + h) * D + d4) * 4), o);
+    if (d4 == 0) {
+      pm.st1((uint32_t)(((slot * 16 + h) * 2) * 4), M);
+      pm.st1((uint32_t)(((slot * 16 + h) * 2 + 1) * 4), Ls);
+    }
+  }
+
+  // ---- the last attention workgroup of this unit combines -----------------
+  if (!arrive_last(p.attn_counters + unit, (uint32_t)(p.has_lead + p.wg_slc + p.wg_wc), flag)) return;
+
+  // this thread's outputs (G*d/4 <= 512 float4, at most two per thread): the first
+  // 16 partials of each are fetched in the same round as every partial's (max, sum)
+  const int i0 = threadIdx.x, i1 = threadIdx.x + NT;
+  const bool has0 = i0 < items, has1 = NT < items && i1 < items;
+  const int h0 = has0 ? i0 / (D / 4) : 0, d0 = has0 ? (i0 % (D / 4)) * 4 : 0;
+  const int h1 = has1 ? i1 / (D / 4) : h0, d1 = has1 ? (i1 % (D / 4)) * 4 : d0;
+  f32x4 o0[16], o1[16];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = min(c0 + j, P - 1);
+      o0[j] = po.ld4((uint32_t)(((q * G + h0) * D + d0) * 4));
+      if (NT < 512) o1[j] = po.ld4((uint32_t)(((q * G + h1) * D + d1) * 4));
+    }
+  };
+  load_chunk(0);
+  float* sm = reinterpret_cast<float*>(smem);          // [P][16][2]
+  float* fac = sm + (size_t)P * 32;                    // [P][16]
+  for (int i = threadIdx.x; i < P * G; i += NT) {
+    const int q = i / G, h = i % G;
+    sm[(q * 16 + h) * 2] = pm.ld1((uint32_t)(((q * 16 + h) * 2) * 4));
+    sm[(q * 16 + h) * 2 + 1] = pm.ld1((uint32_t)(((q * 16 + h) * 2 + 1) * 4));
+  }
+  __syncthreads();
+  const int ns = slc_slots(p);
+  const int pb[4] = {0, ns, ns + p.wg_wc, P};        // SLC, WIN, CMP partial ranges
+  // merge factor of partial q for head h: gate / L_branch * 2^(m_q - M_branch)
+  for (int i = threadIdx.x; i < 3 * G; i += NT) {
+    const int br = i / G, h = i % G;
+    const int hq = head * G + h;
+    float gate = (br == 0) ? 1.f : 0.f;                 // gates absent: slc only
+    if (p.gates) gate = p.gates[((size_t)seq * p.hkv * G + hq) * 3 + (br == 0 ? 1 : br == 1 ? 2 : 0)];
+    const int q0 = pb[br], q1 = pb[br + 1];
+    float M = -INFINITY, Ls = 0.f;
+    for (int c0 = q0; c0 < q1; c0 += 16) {            // all reads of a chunk in flight together
+      float mv[16], lv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool ok = c0 + j < q1;
+        mv[j] = ok ? sm[((c0 + j) * 16 + h) * 2] : -INFINITY;
+        lv[j] = ok ? sm[((c0 + j) * 16 + h) * 2 + 1] : 0.f;
+      }
+      float Mc = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) if (lv[j] > 0.f) Mc = fmaxf(Mc, mv[j]);
+      if (Mc == -INFINITY) continue;
+      const float Mn = fmaxf(M, Mc);
+      Ls = (M == -INFINITY) ? 0.f : Ls * fast_exp2(M - Mn);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) if (lv[j] > 0.f) Ls += fast_exp2(mv[j] - Mn) * lv[j];
+      M = Mn;
+    }
+    const float inv = (Ls > 0.f) ? gate / Ls : 0.f;
+    for (int q = q0; q < q1; ++q) {
+      const float lq = sm[(q * 16 + h) * 2 + 1];
+      fac[q * 16 + h] = (lq > 0.f) ? inv * fast_exp2(sm[(q * 16 + h) * 2] - M) : 0.f;
+    }
+  }
+  __syncthreads();
+  // out[h][d] = sum_q fac[q][h] O_q[h][d]
+  f32x4 r0 = {0.f, 0.f, 0.f, 0.f}, r1 = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < P; c0 += 16) {
+    if (c0 > 0) load_chunk(c0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (c0 + j < P) {
+        r0 += fac[(c0 + j) * 16 + h0] * o0[j];
+        if (NT < 512) r1 += fac[(c0 + j) * 16 + h1] * o1[j];
+      }
+    }
+  }
+  if (has0) st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h0) * D + d0, r0);
+  if (has1) st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h1) * D + d1, r1);
+  if (threadIdx.x == 0) reset_counter(p.attn_counters + unit);
+  if (p.pub) {                                      // codes back to "not yet" for the next call
+    const Coherent pc(p.pub + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
+    for (int i = threadIdx.x; i < p.top_k; i += NT) pc.st1((uint32_t)(i * 4), 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scoring role.  Returns true in the lead (every thread), with the selection of
+// this unit in s_sel[0..top_k) (ascending, -1 padded) and the count in *n_sel.
+// ---------------------------------------------------------------------------
+template <typename E, int D, int KIND, int HV, int NW>
+__device__ bool select_role(const DecodeParams& p, int unit, int split, unsigned char* smem, int* s_sel,
+                            int* n_sel) {
+  constexpr int NT = 64 * NW;
+  SelLds<NW>& sl = *reinterpret_cast<SelLds<NW>*>(smem);
+  uint32_t* s_key = reinterpret_cast<uint32_t*>(smem + sizeof(SelLds<NW>));
   float* s_shat = reinterpret_cast<float*>(s_key + p.nb_pad);
+  float* s_raw = s_shat + p.nb_pad;                  // [nb_pad][16] when splits == 1
+  const bool in_lds = p.splits == 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int seq = unit / p.hkv, head = unit % p.hkv;
@@ -100,9 +322,10 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
 
   // ---- phase 1: scores of this workgroup's tiles -------------------------
   const int tiles_total = (ncand + 15) / 16;
-  const int tile0 = (split * 4 + wave) * p.sel_tpw;
+  const int tile0 = (split * NW + wave) * p.sel_tpw;
   float run_m = -INFINITY, run_s = 0.f;        // LSE partial of head n over this lane's blocks
-  // scores s4[i] of blocks tile*16 + 4g + i for head n: running LSE and block-major hand-off
+  // scores s4[i] of blocks tile*16 + 4g + i for head n: running LSE and the block-major
+  // raw scores (LDS with one scoring workgroup, the workspace otherwise)
   auto post = [&](int tile, const f32x4& s4, bool add_ln_n) {
     float sv[4];
     float mt = -INFINITY;
@@ -113,7 +336,10 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
       const float ln_n = !add_ln_n ? 0.f : (nbk == kBlock ? kLnBlock : __logf((float)nbk));
       sv[i] = (b < ncand) ? s4[i] + ln_n : -INFINITY;
       mt = fmaxf(mt, sv[i]);
-      if (n < G) sc.st1((uint32_t)((b * 16 + n) * 4), sv[i]);
+      if (n < G) {
+        if (in_lds) s_raw[b * 16 + n] = sv[i];
+        else sc.st1((uint32_t)((b * 16 + n) * 4), sv[i]);
+      }
     }
     const float mx = fmaxf(run_m, mt);          // one rescale per tile
     if (mx != -INFINITY) {
@@ -202,11 +428,12 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
     prepare_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
                                 W);
     if constexpr (Kind<KIND>::kSub) {
-      // scale * P q: the four waves each contract a quarter of the column tiles
+      // scale * P q: four waves split the column tiles and exchange them through LDS
+      // (waves 4.. repeat the first four and write the same values)
       const float* Ph = p.P + (size_t)head * p.sub_s * D;
-      subspace_weights_part<D>(Ph, p.sub_s, p.vlen, wave, 4, n, g, W.lin, sl.wsub_x, W.quad);
+      subspace_weights_part<D>(Ph, p.sub_s, p.vlen, wave & 3, 4, n, g, W.lin, sl.wsub_x, W.quad);
       __syncthreads();
-      subspace_weights_gather<D>(p.vlen, wave, 4, n, g, sl.wsub_x, W.quad);
+      subspace_weights_gather<D>(p.vlen, wave & 3, 4, n, g, sl.wsub_x, W.quad);
       finish_subspace_weights<E, D, KIND>(W);
     }
     for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
@@ -238,22 +465,27 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
   __syncthreads();
   if (threadIdx.x < 16) {
     float M = -INFINITY, S = 0.f;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float om = sl.red_m[w][threadIdx.x], os = sl.red_s[w][threadIdx.x];
       const float mx = fmaxf(M, om);
       if (mx != -INFINITY) { S = S * __expf(M - mx) + os * __expf(om - mx); M = mx; }
     }
-    const uint32_t o = (uint32_t)((split * 16 + threadIdx.x) * 2 * 4);
-    lp.st1(o, M);
-    lp.st1(o + 4, S);
+    if (in_lds) {
+      sl.lse_sh[threadIdx.x] = (M == -INFINITY) ? -INFINITY : M + __logf(S);
+    } else {
+      const uint32_t o = (uint32_t)((split * 16 + threadIdx.x) * 2 * 4);
+      lp.st1(o, M);
+      lp.st1(o + 4, S);
+    }
   }
 
   // ---- hand-off: the last scoring workgroup of this unit selects ----------
-  if (!arrive_last(p.sel_counters + unit, (uint32_t)p.splits, &sl.bcast[0])) return;
+  if (!in_lds && !arrive_last(p.sel_counters + unit, (uint32_t)p.splits, &sl.bcast[0])) return false;
 
-  // phase 2 is latency-bound: the first round of this thread's block scores and the
-  // LSE partials are fetched together, so both cost one memory round trip
-  const int per = (p.nb_max + kThreads - 1) / kThreads;
+  // phase 2 is latency-bound: with the scores in the workspace, the first round of
+  // this thread's block scores and the LSE partials are fetched together, so both
+  // cost one memory round trip
+  const int per = (p.nb_max + NT - 1) / NT;
   const int b0 = threadIdx.x * per;
   constexpr int kRound = 8 / HV;                                 // blocks per load round (8 float4)
   f32x4 raw[kRound][HV];
@@ -263,26 +495,32 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
       const int b = b0 + e0 + e;
       const bool ok = e0 + e < per && b < ncand;
 #pragma unroll
-      for (int v = 0; v < HV; ++v)
-        raw[e][v] = ok ? sc.ld4((uint32_t)((b * 16 + 4 * v) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < HV; ++v) {
+        if (in_lds) raw[e][v] = ok ? *reinterpret_cast<const f32x4*>(s_raw + b * 16 + 4 * v) : f32x4{0.f, 0.f, 0.f, 0.f};
+        else raw[e][v] = ok ? sc.ld4((uint32_t)((b * 16 + 4 * v) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   };
-  load_round(0);
-  for (int i = threadIdx.x; i < p.splits * 16; i += kThreads) {
-    sl.red_part[2 * i] = lp.ld1((uint32_t)(i * 8));
-    sl.red_part[2 * i + 1] = lp.ld1((uint32_t)(i * 8 + 4));
-  }
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    float M = -INFINITY, S = 0.f;
-    for (int x = 0; x < p.splits; ++x) {
-      const float om = sl.red_part[2 * (x * 16 + threadIdx.x)], os = sl.red_part[2 * (x * 16 + threadIdx.x) + 1];
-      const float mx = fmaxf(M, om);
-      if (mx != -INFINITY) { S = S * __expf(M - mx) + os * __expf(om - mx); M = mx; }
+  if (in_lds) {
+    __syncthreads();                              // raw scores and the LSE are in LDS
+  } else {
+    load_round(0);
+    for (int i = threadIdx.x; i < p.splits * 16; i += NT) {
+      sl.red_part[2 * i] = lp.ld1((uint32_t)(i * 8));
+      sl.red_part[2 * i + 1] = lp.ld1((uint32_t)(i * 8 + 4));
     }
-    sl.lse_sh[threadIdx.x] = (M == -INFINITY) ? -INFINITY : M + __logf(S);
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      float M = -INFINITY, S = 0.f;
+      for (int x = 0; x < p.splits; ++x) {
+        const float om = sl.red_part[2 * (x * 16 + threadIdx.x)], os = sl.red_part[2 * (x * 16 + threadIdx.x) + 1];
+        const float mx = fmaxf(M, om);
+        if (mx != -INFINITY) { S = S * __expf(M - mx) + os * __expf(om - mx); M = mx; }
+      }
+      sl.lse_sh[threadIdx.x] = (M == -INFINITY) ? -INFINITY : M + __logf(S);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- group scores: thread owns blocks [tid*per, tid*per + per) ------------
   float lse_r[4 * HV];
@@ -290,7 +528,7 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
   for (int h = 0; h < 4 * HV; ++h) lse_r[h] = (h < G) ? sl.lse_sh[h] : 0.f;
 #pragma unroll 1
   for (int e0 = 0; e0 < per; e0 += kRound) {
-    if (e0 > 0) load_round(e0);
+    if (e0 > 0 || in_lds) load_round(e0);
 #pragma unroll
     for (int e = 0; e < kRound; ++e) {
       const int b = b0 + e0 + e;
@@ -312,290 +550,224 @@ __device__ void select_role(const DecodeParams& p, int unit, int split, unsigned
   __syncthreads();
   if (p.sel_score) {
     float* ss = p.sel_score + (size_t)unit * p.nb_max;
-    for (int b = threadIdx.x; b < p.nb_max; b += kThreads) ss[b] = (b < ncand) ? s_shat[b] : -INFINITY;
+    for (int b = threadIdx.x; b < p.nb_max; b += NT) ss[b] = (b < ncand) ? s_shat[b] : -INFINITY;
   }
 
-  // ---- radix select; the selection (ascending, -1 padded) and, for waiting
-  // attention waves, its codes
-  const Coherent so(p.sel + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
-  const Coherent pc(p.pub ? static_cast<const void*>(p.pub + (size_t)unit * p.top_k) : static_cast<const void*>(p.sel),
+  // ---- radix select: the selection (ascending, -1 padded) to the caller, into LDS
+  // for the lead's own tiles, and as codes for the waiting selected-branch waves
+  int32_t* so = p.sel + (size_t)unit * p.top_k;
+  const Coherent pc(p.pub ? static_cast<const void*>(p.pub + (size_t)unit * p.top_k) : static_cast<const void*>(so),
                     (uint32_t)(p.top_k * 4));
-  const int sel_total = wg_select_topk(s_key, ncand, per, p.top_k, &sl.hist2[0][0][0], sl.scan_w,
-                                       [&](int pos, int b) {
-                                         so.st1((uint32_t)(pos * 4), __int_as_float(b));
-                                         if (p.pub) pc.st1((uint32_t)(pos * 4), __uint_as_float((uint32_t)(b + 2)));
-                                       });
-  for (int i = sel_total + (int)threadIdx.x; i < p.top_k; i += kThreads) {
-    so.st1((uint32_t)(i * 4), __int_as_float(-1));
-    if (p.pub) pc.st1((uint32_t)(i * 4), __uint_as_float(1u));
+  const int sel_total = wg_select_topk<NW>(s_key, ncand, per, p.top_k, &sl.hist2[0][0][0], sl.scan_w,
+                                           [&](int pos, int b) {
+                                             so[pos] = b;
+                                             s_sel[pos] = b;
+                                             if (p.pub && pos >= p.lead_tiles)
+                                               pc.st1((uint32_t)(pos * 4), __uint_as_float((uint32_t)(b + 2)));
+                                           });
+  for (int i = sel_total + (int)threadIdx.x; i < p.top_k; i += NT) {
+    so[i] = -1;
+    s_sel[i] = -1;
+    if (p.pub && i >= p.lead_tiles) pc.st1((uint32_t)(i * 4), __uint_as_float(1u));
   }
-  if (threadIdx.x == 0) reset_counter(p.sel_counters + unit);
+  if (!in_lds && threadIdx.x == 0) reset_counter(p.sel_counters + unit);
+  if (threadIdx.x == 0) *n_sel = sel_total;
+  __syncthreads();
+  return true;
 }
 
-// branch: 0 = SLC, 1 = WIN, 2 = CMP; slot = the workgroup's partial index in its unit.
-template <typename E, int D>
-__device__ void attn_role(const DecodeParams& p, int unit, int branch, int local, int slot,
-                          unsigned char* smem, int* flag) {
+// ---------------------------------------------------------------------------
+// The lead's share of the selected branch: tiles [0, lead_tiles) of the
+// selection in LDS, strided over the waves.
+// ---------------------------------------------------------------------------
+template <typename E, int D, int NW>
+__device__ void lead_attention(const DecodeParams& p, int unit, const int* s_sel, int n_sel, unsigned char* smem,
+                               int* flag) {
   using T = AttnTiling<E, D>;
-  constexpr int NCH = T::kChunks, EPL = T::kEpl, NDT = T::kDt;
-  constexpr int nw = kThreads / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
+  const int wave = threadIdx.x >> 6;
   const int seq = unit / p.hkv, head = unit % p.hkv;
   const int G = p.group;
   const int L = p.seq_lens[seq];
-  const int P = p.wg_slc + p.wg_win + p.wg_cmp;
+  const int nb = (L + kBlock - 1) / kBlock;
+  const int ntiles = min(p.lead_tiles, n_sel);
+  const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
+  const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)unit * p.max_len * D;
+  auto src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
+    const int t = wave + j * NW;
+    if (t >= ntiles) return 0;
+    const int b = s_sel[t];
+    if (b < 0 || b >= nb) return 0;
+    Kt = Ku + (size_t)b * kBlock * D;
+    Vt = Vu + (size_t)b * kBlock * D;
+    return min(kBlock, L - b * kBlock);
+  };
+  const typename E::storage* Qg = reinterpret_cast<const typename E::storage*>(p.Q) + ((size_t)seq * p.hkv * G + (size_t)head * G) * D;
+  typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
+  float m_run, l_run;
+  f32x4 acc_o[T::kDt];
+  wave_tiles<E, D>(src, Qg, G, p.scale_log2, lds, m_run, l_run, acc_o);
+  const int mine[2] = {0, 0};
+  merge_and_finish<E, D, NW>(p, unit, 0, mine, 1, m_run, l_run, acc_o, smem, flag);
+}
 
+// ---------------------------------------------------------------------------
+// Window and pooled-token workgroups (`local` of wg_wc per unit): the unit's waves
+// split between the two branches so that the longest run of tiles is shortest,
+// then each wave takes an even share of its branch's tiles.
+// ---------------------------------------------------------------------------
+template <typename E, int D, int NW>
+__device__ void wc_attention(const DecodeParams& p, int unit, int local, unsigned char* smem, int* flag) {
+  using T = AttnTiling<E, D>;
+  const int wave = threadIdx.x >> 6;
+  const int seq = unit / p.hkv, head = unit % p.hkv;
+  const int G = p.group;
+  const int L = p.seq_lens[seq];
+  const int nc = (p.cmp_on && L >= 32) ? (L - 32) / 16 + 1 : 0;
+  const int win_len = min(p.window, L);
+  const int win_start = L - win_len;
+  const int t_win = (win_len + kBlock - 1) / kBlock, t_cmp = (nc + kBlock - 1) / kBlock;
+  const int waves = p.wg_wc * NW;
+  int nw_win = 0;
+  if (t_win > 0 && t_cmp == 0) {
+    nw_win = waves;
+  } else if (t_win > 0) {
+    int best = 1 << 30;
+    for (int a = 1; a < waves; ++a) {
+      const int c = max((t_win + a - 1) / a, (t_cmp + waves - a - 1) / (waves - a));
+      if (c < best) { best = c; nw_win = a; }
+    }
+  }
+  const int gw = local * NW + wave;
+  const bool is_win = gw < nw_win;
+  const int nwb = is_win ? nw_win : waves - nw_win;          // waves of this branch
+  const int idx = is_win ? gw : gw - nw_win;
+  const int tb = is_win ? t_win : t_cmp;
+  const int j0 = (int)((int64_t)idx * tb / max(nwb, 1)), j1 = (int)((int64_t)(idx + 1) * tb / max(nwb, 1));
   const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
   const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)unit * p.max_len * D;
   const typename E::storage* kcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.kc) + (size_t)unit * p.nc_max * D : nullptr;
   const typename E::storage* vcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.vc) + (size_t)unit * p.nc_max * D : nullptr;
-  const int nb = (L + kBlock - 1) / kBlock;
-  const int nc = (p.cmp_on && L >= 32) ? (L - 32) / 16 + 1 : 0;
-  const int win_len = min(p.window, L);
-  const int win_start = L - win_len;
-
-  // Source rows of this wave's j-th tile; returns the number of valid keys (0:
-  // none).  Selected blocks come from the published codes (polled, bounded) or
-  // the caller's selection; every block index is bounds-checked.
-  auto tile_src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
-    const int tpw = branch == 0 ? p.tpw_slc : p.tpw;       // tiles per wave of this branch
-    if (j >= tpw) return 0;
-    const int tile = (local * nw + wave) * tpw + j;
-    if (branch == 0) {
-      if (tile >= p.top_k) return 0;
-      int b = -1;
-      if (p.wait_ready) {
-        const Coherent pc(p.pub + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
-        uint32_t code = 0;
-        for (uint32_t it = 0; it < kSpinCap; ++it) {
-          code = __float_as_uint(pc.ld1((uint32_t)(tile * 4)));
-          if (code != 0u) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-        b = (code >= 2u) ? (int)(code - 2u) : -1;
-      } else {
-        const Coherent si(p.sel_attn + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
-        b = __float_as_int(si.ld1((uint32_t)(tile * 4)));
-      }
-      if (b < 0 || b >= nb) return 0;
-      Kt = Ku + (size_t)b * kBlock * D;
-      Vt = Vu + (size_t)b * kBlock * D;
-      return min(kBlock, L - b * kBlock);
-    }
-    if (branch == 1) {
-      const int start = win_start + tile * kBlock;
-      if (start >= L) return 0;
+  auto src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
+    const int t = j0 + j;
+    if (t >= j1) return 0;
+    if (is_win) {
+      const int start = win_start + t * kBlock;
       Kt = Ku + (size_t)start * D;
       Vt = Vu + (size_t)start * D;
       return min(kBlock, L - start);
     }
-    const int start = tile * kBlock;
-    if (start >= nc) return 0;
+    const int start = t * kBlock;
     Kt = kcu + (size_t)start * D;
     Vt = vcu + (size_t)start * D;
     return min(kBlock, nc - start);
   };
-
+  const typename E::storage* Qg = reinterpret_cast<const typename E::storage*>(p.Q) + ((size_t)seq * p.hkv * G + (size_t)head * G) * D;
   typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc_o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run, l_run;
+  f32x4 acc_o[T::kDt];
+  wave_tiles<E, D>(src, Qg, G, p.scale_log2, lds, m_run, l_run, acc_o);
+  const int ns = slc_slots(p);
+  const int mine[2] = {ns + local, ns + p.wg_wc + local};
+  const int wslot = j1 > j0 ? (is_win ? mine[0] : mine[1]) : -1;
+  merge_and_finish<E, D, NW>(p, unit, wslot, mine, 2, m_run, l_run, acc_o, smem, flag);
+}
 
-  // Software pipeline over the wave's tiles (valid tiles form a prefix): the next
-  // tile's K loads go out once this tile's scores are formed (overlapping the
-  // softmax and P V), its V loads after P V (overlapping the next scores).
-  TileRegs<E, D> tr;
-  const typename E::storage *Kt = nullptr, *Vt = nullptr;
-  int nv = tile_src(0, Kt, Vt);
-  if (nv > 0) {
-    tile_load_k<E, D>(Kt, nv, tr);
-    tile_load_v<E, D>(Vt, nv, tr);
-  }
-  // The group's queries as the B operand of S = K Q^T, requested after the first
-  // tile so that no round trip precedes the tile loads.  Columns n >= G repeat
-  // head G-1: their scores and outputs stay in their own columns and are never
-  // merged or written.
-  u32x4 qf[NCH];
-  {
-    const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
-                                    ((size_t)seq * p.hkv * G + (size_t)head * G + min(n, G - 1)) * D;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
-  }
-  for (int j = 0; nv > 0; ++j) {
-    f32x4 sc4[4];
-    tile_scores<E, D>(tr, qf, sc4);
-    const typename E::storage *Kn = nullptr, *Vn = nullptr;
-    const int nv_next = tile_src(j + 1, Kn, Vn);
-    if (nv_next > 0) tile_load_k<E, D>(Kn, nv_next, tr);
-    tile_stage_v<E, D>(tr, lds);
-    tile_softmax_pv<E, D>(sc4, nv, p.scale_log2, lds, m_run, l_run, acc_o);
-    if (nv_next > 0) tile_load_v<E, D>(Vn, nv_next, tr);
-    nv = nv_next;
-  }
-
-  // ---- merge the waves of this workgroup in LDS ----------------------------
-  __syncthreads();
-  float* mo = reinterpret_cast<float*>(smem);        // [nw][16][D] then [nw][16][2]
-  float* mml = mo + (size_t)nw * 16 * D;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mo[((size_t)wave * 16 + n) * D + 16 * dt + 4 * g + i] = acc_o[dt][i];
-  }
-  if (g == 0) { mml[(wave * 16 + n) * 2] = m_run; mml[(wave * 16 + n) * 2 + 1] = l_run; }
-  __syncthreads();
-  const Coherent po(p.part_o + (size_t)unit * P * G * D, (uint32_t)(P * G * D * 4));
-  const Coherent pm(p.part_ml + (size_t)unit * P * 32, (uint32_t)(P * 32 * 4));
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += kThreads) {
-    const int h = idx / (D / 4), d4 = (idx % (D / 4)) * 4;
-    float M = -INFINITY;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, mml[(w * 16 + h) * 2]);
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    float Ls = 0.f;
-    if (M != -INFINITY) {
-      for (int w = 0; w < nw; ++w) {
-        const float mw = mml[(w * 16 + h) * 2];
-        if (mw == -INFINITY) continue;
-        const float f = fast_exp2(mw - M);
-        Ls += f * mml[(w * 16 + h) * 2 + 1];
-        const float* src = mo + ((size_t)w * 16 + h) * D + d4;
-        o[0] += f * src[0]; o[1] += f * src[1]; o[2] += f * src[2]; o[3] += f * src[3];
+// ---------------------------------------------------------------------------
+// Selected-branch workgroups beyond the lead's share (`local` of wg_slc): tile
+// t = lead_tiles + local * NW * tpw_slc + j * NW + wave.  With a lead the block
+// comes from its published code (polled, bounded); otherwise from the caller's
+// selection.
+// ---------------------------------------------------------------------------
+template <typename E, int D, int NW>
+__device__ void slc_attention(const DecodeParams& p, int unit, int local, unsigned char* smem, int* flag) {
+  using T = AttnTiling<E, D>;
+  const int wave = threadIdx.x >> 6;
+  const int seq = unit / p.hkv, head = unit % p.hkv;
+  const int G = p.group;
+  const int L = p.seq_lens[seq];
+  const int nb = (L + kBlock - 1) / kBlock;
+  const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
+  const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)unit * p.max_len * D;
+  bool gave_up = false;
+  auto src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
+    if (j >= p.tpw_slc) return 0;
+    const int t = p.lead_tiles + local * NW * p.tpw_slc + j * NW + wave;
+    if (t >= p.top_k) return 0;
+    int b = -1;
+    if (p.pub) {
+      const Coherent pc(p.pub + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
+      uint32_t code = 0;
+      for (uint32_t it = 0; it < p.poll_cap; ++it) {
+        code = __float_as_uint(pc.ld1((uint32_t)(t * 4)));
+        if (code != 0u) break;
+        __builtin_amdgcn_s_sleep(1);
       }
+      if (code == 0u) gave_up = true;
+      b = (code >= 2u) ? (int)(code - 2u) : -1;
+    } else {
+      const Coherent si(p.sel_in + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
+      b = __float_as_int(si.ld1((uint32_t)(t * 4)));
     }
-    po.st4((uint32_t)(((slot * G + h) * D + d4) * 4), o);
-    if (d4 == 0) {
-      pm.st1((uint32_t)(((slot * 16 + h) * 2) * 4), M);
-      pm.st1((uint32_t)(((slot * 16 + h) * 2 + 1) * 4), Ls);
-    }
-  }
-
-  // ---- the last attention workgroup of this unit combines -----------------
-  if (!arrive_last(p.attn_counters + unit, (uint32_t)P, flag)) return;
-
-  // this thread's two outputs (G*d/4 <= 512 float4): the first 16 partials of each
-  // are fetched in the same round as every partial's (max, sum)
-  const int items = G * (D / 4);
-  const int i0 = threadIdx.x, i1 = threadIdx.x + kThreads;
-  const bool has0 = i0 < items, has1 = i1 < items;
-  const int h0 = has0 ? i0 / (D / 4) : 0, d0 = has0 ? (i0 % (D / 4)) * 4 : 0;
-  const int h1 = has1 ? i1 / (D / 4) : h0, d1 = has1 ? (i1 % (D / 4)) * 4 : d0;
-  f32x4 o0[16], o1[16];
-  auto load_chunk = [&](int c0) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int q = min(c0 + j, P - 1);
-      o0[j] = po.ld4((uint32_t)(((q * G + h0) * D + d0) * 4));
-      o1[j] = po.ld4((uint32_t)(((q * G + h1) * D + d1) * 4));
-    }
+    if (b < 0 || b >= nb) return 0;
+    Kt = Ku + (size_t)b * kBlock * D;
+    Vt = Vu + (size_t)b * kBlock * D;
+    return min(kBlock, L - b * kBlock);
   };
-  load_chunk(0);
-  float* sm = reinterpret_cast<float*>(smem);          // [P][16][2]
-  float* fac = sm + (size_t)P * 32;                    // [P][16]
-  for (int i = threadIdx.x; i < P * G; i += kThreads) {
-    const int q = i / G, h = i % G;
-    sm[(q * 16 + h) * 2] = pm.ld1((uint32_t)(((q * 16 + h) * 2) * 4));
-    sm[(q * 16 + h) * 2 + 1] = pm.ld1((uint32_t)(((q * 16 + h) * 2 + 1) * 4));
-  }
-  __syncthreads();
-  const int pb[4] = {0, p.wg_slc, p.wg_slc + p.wg_win, P};   // SLC, WIN, CMP partial ranges
-  // merge factor of partial q for head h: gate / L_branch * 2^(m_q - M_branch)
-  for (int i = threadIdx.x; i < 3 * G; i += kThreads) {
-    const int br = i / G, h = i % G;
-    const int hq = head * G + h;
-    float gate = (br == 0) ? 1.f : 0.f;                 // gates absent: slc only
-    if (p.gates) gate = p.gates[((size_t)seq * p.hkv * G + hq) * 3 + (br == 0 ? 1 : br == 1 ? 2 : 0)];
-    const int q0 = pb[br], q1 = pb[br + 1];
-    float M = -INFINITY, Ls = 0.f;
-    for (int c0 = q0; c0 < q1; c0 += 16) {            // all reads of a chunk in flight together
-      float mv[16], lv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool ok = c0 + j < q1;
-        mv[j] = ok ? sm[((c0 + j) * 16 + h) * 2] : -INFINITY;
-        lv[j] = ok ? sm[((c0 + j) * 16 + h) * 2 + 1] : 0.f;
-      }
-      float Mc = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) if (lv[j] > 0.f) Mc = fmaxf(Mc, mv[j]);
-      if (Mc == -INFINITY) continue;
-      const float Mn = fmaxf(M, Mc);
-      Ls = (M == -INFINITY) ? 0.f : Ls * fast_exp2(M - Mn);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) if (lv[j] > 0.f) Ls += fast_exp2(mv[j] - Mn) * lv[j];
-      M = Mn;
-    }
-    const float inv = (Ls > 0.f) ? gate / Ls : 0.f;
-    for (int q = q0; q < q1; ++q) {
-      const float lq = sm[(q * 16 + h) * 2 + 1];
-      fac[q * 16 + h] = (lq > 0.f) ? inv * fast_exp2(sm[(q * 16 + h) * 2] - M) : 0.f;
-    }
-  }
-  __syncthreads();
-  // out[h][d] = sum_q fac[q][h] O_q[h][d]
-  f32x4 r0 = {0.f, 0.f, 0.f, 0.f}, r1 = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < P; c0 += 16) {
-    if (c0 > 0) load_chunk(c0);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (c0 + j < P) {
-        r0 += fac[(c0 + j) * 16 + h0] * o0[j];
-        r1 += fac[(c0 + j) * 16 + h1] * o1[j];
-      }
-    }
-  }
-  if (has0) st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h0) * D + d0, r0);
-  if (has1) st_f32x4(p.out + ((size_t)seq * p.hkv * G + head * G + h1) * D + d1, r1);
-  if (threadIdx.x == 0) reset_counter(p.attn_counters + unit);
-  if (p.wait_ready) {                               // codes back to "not yet" for the next call
-    const Coherent pc(p.pub + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
-    for (int i = threadIdx.x; i < p.top_k; i += kThreads) pc.st1((uint32_t)(i * 4), 0.f);
-  }
+  const typename E::storage* Qg = reinterpret_cast<const typename E::storage*>(p.Q) + ((size_t)seq * p.hkv * G + (size_t)head * G) * D;
+  typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
+  float m_run, l_run;
+  f32x4 acc_o[T::kDt];
+  wave_tiles<E, D>(src, Qg, G, p.scale_log2, lds, m_run, l_run, acc_o);
+  if (gave_up && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int mine[2] = {p.has_lead + local, 0};
+  merge_and_finish<E, D, NW>(p, unit, mine[0], mine, 1, m_run, l_run, acc_o, smem, flag);
 }
-
-template <typename E, int D, int KIND, int HV>
-__global__ __launch_bounds__(kThreads, E::kBytes * D <= 256 ? 2 : 1) void k_decode(DecodeParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int flag;
-  const int i = blockIdx.x;
-  if (i < p.sel_wgs) {
-    select_role<E, D, KIND, HV>(p, i / p.splits, i % p.splits, smem);
-    return;
-  }
-  const int j = i - p.sel_wgs;
-  int unit, branch, local, slot;
-  if (j < p.wc_wgs) {
-    const int per_unit = p.wg_win + p.wg_cmp;
-    unit = j / per_unit;
-    const int l = j % per_unit;
-    branch = l < p.wg_win ? 1 : 2;
-    local = l < p.wg_win ? l : l - p.wg_win;
-    slot = p.wg_slc + l;
-  } else {
-    const int k = j - p.wc_wgs;
-    unit = k / p.wg_slc;
-    branch = 0;
-    local = slot = k % p.wg_slc;
-  }
-  attn_role<E, D>(p, unit, branch, local, slot, smem, &flag);
-}
-
-size_t select_lds_bytes(int nb_pad) { return sizeof(SelLds) + (size_t)nb_pad * 8; }
 
 template <typename E, int D>
-size_t attn_role_lds_bytes(int P) {
-  return std::max(attn_lds_bytes<E, D>(kThreads / 64), (size_t)P * 48 * sizeof(float));
+constexpr int waves_of() { return (E::kBytes == 4 && D == 128) ? 4 : 8; }
+
+template <typename E, int D, int KIND, int HV>
+__global__ __launch_bounds__((64 * waves_of<E, D>()), 1) void k_decode(DecodeParams p) {
+  constexpr int NW = waves_of<E, D>();
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int flag;
+  __shared__ int s_sel[64];
+  __shared__ int n_sel;
+  const int i = blockIdx.x;
+  if (i < p.sel_wgs) {
+    if (!select_role<E, D, KIND, HV, NW>(p, i / p.splits, i % p.splits, smem, s_sel, &n_sel)) return;
+    if constexpr (KIND != 2) {
+      if (p.has_lead) lead_attention<E, D, NW>(p, i / p.splits, s_sel, n_sel, smem, &flag);
+    }
+    return;
+  }
+  if constexpr (KIND != 2) {
+    const int j = i - p.sel_wgs;
+    if (j < p.wc_wgs) {
+      wc_attention<E, D, NW>(p, j / p.wg_wc, j % p.wg_wc, smem, &flag);
+    } else {
+      const int k = j - p.wc_wgs;
+      slc_attention<E, D, NW>(p, k / p.wg_slc, k % p.wg_slc, smem, &flag);
+    }
+  }
+}
+
+template <typename E, int D>
+static size_t attn_role_lds_bytes(int P) {
+  constexpr int NW = waves_of<E, D>();
+  const size_t merge = (size_t)NW * 16 * (D + 2) * sizeof(float) + NW * sizeof(int);
+  return std::max(std::max(attn_stage_bytes<E, D, NW>(), merge), (size_t)P * 48 * sizeof(float));
 }
 
 template <typename E, int D, int KIND, int HV>
 static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeParams& dp) {
+  constexpr int NW = waves_of<E, D>();
   const int total = dp.sel_wgs + dp.wc_wgs + dp.slc_wgs;
   size_t lds = 0;
-  if (dp.sel_wgs) lds = std::max(lds, select_lds_bytes(dp.nb_pad));
-  if (dp.wc_wgs + dp.slc_wgs) lds = std::max(lds, attn_role_lds_bytes<E, D>(dp.wg_slc + dp.wg_win + dp.wg_cmp));
-  hipLaunchKernelGGL((k_decode<E, D, KIND, HV>), dim3(total), dim3(kThreads), lds, a.stream, dp);
+  if (dp.sel_wgs) lds = std::max(lds, select_lds_bytes<NW>(dp.nb_pad, dp.splits == 1));
+  if (dp.do_attn) lds = std::max(lds, attn_role_lds_bytes<E, D>(dp.has_lead + dp.wg_slc + 2 * dp.wg_wc));
+  hipLaunchKernelGGL((k_decode<E, D, KIND, HV>), dim3(total), dim3(64 * NW), lds, a.stream, dp);
   return hipGetLastError();
 }
 
@@ -632,6 +804,13 @@ static hipError_t launch_decode_ed(const DecodeArgs& a, const DecodeParams& dp) 
   return launch_decode_t<E, D, 1, 4>(a, dp);
 }
 
+int decode_waves(bool bf16, int head_dim) { return (!bf16 && head_dim == 128) ? 4 : 8; }
+
+size_t decode_select_lds_bytes(bool bf16, int head_dim, int nb_pad, bool raw_in_lds) {
+  return decode_waves(bf16, head_dim) == 8 ? select_lds_bytes<8>(nb_pad, raw_in_lds)
+                                           : select_lds_bytes<4>(nb_pad, raw_in_lds);
+}
+
 hipError_t launch_decode(const DecodeArgs& a) {
   DecodeParams p;
   const int units = a.batch * a.hkv;
@@ -639,17 +818,22 @@ hipError_t launch_decode(const DecodeArgs& a) {
   p.nb_pad = (a.nb_max + 15) / 16 * 16; p.top_k = a.top_k; p.seq_lens = a.seq_lens; p.Q = a.Q;
   p.sel_wgs = a.do_select ? units * a.splits : 0;
   p.splits = a.splits; p.sel_tpw = a.sel_tpw; p.rank = a.rank; p.alpha = a.alpha; p.scale = a.scale;
-  p.mu = a.mu; p.so = a.so; p.P = a.P; p.sub_s = a.sub_s; p.vlen = a.vlen; p.sel = a.sel; p.sel_score = a.sel_score; p.sel_counters = a.sel_counters;
-  p.scores = a.scores; p.lse_part = a.lse_part;
-  p.pub = (a.do_select && a.do_attn) ? a.ready : nullptr;
-  p.wc_wgs = a.do_attn ? units * (a.wg_win + a.wg_cmp) : 0;
-  p.slc_wgs = a.do_attn ? units * a.wg_slc : 0;
-  p.nc_max = a.nc_max; p.window = a.window; p.cmp_on = a.cmp_on; p.tpw = a.tpw_wc; p.tpw_slc = a.tpw_slc;
-  p.wg_slc = a.wg_slc; p.wg_win = a.wg_win; p.wg_cmp = a.wg_cmp; p.scale_log2 = a.scale * kLog2e;
+  p.mu = a.mu; p.so = a.so; p.P = a.P; p.sub_s = a.sub_s; p.vlen = a.vlen; p.sel = a.sel; p.sel_score = a.sel_score;
+  p.sel_counters = a.sel_counters; p.scores = a.scores; p.lse_part = a.lse_part;
+  p.do_attn = a.do_attn ? 1 : 0;
+  p.has_lead = (a.do_select && a.do_attn) ? 1 : 0;
+  p.lead_tiles = p.has_lead ? a.lead_tiles : 0;
+  p.wg_slc = a.do_attn ? a.wg_slc : 0;
+  p.wg_wc = a.do_attn ? a.wg_wc : 0;
+  p.pub = (p.has_lead && p.wg_slc > 0) ? a.ready : nullptr;
+  p.wc_wgs = units * p.wg_wc;
+  p.slc_wgs = units * p.wg_slc;
+  p.nc_max = a.nc_max; p.window = a.window; p.cmp_on = a.cmp_on; p.tpw_slc = a.tpw_slc;
+  p.scale_log2 = a.scale * kLog2e;
   p.K = a.K; p.V = a.V; p.kc = a.kc; p.vc = a.vc; p.gates = a.gates;
-  p.sel_attn = a.do_select ? a.sel : a.sel_in;
-  p.wait_ready = (a.do_select && a.do_attn) ? 1 : 0;
+  p.sel_in = a.sel_in;
   p.out = a.out; p.attn_counters = a.attn_counters; p.part_ml = a.part_ml; p.part_o = a.part_o;
+  p.status = a.status; p.poll_cap = a.poll_cap;
   if (a.bf16) return a.head_dim == 128 ? launch_decode_ed<EltBF16, 128>(a, p) : launch_decode_ed<EltBF16, 64>(a, p);
   return a.head_dim == 128 ? launch_decode_ed<EltF32, 128>(a, p) : launch_decode_ed<EltF32, 64>(a, p);
 }

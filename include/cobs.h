@@ -215,7 +215,29 @@ cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t
                                     const int32_t* sel_in, int32_t* sel_out, float* out,
                                     void* ws, size_t ws_bytes, void* stream);
 
-/* Chunked causal prefill of one sequence: queries at t = q_pos0 .. q_pos0+n_q_tokens-1
+/* Status of the decode steps run on a workspace since the last query (host,
+ * synchronous: waits for `stream`, then reads and clears the workspace's status word).
+ * A decode step whose selected-branch workgroups wait for the selection published by
+ * the unit's selecting workgroup bounds that wait (about 0.1 s of polling); a wave that
+ * gives up attends to no block for that tile, so the step's output is incomplete, and
+ * sets bit 0 of *flags (COBS_STATUS_WAIT_GAVE_UP).  *flags == 0 means every step since
+ * the last query completed as specified.
+ *   p, batch, max_len, ws, ws_bytes  as passed to cobs_sparse_attn_decode
+ *   flags   host out
+ * Errors: INVALID_ARG (null ws or flags, bad sizes), WORKSPACE, HIP. */
+#define COBS_STATUS_WAIT_GAVE_UP 1u
+cobs_status cobs_decode_status(const cobs_params* p, int32_t batch, int32_t max_len, void* ws, size_t ws_bytes,
+                               uint32_t* flags, void* stream);
+
+/* Test hook: polls of one published selection code before a selected-branch wave gives
+ * up, for every later decode call of this process (0 = give up at once, which makes a
+ * step whose selected workgroups must wait report COBS_STATUS_WAIT_GAVE_UP;
+ * 0xFFFFFFFF restores the default).  Not for production use. */
+void cobs_set_poll_limit(uint32_t polls);
+
+/* Chunked causal prefill of one sequence (NSA's three paths with the COBS selector at
+ * every query position: COBS Technisches Resuemee 2.1-2.3 and the skill card
+ * "Implementation steps"; causal candidates as in cobs_select_topk): queries at t = q_pos0 .. q_pos0+n_q_tokens-1
  * against a KV prefix of seq_len positions whose summaries were built once over
  * all seq_len keys; per (token, kv-head group) selection over the candidate blocks
  * of that token, then the three branches and the gated combine.

@@ -176,3 +176,17 @@ def test_query_subspace_rejects_bad_calls():
     assert lib.cobs_query_subspace(ctypes.byref(p), 10, fake, fake, fake, n, None) == B.COBS_ERR_INVALID_ARG
     p.subspace_dim, p.so_kind, p.rank = 16, B.COBS_SO_DIAG, 0
     assert lib.cobs_query_subspace(ctypes.byref(p), 10, fake, fake, fake, n, None) == B.COBS_ERR_INVALID_ARG
+
+
+def test_decode_status_argument_checks_on_the_host():
+    p = good()
+    flags = ctypes.c_uint32()
+    assert B.lib().cobs_decode_status(ctypes.byref(p), 1, 1024, None, 0, None, None) == B.COBS_ERR_INVALID_ARG
+    assert B.lib().cobs_decode_status(ctypes.byref(p), 1, 1024, None, 64, ctypes.byref(flags),
+                                      None) == B.COBS_ERR_INVALID_ARG
+    assert B.lib().cobs_decode_status(ctypes.byref(p), 1, 1024, None, 0, ctypes.byref(flags),
+                                      None) == B.COBS_ERR_INVALID_ARG
+    ws_bytes = B.cobs_workspace_bytes(p, 1, 1024)
+    buf = ctypes.create_string_buffer(16)
+    assert B.lib().cobs_decode_status(ctypes.byref(p), 1, 1024, buf, ws_bytes - 1, ctypes.byref(flags),
+                                      None) == B.COBS_ERR_WORKSPACE

@@ -73,6 +73,7 @@ def check_fp4(w, x, s, units=None, gap_min=1e-2):
     units = units or [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
     strict = loose = exempt = total = mu_equal = mu_total = 0
     for (b, h) in units:
+        print(f"[test] compressed summaries of unit ({b}, {h})", flush=True)
         L = int(x["lens"][b])
         keys = x["K"][b, h, :L].astype(np.float64)
         Ph = None if not w.subspace else x["P"][h].astype(np.float64)
@@ -172,18 +173,23 @@ def test_update_fp4():
     untouched_equal(s, before, old_lens, w)
 
 
-def test_full_size_long_decode_fp4_sampled():
+def test_full_size_long_decode_fp4(long_inputs, long_oracle_lowrank):
+    """8 x 128k with the compressed storage: codes, exponents and means of 4 units,
+    selections of 16 units over all 8 sequences and every kv head, outputs where the
+    gap is unambiguous.  The oracle's compressed summaries are its fp64 rank-4
+    summaries rounded (bf16 mean, MX FP4 vectors), as its summary builder does."""
+    from tests.test_gpu_parity import check_long_units
     w = synth.WORKLOADS["decode_b8_L128k_rank4_fp4"]
-    x = synth.make_inputs(w, 4)
+    _, x = long_inputs
+    x = dict(x, workload=w)
     p = U.params_for(w)
     g = U.to_device(x)
     s = U.build(p, g)
-    check_fp4(w, x, s, units=[(7, 5)])
+    check_fp4(w, x, s, units=[(0, 0), (3, 1), (7, 5), (5, 3)])
     out, sel = U.decode(p, g, s)
-    G = w.group
-    for (b, h) in [(0, 0), (7, 7)]:
-        o_out, o_sel, shat, gap = O.run(x, O.params_of(w), seqs=[b], groups=[h])[(b, h, 0)]
-        ok, msg = U.selection_ok(sel[b, h], shat, w.top_k)
-        assert ok, f"seq {b} group {h}: {msg}"
-        if gap >= U.GAP:
-            assert np.abs(out[b, h * G:(h + 1) * G] - o_out).max() <= 1e-2
+    units = {}
+    for key, ((mu, so, n), kc, vc) in long_oracle_lowrank.items():
+        qmu = O.round_bf16(mu)
+        qso = np.array([[O.quantize_dequantize_padded(v) for v in blk] for blk in so])
+        units[key] = ((qmu, qso, n), kc, vc)
+    check_long_units(w, x, out, sel, units, O.params_of(w))

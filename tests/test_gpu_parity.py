@@ -176,6 +176,27 @@ def test_decode_tiny_f32():
         assert worst < 1e-4
 
 
+def test_decode_f32_d128():
+    """fp32 inputs at d = 128 (four-wave workgroups: the attention tile then needs a
+    SIMD's whole register file)."""
+    w = W("f32d128", batch=2, max_len=2500, min_len=900, n_q_heads=16, n_kv_heads=2, head_dim=128, top_k=8,
+          window=200, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0, dtype="f32", needles=2)
+    x = synth.make_inputs(w, 23, lens=np.array([2500, 900]))
+    worst = run_and_check(w, x, out_tol=1e-4)
+    assert worst <= 1e-4
+
+
+@pytest.mark.parametrize("L", [200000, 262144])
+def test_decode_beyond_2048_blocks(L):
+    """Contexts of 3125 and 4096 blocks (the most the library accepts): the scoring is
+    split over several workgroups whose block scores are handed off through the
+    workspace."""
+    w = W("long1", batch=1, max_len=L, min_len=L, n_q_heads=8, n_kv_heads=1, head_dim=128, top_k=16,
+          window=512, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0, alpha=1.0, dtype="bf16", needles=4)
+    x = synth.make_inputs(w, 24)
+    run_and_check(w, x)
+
+
 def test_decode_single_block_and_tiny_lengths():
     name = "g2_d64_bf16_nocmp"
     w = W(name, **dict(SMALL[name], window=16, max_len=70))
@@ -247,12 +268,77 @@ def batched_inputs():
     return w, synth.make_inputs(w, 2)
 
 
-@pytest.mark.parametrize("alpha", [1.0, 0.0])
-def test_full_size_batched_decode_sampled(alpha, batched_inputs):
+@pytest.fixture(scope="module")
+def batched_device(batched_inputs):
+    """The batch on the GPU and its summaries (the summaries do not depend on alpha)."""
     w, x = batched_inputs
-    lens = x["lens"]
-    seqs = sorted({0, int(np.argmin(lens)), int(np.argmax(lens)), w.batch - 1})
-    run_and_check(w, x, alpha=alpha, seqs=seqs)
+    g = U.to_device(x)
+    s = U.build(U.params_for(w), g)
+    return g, s
+
+
+@pytest.fixture(scope="module")
+def batched_oracle(batched_inputs):
+    """The oracle's summaries and pooled tokens of every (sequence, kv-head)."""
+    w, x = batched_inputs
+    p = O.params_of(w)
+    units = {}
+    for b in range(w.batch):
+        L = int(x["lens"][b])
+        print(f"[fixture] oracle summaries of sequence {b}", flush=True)
+        for h in range(w.n_kv_heads):
+            units[(b, h)] = O.build_unit(p, x["K"][b, h, :L].astype(np.float64),
+                                         x["V"][b, h, :L].astype(np.float64), L)
+    return units
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0, 2.0])
+def test_full_size_batched_decode_all_units(alpha, batched_inputs, batched_device, batched_oracle):
+    """Batch 32, lengths 16k-32k, in the launch configuration the benchmark times:
+    the selection of every (sequence, kv-head) by the gap rule at each alpha; at
+    alpha = 1 every output too, where the gap is unambiguous from the fused step and
+    everywhere from the attention path fed with the oracle's own selection."""
+    w, x = batched_inputs
+    g, s = batched_device
+    p = U.params_for(w, alpha=alpha)
+    out, sel = U.decode(p, g, s)
+    op = O.params_of(w, alpha=alpha)
+    G = w.group
+    oracle_sel = np.full_like(sel, -1)
+    oracle_out = {}
+    outs = 0
+    for b in range(w.batch):
+        L = int(x["lens"][b])
+        for h in range(w.n_kv_heads):
+            summ, kc, vc = batched_oracle[(b, h)]
+            qg = x["Q"][b, 0, h * G:(h + 1) * G].astype(np.float64)
+            if alpha == 1.0:
+                keys = x["K"][b, h, :L].astype(np.float64)
+                vals = x["V"][b, h, :L].astype(np.float64)
+                gt = x["gates"][b, 0, h * G:(h + 1) * G].astype(np.float64)
+                o_out, o_sel, shat, gap = O.query_group(op, qg, keys, vals, L, L - 1, summ, kc, vc, gt)
+                oracle_out[(b, h)] = o_out
+            else:
+                mu, so, n = summ
+                shat = O.group_scores(O.block_scores(qg, mu, so, n, alpha, op["scale"], op["so_kind"]))
+                o_sel, gap = O.select_topk(shat, w.top_k)
+            ok, msg = U.selection_ok(sel[b, h], shat, w.top_k)
+            assert ok, f"alpha {alpha} seq {b} group {h}: {msg}; gap {gap:.3g}"
+            oracle_sel[b, h] = o_sel
+            if gap >= U.GAP:
+                np.testing.assert_array_equal(sel[b, h], o_sel)
+                if alpha == 1.0:
+                    err = float(np.abs(out[b, h * G:(h + 1) * G] - o_out).max())
+                    assert err <= 1e-2, f"seq {b} group {h}: max-abs {err}"
+                    outs += 1
+    if alpha == 1.0:
+        assert outs >= w.batch * w.n_kv_heads // 2
+        # every unit's outputs on the oracle's selection (attention roles with a given selection)
+        sel_in = torch.from_numpy(oracle_sel.astype(np.int32)).cuda()
+        out2, _ = U.decode(p, g, s, sel_in=sel_in)
+        for (b, h), o_out in oracle_out.items():
+            err = float(np.abs(out2[b, h * G:(h + 1) * G] - o_out).max())
+            assert err <= 1e-2, f"seq {b} group {h}: max-abs {err} with the oracle's selection"
 
 
 # ---------------------------------------------------------------------------
@@ -278,6 +364,7 @@ def check_lowrank(w, x, s, units=None, gap_min=1e-2):
     units = units or [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
     checked = loose = 0
     for (b, h) in units:
+        print(f"[test] rank-r summaries of unit ({b}, {h})", flush=True)
         L = int(x["lens"][b])
         keys = x["K"][b, h, :L].astype(np.float64)
         rmu, rso, n = O.summaries(keys, L, "lowrank", w.rank)
@@ -343,27 +430,39 @@ def test_decode_lowrank_small(alpha):
     run_and_check(w, x, alpha=alpha)
 
 
-@pytest.fixture(scope="module")
-def long_inputs():
-    w = synth.WORKLOADS["decode_b8_L128k_rank4"]
-    return w, synth.make_inputs(w, 4)
+def check_long_units(w, x, out, sel, oracle_units, p):
+    """Selections of the given units by the gap rule and their outputs where the gap
+    is unambiguous, from the oracle's summaries of those units."""
+    G = w.group
+    outs = 0
+    for (b, h), (summ, kc, vc) in oracle_units.items():
+        print(f"[test] oracle query of unit ({b}, {h})", flush=True)
+        L = int(x["lens"][b])
+        qg = x["Q"][b, 0, h * G:(h + 1) * G].astype(np.float64)
+        gt = x["gates"][b, 0, h * G:(h + 1) * G].astype(np.float64)
+        o_out, o_sel, shat, gap = O.query_group(p, qg, x["K"][b, h, :L].astype(np.float64),
+                                                x["V"][b, h, :L].astype(np.float64), L, L - 1, summ, kc, vc, gt)
+        ok, msg = U.selection_ok(sel[b, h], shat, w.top_k)
+        assert ok, f"seq {b} group {h}: {msg}"
+        if gap >= U.GAP:
+            np.testing.assert_array_equal(sel[b, h], o_sel)
+            err = float(np.abs(out[b, h * G:(h + 1) * G] - o_out).max())
+            assert err <= 1e-2, f"seq {b} group {h}: max-abs {err}"
+            outs += 1
+    assert outs >= len(oracle_units) // 2
+    return outs
 
 
-def test_full_size_long_decode_rank4_sampled(long_inputs):
+def test_full_size_long_decode_rank4(long_inputs, long_oracle_lowrank):
+    """8 x 128k, rank 4 (fp32 storage): selections of 16 units over all 8 sequences and
+    every kv head, outputs where the gap is unambiguous, rank-4 summaries of 4 units."""
     w, x = long_inputs
     p = U.params_for(w)
     g = U.to_device(x)
     s = U.build(p, g)
-    check_lowrank(w, x, s, units=[(0, 0), (7, 5)])
+    check_lowrank(w, x, s, units=[(0, 0), (2, 6), (5, 7), (7, 5)])
     out, sel = U.decode(p, g, s)
-    G = w.group
-    for (b, h) in [(0, 0), (3, 2), (7, 7)]:
-        ref = O.run(x, O.params_of(w), seqs=[b], groups=[h])[(b, h, 0)]
-        o_out, o_sel, shat, gap = ref
-        ok, msg = U.selection_ok(sel[b, h], shat, w.top_k)
-        assert ok, f"seq {b} group {h}: {msg}"
-        if gap >= U.GAP:
-            assert np.abs(out[b, h * G:(h + 1) * G] - o_out).max() <= 1e-2
+    check_long_units(w, x, out, sel, long_oracle_lowrank, O.params_of(w))
 
 
 def test_decode_graph_replays_match_eager():

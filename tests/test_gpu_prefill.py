@@ -133,8 +133,28 @@ def test_select_topk_at_positions_batched():
 
 
 def test_full_size_prefill_sampled():
+    """8192 queries over a 32k prefix: every 16th token (a strided 1/16 of the chunk,
+    starting with the first) and the last."""
     w = synth.WORKLOADS["prefill_T8k_L32k"]
     x = synth.make_inputs(w, 3)
-    rng = np.random.default_rng(0)
-    toks = sorted({0, 1, 63, 64, w.n_q_tokens - 1} | set(rng.integers(0, w.n_q_tokens, 11).tolist()))
+    toks = sorted(set(range(0, w.n_q_tokens, 16)) | {w.n_q_tokens - 1})
     check_prefill(w, x, tokens=toks)
+
+
+def test_prefill_diag_beyond_512_blocks():
+    """Diagonal summaries over 625 candidate blocks: the one-workgroup-per-(token,
+    group) selection kernel (the two-token kernel covers up to 512 blocks)."""
+    L, T = 40000, 40
+    w = synth.Workload("pf625", max_len=L, min_len=L, n_q_tokens=T, q_pos0=L - T, **dict(BASE, top_k=16))
+    x = synth.make_inputs(w, 18)
+    check_prefill(w, x, tokens=list(range(T)))
+
+
+def test_prefill_beyond_2048_blocks():
+    """A 150k-key prefix (2344 blocks): the one-wave-per-(token, group) selection
+    kernel for contexts beyond the LDS of the workgroup kernels."""
+    L, T = 150000, 24
+    w = synth.Workload("pf150k", max_len=L, min_len=L, n_q_tokens=T, q_pos0=L - T,
+                       **dict(BASE, n_q_heads=8, n_kv_heads=1, top_k=16, window=512))
+    x = synth.make_inputs(w, 19)
+    check_prefill(w, x, tokens=list(range(T)))

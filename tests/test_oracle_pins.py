@@ -248,6 +248,50 @@ def test_topk_brute_force_with_ties():
         assert S == sorted(best)
 
 
+def test_topk_gap_is_the_margin_between_chosen_and_rest():
+    """The reported gap is the margin of the chosen set: the lowest chosen score minus
+    the highest score left out (inf when nothing is left out), checked on random
+    scores with many exact ties (gap 0 where the cut falls inside a tie)."""
+    rng = np.random.default_rng(12)
+    for trial in range(300):
+        n = int(rng.integers(1, 12))
+        k = int(rng.integers(1, 12))
+        shat = rng.integers(0, 5, size=n).astype(np.float64) * 0.25
+        sel, gap = O.select_topk(shat, k)
+        chosen = [int(b) for b in sel if b >= 0]
+        rest = [b for b in range(n) if b not in chosen]
+        if not rest:
+            assert gap == np.inf
+        else:
+            assert gap == min(shat[chosen]) - max(shat[rest])
+            assert gap >= 0.0
+
+
+def test_topk_gap_of_constant_blocks_is_the_logit_difference():
+    """Blocks of 64 identical keys have zero covariance, so their score is exactly
+    ln 64 + scale q.k_b; with one head the group score is that minus a common
+    log-sum-exp, and the gap between the k-th and (k+1)-th block is the scaled
+    difference of their logits: for keys c_b e_0 against q = e_0 at scale 1/8 and
+    c = (0.5, 2.0, 1.25, 3.0, -1.0), k = 2 gives (2.0 - 1.25)/8 = 0.09375."""
+    d = 64
+    c = [0.5, 2.0, 1.25, 3.0, -1.0]
+    keys = np.zeros((64 * len(c), d))
+    for b, cb in enumerate(c):
+        keys[64 * b: 64 * b + 64, 0] = cb
+    vals = np.ones((64 * len(c), d))
+    L = keys.shape[0]
+    p = {"top_k": 2, "window": 0, "cmp_len": 0, "cmp_stride": 16, "so_kind": "diag", "rank": 0, "alpha": 1.0,
+         "scale": 0.125}
+    summ = O.summaries(keys, L, "diag")
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    out, sel, shat, gap = O.query_group(p, q, keys, vals, L, L - 1, summ, np.zeros((0, d)), np.zeros((0, d)), None)
+    assert list(sel) == [1, 3]
+    assert abs(gap - 0.09375) < 1e-14
+    p["top_k"] = 5
+    assert O.query_group(p, q, keys, vals, L, L - 1, summ, np.zeros((0, d)), np.zeros((0, d)), None)[3] == np.inf
+
+
 def test_duplicate_blocks_tie_to_lower_index():
     rng = np.random.default_rng(11)
     d = 8
