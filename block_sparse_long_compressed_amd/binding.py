@@ -67,6 +67,8 @@ _SIGNATURES = {
                                         _vp, _vp, _sz, _vp]),
     "cobs_decode_status": (_i32, [_P, _i32, _i32, _vp, _sz, ctypes.POINTER(ctypes.c_uint32), _vp]),
     "cobs_set_poll_limit": (None, [ctypes.c_uint32]),
+    "cobs_sparse_attn_decode_static": (_i32, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _vp, _vp, _vp]),
     "cobs_query_subspace_workspace_bytes": (_sz, [_P]),
     "cobs_query_subspace": (_i32, [_P, _i32, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -195,12 +197,25 @@ COBS_STATUS_WAIT_GAVE_UP = 1
 
 
 def cobs_decode_status(p: cobs_params, batch: int, max_len: int, ws, stream=None) -> int:
-    """Status bits of the decode steps run on ws since the last query (synchronises)."""
+    """Status bits of the decode steps run on ws since the last query (synchronises);
+    ws=None reads the array of cobs_sparse_attn_decode_static."""
     flags = ctypes.c_uint32()
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("cobs_decode_status", lib().cobs_decode_status(ctypes.byref(p), batch, max_len, _ptr(ws), nbytes,
                                                           ctypes.byref(flags), _stream(stream)))
     return flags.value
+
+
+COBS_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def cobs_sparse_attn_decode_static(p: cobs_params, seq_lens, Q, K, V, mu, so, kc, vc, gates, out,
+                                   sel_in=None, sel_out=None, stream=None) -> None:
+    """cobs_sparse_attn_decode with the library's static device workspace (no allocation)."""
+    batch, max_len = K.shape[0], K.shape[2]
+    _check("cobs_sparse_attn_decode_static", lib().cobs_sparse_attn_decode_static(
+        ctypes.byref(p), batch, max_len, _ptr(seq_lens), _ptr(Q), _ptr(K), _ptr(V), _ptr(mu), _ptr(so),
+        _ptr(kc), _ptr(vc), _ptr(gates), _ptr(sel_in), _ptr(sel_out), _ptr(out), _stream(stream)))
 
 
 def cobs_set_poll_limit(polls: int) -> None:

@@ -376,8 +376,14 @@ cobs_status cobs_decode_status(const cobs_params* p, int32_t batch, int32_t max_
   cobs_status st = check_params(p);
   if (st != COBS_OK) return st;
   if ((st = check_sizes(batch, max_len, 1)) != COBS_OK) return st;
-  if (!flags || !ws) return COBS_ERR_INVALID_ARG;
+  if (!flags) return COBS_ERR_INVALID_ARG;
   const Plan pl = make_plan(p, batch, max_len, 1);
+  if (!ws && ws_bytes == 0) {                   // the array of cobs_sparse_attn_decode_static
+    ws = static_scratch_of_current_device();
+    ws_bytes = COBS_STATIC_SCRATCH_BYTES;
+    if (!ws) { *flags = 0u; return COBS_OK; }   // no call on this device yet
+  }
+  if (!ws) return COBS_ERR_INVALID_ARG;
   if (ws_bytes < pl.total) return COBS_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   uint32_t* dev = at<uint32_t>(ws, pl.off_status);

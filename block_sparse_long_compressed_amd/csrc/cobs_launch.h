@@ -89,5 +89,6 @@ hipError_t launch_prefill_attn(const PrefillArgs& a);
 hipError_t launch_prefill_attn_bf16(const PrefillArgs& a);   // token-blocked, bf16 K/V
 hipError_t launch_query_subspace(const SubspaceArgs& a);
 size_t subspace_ws_bytes(int hkv, int d);
+void* static_scratch_of_current_device();       // cobs_sparse_attn_decode_static's array, or null
 
 }  // namespace cobs

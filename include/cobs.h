@@ -215,6 +215,26 @@ cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t
                                     const int32_t* sel_in, int32_t* sel_out, float* out,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/* cobs_sparse_attn_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The workspace is a file-scope device array of
+ * COBS_STATIC_SCRATCH_BYTES (16 MiB) that each GPU holds until the process ends; the
+ * call allocates and frees nothing.
+ *   Arguments, layouts and results as for cobs_sparse_attn_decode.
+ *   Errors as for cobs_sparse_attn_decode; COBS_ERR_WORKSPACE when
+ *   cobs_workspace_bytes(p, batch, max_len, 1) exceeds COBS_STATIC_SCRATCH_BYTES.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.  The first
+ * call on a device looks the array up and zero-fills it with a kernel on `stream`;
+ * make that call outside stream capture.  The status word of cobs_decode_status is in
+ * the array too: query it with ws = NULL and ws_bytes = 0 (see below). */
+#define COBS_STATIC_SCRATCH_BYTES (16u << 20)
+cobs_status cobs_sparse_attn_decode_static(const cobs_params* p, int32_t batch, int32_t max_len,
+                                           const int32_t* seq_lens, const void* Q, const void* K, const void* V,
+                                           const void* mu, const void* so, const void* kc, const void* vc,
+                                           const float* gates, const int32_t* sel_in, int32_t* sel_out, float* out,
+                                           void* stream);
+
 /* Status of the decode steps run on a workspace since the last query (host,
  * synchronous: waits for `stream`, then reads and clears the workspace's status word).
  * A decode step whose selected-branch workgroups wait for the selection published by
@@ -222,9 +242,11 @@ cobs_status cobs_sparse_attn_decode(const cobs_params* p, int32_t batch, int32_t
  * gives up attends to no block for that tile, so the step's output is incomplete, and
  * sets bit 0 of *flags (COBS_STATUS_WAIT_GAVE_UP).  *flags == 0 means every step since
  * the last query completed as specified.
- *   p, batch, max_len, ws, ws_bytes  as passed to cobs_sparse_attn_decode
+ *   p, batch, max_len, ws, ws_bytes  as passed to cobs_sparse_attn_decode; ws = NULL with
+ *           ws_bytes = 0 reads the array of cobs_sparse_attn_decode_static on the
+ *           current device (flags 0 before its first call there)
  *   flags   host out
- * Errors: INVALID_ARG (null ws or flags, bad sizes), WORKSPACE, HIP. */
+ * Errors: INVALID_ARG (null flags, null ws with ws_bytes > 0, bad sizes), WORKSPACE, HIP. */
 #define COBS_STATUS_WAIT_GAVE_UP 1u
 cobs_status cobs_decode_status(const cobs_params* p, int32_t batch, int32_t max_len, void* ws, size_t ws_bytes,
                                uint32_t* flags, void* stream);

@@ -178,13 +178,26 @@ def test_query_subspace_rejects_bad_calls():
     assert lib.cobs_query_subspace(ctypes.byref(p), 10, fake, fake, fake, n, None) == B.COBS_ERR_INVALID_ARG
 
 
+def test_static_decode_rejects_oversized_workspace_on_the_host():
+    # a configuration whose workspace exceeds the library's static array: rejected
+    # before any HIP call (the tensors are never looked at)
+    p = B.make_params(128, 32, 8, 32, window=1024, cmp_len=32, cmp_stride=16, so_kind=B.COBS_SO_LOWRANK, rank=4)
+    assert B.cobs_workspace_bytes(p, 256, 131072) > B.COBS_STATIC_SCRATCH_BYTES
+    st = B.lib().cobs_sparse_attn_decode_static(ctypes.byref(p), 256, 131072, None, None, None, None, None, None,
+                                                None, None, None, None, None, None, None)
+    assert st == B.COBS_ERR_WORKSPACE
+    bad = good()
+    bad.head_dim = 96
+    st = B.lib().cobs_sparse_attn_decode_static(ctypes.byref(bad), 1, 1024, None, None, None, None, None, None,
+                                                None, None, None, None, None, None, None)
+    assert st == B.COBS_ERR_UNSUPPORTED
+
+
 def test_decode_status_argument_checks_on_the_host():
     p = good()
     flags = ctypes.c_uint32()
     assert B.lib().cobs_decode_status(ctypes.byref(p), 1, 1024, None, 0, None, None) == B.COBS_ERR_INVALID_ARG
     assert B.lib().cobs_decode_status(ctypes.byref(p), 1, 1024, None, 64, ctypes.byref(flags),
-                                      None) == B.COBS_ERR_INVALID_ARG
-    assert B.lib().cobs_decode_status(ctypes.byref(p), 1, 1024, None, 0, ctypes.byref(flags),
                                       None) == B.COBS_ERR_INVALID_ARG
     ws_bytes = B.cobs_workspace_bytes(p, 1, 1024)
     buf = ctypes.create_string_buffer(16)
