@@ -71,15 +71,20 @@ cobs_status check_sizes(int batch, int max_len, int tokens) {
 // Launch shapes and the workspace carve-up; a pure function of the sizes so that
 // cobs_workspace_bytes and every call agree.  Decode workgroups have NW waves (8, or 4
 // for fp32 keys at d = 128, whose attention tile needs a SIMD's whole register file).
+constexpr int kWideUnits = 64;          // units from which eight-wave workgroups pay off
 constexpr int kLeadTilesPerWave = 2;    // selected tiles each wave of the selecting workgroup runs
 constexpr int kSlcTilesPerWave = 2;     // selected tiles per wave of the other selected-branch workgroups
-constexpr int kScoreTilesPerWave = 4;   // 16-block summary tiles per scoring wave
-constexpr int kWcTilesPerWave = 5;      // target window/pooled tiles per wave
+constexpr int kLeadTilesPerWaveNarrow = 1;   // the same with four-wave workgroups
+constexpr int kSlcTilesPerWaveNarrow = 1;
+constexpr int kScoreTilesPerWave = 4;   // 16-block summary tiles per wave of a whole-unit scoring workgroup
+constexpr int kScoreWaves = 1024;       // scoring waves of a launch with split scoring
+constexpr int kWcTilesPerWave = 5;      // target window/pooled tiles per wave (eight-wave workgroups)
+constexpr int kWcTilesPerWaveNarrow = 4;   // the same with four-wave workgroups
 constexpr int kFillWorkgroups = 256;    // workgroups that fill the chip once (one per CU)
 constexpr size_t kDecodeLdsBudget = 150 * 1024;
 
 struct Plan {
-  int nw, splits, sel_tpw;
+  int nw, splits, sel_tpw, tpw_slc;
   int lead_tiles, wg_slc, wg_wc;         // with a selecting workgroup (the fused step)
   int wg_slc_in;                         // with the caller's selection (attention only)
   size_t off_cnt_sel, off_cnt_attn, off_ready, off_status, off_scores, off_lse, off_sel, off_ml, off_o, total;
@@ -93,28 +98,33 @@ Plan make_plan(const cobs_params* p, int batch, int max_len, int tokens) {
   const int nb_pad = (nb + 15) / 16 * 16;
   const int units_sel = batch * tokens * hkv;
   const int units = batch * hkv;
-  pl.nw = decode_waves(bf16, d);
-  // scoring: one workgroup per unit keeps the raw scores in LDS when the unit's tiles
-  // fit its waves; longer contexts split the tiles and hand the scores off
   const int tiles = cdiv(nb, 16);
-  if (tiles <= pl.nw * kScoreTilesPerWave &&
-      decode_select_lds_bytes(bf16, d, nb_pad, true) <= kDecodeLdsBudget) {
+  // Eight-wave workgroups when there are units enough to fill the chip and one
+  // workgroup can score a whole unit (its scores then stay in LDS); otherwise four
+  // (two per CU), with the scoring spread over many waves and handed off.
+  const bool wide = decode_max_waves(bf16, d) == 8 && units >= kWideUnits &&
+                    tiles <= 8 * kScoreTilesPerWave && decode_select_lds_bytes(8, nb_pad, true) <= kDecodeLdsBudget;
+  pl.nw = wide ? 8 : 4;
+  if (wide) {
     pl.splits = 1;
     pl.sel_tpw = cdiv(tiles, pl.nw);
   } else {
-    pl.splits = cdiv(tiles, pl.nw * kScoreTilesPerWave);
-    pl.sel_tpw = cdiv(tiles, pl.nw * pl.splits);
+    pl.sel_tpw = std::min(8, std::max(1, cdiv(units_sel * tiles, kScoreWaves)));
+    pl.splits = cdiv(tiles, pl.nw * pl.sel_tpw);
   }
   // selected branch: the lead's share, then workgroups that wait for the rest
-  pl.lead_tiles = std::min(p->top_k, pl.nw * kLeadTilesPerWave);
-  pl.wg_slc = cdiv(p->top_k - pl.lead_tiles, pl.nw * kSlcTilesPerWave);
-  pl.wg_slc_in = cdiv(p->top_k, pl.nw * kSlcTilesPerWave);
+  pl.lead_tiles = std::min(p->top_k, pl.nw * (wide ? kLeadTilesPerWave : kLeadTilesPerWaveNarrow));
+  const int tpw_slc = wide ? kSlcTilesPerWave : kSlcTilesPerWaveNarrow;
+  pl.tpw_slc = tpw_slc;
+  pl.wg_slc = cdiv(p->top_k - pl.lead_tiles, pl.nw * tpw_slc);
+  pl.wg_slc_in = cdiv(p->top_k, pl.nw * tpw_slc);
   // window and pooled tiles: about kWcTilesPerWave per wave, spread wider when the
   // units are too few to fill the chip
   const int t_win = p->window > 0 ? cdiv(std::min(p->window, max_len), 64) : 0;
   const int t_cmp = cdiv((int)nc_of(p, max_len), 64);
   const int t_wc = t_win + t_cmp;
-  pl.wg_wc = t_wc == 0 ? 0 : std::max(cdiv(t_wc, pl.nw * kWcTilesPerWave),
+  const int wc_tpw = wide ? kWcTilesPerWave : kWcTilesPerWaveNarrow;
+  pl.wg_wc = t_wc == 0 ? 0 : std::max(cdiv(t_wc, pl.nw * wc_tpw),
                                       std::min(cdiv(t_wc, pl.nw), cdiv(kFillWorkgroups, std::max(units, 1)) - 1));
   if (t_wc > 0) pl.wg_wc = std::max(pl.wg_wc, 1);
   const int P = std::max(1 + pl.wg_slc, pl.wg_slc_in) + 2 * pl.wg_wc;   // partial slots, either mode
@@ -266,7 +276,7 @@ static DecodeArgs decode_args(const cobs_params* p, const Plan& pl, int32_t batc
   a.so_kind = kernel_kind(p); a.bf16 = p->kv_dtype == COBS_BF16; a.alpha = p->alpha; a.scale = scale_of(p);
   a.do_select = a.do_attn = false;
   a.splits = pl.splits; a.sel_tpw = pl.sel_tpw;
-  a.lead_tiles = pl.lead_tiles; a.wg_slc = pl.wg_slc; a.tpw_slc = kSlcTilesPerWave; a.wg_wc = pl.wg_wc;
+  a.lead_tiles = pl.lead_tiles; a.wg_slc = pl.wg_slc; a.tpw_slc = pl.tpw_slc; a.wg_wc = pl.wg_wc; a.nw = pl.nw;
   a.seq_lens = seq_lens; a.Q = a.K = a.V = a.kc = a.vc = nullptr; a.mu = a.so = a.gates = nullptr;
   a.sel = nullptr; a.sel_in = nullptr; a.sel_score = nullptr; a.out = nullptr;
   a.P = p->subspace_dim > 0 ? p->subspace : nullptr; a.sub_s = p->subspace_dim; a.vlen = vec_len(p);

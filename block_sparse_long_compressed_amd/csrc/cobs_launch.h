@@ -33,6 +33,7 @@ struct DecodeArgs {
   int lead_tiles;              // selected tiles the selecting workgroup attends to itself
   int wg_slc, tpw_slc;         // further selected-branch workgroups per unit, tiles per wave
   int wg_wc;                   // window/pooled workgroups per unit
+  int nw;                      // waves per workgroup (4 or 8)
   const int32_t* seq_lens;
   const void *Q, *K, *V, *kc, *vc;
   const void *mu, *so;         // summaries in the layout of so_kind (3, 5: compressed storage)
@@ -82,8 +83,8 @@ hipError_t launch_build_diag(const BuildArgs& a);
 hipError_t launch_build_lowrank(const BuildArgs& a);
 hipError_t launch_append_diag(const BuildArgs& a);     // mean, diagonal, pooled tokens of touched blocks
 hipError_t launch_decode(const DecodeArgs& a);
-int decode_waves(bool bf16, int head_dim);      // waves per decode workgroup
-size_t decode_select_lds_bytes(bool bf16, int head_dim, int nb_pad, bool raw_in_lds);
+int decode_max_waves(bool bf16, int head_dim);  // most waves a decode workgroup can have
+size_t decode_select_lds_bytes(int nw, int nb_pad, bool raw_in_lds);
 hipError_t launch_prefill_select(const PrefillArgs& a);
 hipError_t launch_prefill_attn(const PrefillArgs& a);
 hipError_t launch_prefill_attn_bf16(const PrefillArgs& a);   // token-blocked, bf16 K/V

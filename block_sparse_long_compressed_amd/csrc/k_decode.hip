@@ -151,6 +151,47 @@ __device__ __forceinline__ void wave_tiles(Src&& src, const typename E::storage*
   }
 }
 
+// The same for a wave with at most two tiles (the selecting workgroup's share of
+// the selected blocks): both tiles' K loads go out at once, so the second tile's
+// scores need no round trip of their own; its V loads follow once V of the first
+// tile is staged.
+template <typename E, int D, typename Src>
+__device__ __forceinline__ void wave_tiles_pair(Src&& src, const typename E::storage* Qg, int G, float scale_log2,
+                                                typename E::storage* lds, float& m_run, float& l_run,
+                                                f32x4 (&acc_o)[AttnTiling<E, D>::kDt]) {
+  using T = AttnTiling<E, D>;
+  constexpr int NCH = T::kChunks, EPL = T::kEpl, NDT = T::kDt;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  m_run = -INFINITY;
+  l_run = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const typename E::storage *K0 = nullptr, *V0 = nullptr, *K1 = nullptr, *V1 = nullptr;
+  const int n0 = src(0, K0, V0);
+  if (n0 <= 0) return;
+  const int n1 = src(1, K1, V1);
+  TileRegs<E, D> t0, t1;
+  tile_load_k<E, D>(K0, n0, t0);
+  tile_load_v<E, D>(V0, n0, t0);
+  if (n1 > 0) tile_load_k<E, D>(K1, n1, t1);
+  u32x4 qf[NCH];
+  {
+    const typename E::storage* Qh = Qg + (size_t)min(n, G - 1) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
+  }
+  f32x4 sc4[4];
+  tile_scores<E, D>(t0, qf, sc4);
+  tile_stage_v<E, D>(t0, lds);
+  if (n1 > 0) tile_load_v<E, D>(V1, n1, t1);
+  tile_softmax_pv<E, D>(sc4, n0, scale_log2, lds, m_run, l_run, acc_o);
+  if (n1 <= 0) return;
+  tile_scores<E, D>(t1, qf, sc4);
+  tile_stage_v<E, D>(t1, lds);
+  tile_softmax_pv<E, D>(sc4, n1, scale_log2, lds, m_run, l_run, acc_o);
+}
+
 template <typename E, int D, int NW>
 __host__ __device__ constexpr size_t attn_stage_bytes() {
   return (size_t)NW * kBlock * AttnTiling<E, D>::kRowStride * E::kBytes;
@@ -164,9 +205,9 @@ __host__ __device__ constexpr size_t attn_stage_bytes() {
 // workgroup owns (each is written, empty when no wave contributed).
 // ---------------------------------------------------------------------------
 template <typename E, int D, int NW>
-__device__ void merge_and_finish(const DecodeParams& p, int unit, int wave_slot, const int (&my_slots)[2], int nmine,
+__device__ __forceinline__ void merge_and_finish(const DecodeParams& p, int unit, int wave_slot, const int (&my_slots)[2], int nmine,
                                  float m_run, float l_run, const f32x4 (&acc_o)[D / 16], unsigned char* smem,
-                                 int* flag) {
+                                 int* flag, const float* spare = nullptr, const int* spare_used = nullptr) {
   constexpr int NT = 64 * NW, NDT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -186,6 +227,8 @@ __device__ void merge_and_finish(const DecodeParams& p, int unit, int wave_slot,
   if (g == 0) { mml[(wave * 16 + n) * 2] = m_run; mml[(wave * 16 + n) * 2 + 1] = l_run; }
   if (lane == 0) wslot[wave] = wave_slot;
   __syncthreads();
+  // a parked window partial (see wc_attention) joins the window slot my_slots[0]
+  const bool use_spare = spare_used && *spare_used;
   const Coherent po(p.part_o + (size_t)unit * P * G * D, (uint32_t)(P * G * D * 4));
   const Coherent pm(p.part_ml + (size_t)unit * P * 32, (uint32_t)(P * 32 * 4));
   const int items = G * (D / 4);
@@ -193,7 +236,8 @@ __device__ void merge_and_finish(const DecodeParams& p, int unit, int wave_slot,
     const int which = idx / items, r = idx % items;
     const int slot = my_slots[which];
     const int h = r / (D / 4), d4 = (r % (D / 4)) * 4;
-    float M = -INFINITY;
+    const bool sp = use_spare && which == 0;
+    float M = sp ? spare[16 * D + 2 * h] : -INFINITY;
     for (int w = 0; w < NW; ++w)
       if (wslot[w] == slot) M = fmaxf(M, mml[(w * 16 + h) * 2]);
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
@@ -205,6 +249,12 @@ __device__ void merge_and_finish(const DecodeParams& p, int unit, int wave_slot,
         const float f = fast_exp2(mw - M);
         Ls += f * mml[(w * 16 + h) * 2 + 1];
         const float* src = mo + ((size_t)w * 16 + h) * D + d4;
+        o[0] += f * src[0]; o[1] += f * src[1]; o[2] += f * src[2]; o[3] += f * src[3];
+      }
+      if (sp && spare[16 * D + 2 * h] != -INFINITY) {
+        const float f = fast_exp2(spare[16 * D + 2 * h] - M);
+        Ls += f * spare[16 * D + 2 * h + 1];
+        const float* src = spare + h * D + d4;
         o[0] += f * src[0]; o[1] += f * src[1]; o[2] += f * src[2]; o[3] += f * src[3];
       }
     }
@@ -302,8 +352,8 @@ __device__ void merge_and_finish(const DecodeParams& p, int unit, int wave_slot,
 // Scoring role.  Returns true in the lead (every thread), with the selection of
 // this unit in s_sel[0..top_k) (ascending, -1 padded) and the count in *n_sel.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int KIND, int HV, int NW>
-__device__ bool select_role(const DecodeParams& p, int unit, int split, unsigned char* smem, int* s_sel,
+template <typename E, int D, int KIND, int NW>
+__device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int split, unsigned char* smem, int* s_sel,
                             int* n_sel) {
   constexpr int NT = 64 * NW;
   SelLds<NW>& sl = *reinterpret_cast<SelLds<NW>*>(smem);
@@ -487,6 +537,7 @@ __device__ bool select_role(const DecodeParams& p, int unit, int split, unsigned
   // cost one memory round trip
   const int per = (p.nb_max + NT - 1) / NT;
   const int b0 = threadIdx.x * per;
+  constexpr int HV = 4;                                          // float4s of head scores per block (G <= 16)
   constexpr int kRound = 8 / HV;                                 // blocks per load round (8 float4)
   f32x4 raw[kRound][HV];
   auto load_round = [&](int e0) {
@@ -581,7 +632,7 @@ __device__ bool select_role(const DecodeParams& p, int unit, int split, unsigned
 // selection in LDS, strided over the waves.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int NW>
-__device__ void lead_attention(const DecodeParams& p, int unit, const int* s_sel, int n_sel, unsigned char* smem,
+__device__ __forceinline__ void lead_attention(const DecodeParams& p, int unit, const int* s_sel, int n_sel, unsigned char* smem,
                                int* flag) {
   using T = AttnTiling<E, D>;
   const int wave = threadIdx.x >> 6;
@@ -605,20 +656,25 @@ __device__ void lead_attention(const DecodeParams& p, int unit, const int* s_sel
   typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
   float m_run, l_run;
   f32x4 acc_o[T::kDt];
-  wave_tiles<E, D>(src, Qg, G, p.scale_log2, lds, m_run, l_run, acc_o);
+  if (p.lead_tiles <= 2 * NW) wave_tiles_pair<E, D>(src, Qg, G, p.scale_log2, lds, m_run, l_run, acc_o);
+  else wave_tiles<E, D>(src, Qg, G, p.scale_log2, lds, m_run, l_run, acc_o);
   const int mine[2] = {0, 0};
   merge_and_finish<E, D, NW>(p, unit, 0, mine, 1, m_run, l_run, acc_o, smem, flag);
 }
 
 // ---------------------------------------------------------------------------
-// Window and pooled-token workgroups (`local` of wg_wc per unit): the unit's waves
-// split between the two branches so that the longest run of tiles is shortest,
-// then each wave takes an even share of its branch's tiles.
+// Window and pooled-token workgroups (`local` of wg_wc per unit): the unit's window
+// tiles followed by its pooled tiles form one list, split evenly over the unit's
+// waves.  The one wave of a workgroup whose share crosses from window to pooled
+// tiles parks its window partial in a spare LDS slot beyond the V staging area, and
+// the workgroup merge counts it with the window waves.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int NW>
-__device__ void wc_attention(const DecodeParams& p, int unit, int local, unsigned char* smem, int* flag) {
+__device__ __forceinline__ void wc_attention(const DecodeParams& p, int unit, int local, unsigned char* smem, int* flag) {
   using T = AttnTiling<E, D>;
-  const int wave = threadIdx.x >> 6;
+  constexpr int NCH = T::kChunks, EPL = T::kEpl, NDT = T::kDt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
   const int seq = unit / p.hkv, head = unit % p.hkv;
   const int G = p.group;
   const int L = p.seq_lens[seq];
@@ -626,50 +682,95 @@ __device__ void wc_attention(const DecodeParams& p, int unit, int local, unsigne
   const int win_len = min(p.window, L);
   const int win_start = L - win_len;
   const int t_win = (win_len + kBlock - 1) / kBlock, t_cmp = (nc + kBlock - 1) / kBlock;
-  const int waves = p.wg_wc * NW;
-  int nw_win = 0;
-  if (t_win > 0 && t_cmp == 0) {
-    nw_win = waves;
-  } else if (t_win > 0) {
-    int best = 1 << 30;
-    for (int a = 1; a < waves; ++a) {
-      const int c = max((t_win + a - 1) / a, (t_cmp + waves - a - 1) / (waves - a));
-      if (c < best) { best = c; nw_win = a; }
-    }
-  }
+  const int Tt = t_win + t_cmp, waves = p.wg_wc * NW;
   const int gw = local * NW + wave;
-  const bool is_win = gw < nw_win;
-  const int nwb = is_win ? nw_win : waves - nw_win;          // waves of this branch
-  const int idx = is_win ? gw : gw - nw_win;
-  const int tb = is_win ? t_win : t_cmp;
-  const int j0 = (int)((int64_t)idx * tb / max(nwb, 1)), j1 = (int)((int64_t)(idx + 1) * tb / max(nwb, 1));
+  int j0, j1;                                  // this wave's share of the list
+  if constexpr (NW == 8) {                     // even split; at most one wave per workgroup straddles
+    j0 = (int)((int64_t)gw * Tt / waves);
+    j1 = (int)((int64_t)(gw + 1) * Tt / waves);
+  } else {                                     // no spare LDS slot: each wave stays in one branch,
+    int nw_win = 0;                            // the split that makes the longest share shortest
+    if (t_win > 0 && t_cmp == 0) {
+      nw_win = waves;
+    } else if (t_win > 0) {
+      int best = 1 << 30;
+      for (int a = 1; a < waves; ++a) {
+        const int c = max((t_win + a - 1) / a, (t_cmp + waves - a - 1) / (waves - a));
+        if (c < best) { best = c; nw_win = a; }
+      }
+    }
+    const bool is_win = gw < nw_win;
+    const int nwb = max(is_win ? nw_win : waves - nw_win, 1), idx = is_win ? gw : gw - nw_win;
+    const int tb = is_win ? t_win : t_cmp, base = is_win ? 0 : t_win;
+    j0 = base + (int)((int64_t)idx * tb / nwb);
+    j1 = base + (int)((int64_t)(idx + 1) * tb / nwb);
+  }
   const typename E::storage* Ku = reinterpret_cast<const typename E::storage*>(p.K) + (size_t)unit * p.max_len * D;
   const typename E::storage* Vu = reinterpret_cast<const typename E::storage*>(p.V) + (size_t)unit * p.max_len * D;
   const typename E::storage* kcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.kc) + (size_t)unit * p.nc_max * D : nullptr;
   const typename E::storage* vcu = p.cmp_on ? reinterpret_cast<const typename E::storage*>(p.vc) + (size_t)unit * p.nc_max * D : nullptr;
-  auto src = [&](int j, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
-    const int t = j0 + j;
-    if (t >= j1) return 0;
-    if (is_win) {
+  auto src = [&](int t, const typename E::storage*& Kt, const typename E::storage*& Vt) -> int {
+    if (t < t_win) {
       const int start = win_start + t * kBlock;
       Kt = Ku + (size_t)start * D;
       Vt = Vu + (size_t)start * D;
       return min(kBlock, L - start);
     }
-    const int start = t * kBlock;
+    const int start = (t - t_win) * kBlock;
     Kt = kcu + (size_t)start * D;
     Vt = vcu + (size_t)start * D;
     return min(kBlock, nc - start);
   };
-  const typename E::storage* Qg = reinterpret_cast<const typename E::storage*>(p.Q) + ((size_t)seq * p.hkv * G + (size_t)head * G) * D;
   typename E::storage* lds = reinterpret_cast<typename E::storage*>(smem) + (size_t)wave * kBlock * T::kRowStride;
-  float m_run, l_run;
-  f32x4 acc_o[T::kDt];
-  wave_tiles<E, D>(src, Qg, G, p.scale_log2, lds, m_run, l_run, acc_o);
+  float* spare = reinterpret_cast<float*>(smem + attn_stage_bytes<E, D, NW>());   // [16][D] then [16][2]
+  __shared__ int s_straddle;
+  if (threadIdx.x == 0) s_straddle = 0;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc_o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  if (j0 < j1) {
+    TileRegs<E, D> tr;
+    const typename E::storage *Kt = nullptr, *Vt = nullptr;
+    int nv = src(j0, Kt, Vt);
+    tile_load_k<E, D>(Kt, nv, tr);
+    tile_load_v<E, D>(Vt, nv, tr);
+    u32x4 qf[NCH];
+    {
+      const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
+                                      ((size_t)seq * p.hkv * G + (size_t)head * G + min(n, G - 1)) * D;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
+    }
+    for (int t = j0; t < j1; ++t) {
+      f32x4 sc4[4];
+      tile_scores<E, D>(tr, qf, sc4);
+      const typename E::storage *Kn = nullptr, *Vn = nullptr;
+      const int nv_next = (t + 1 < j1) ? src(t + 1, Kn, Vn) : 0;
+      if (nv_next > 0) tile_load_k<E, D>(Kn, nv_next, tr);
+      tile_stage_v<E, D>(tr, lds);
+      tile_softmax_pv<E, D>(sc4, nv, p.scale_log2, lds, m_run, l_run, acc_o);
+      if (nv_next > 0) tile_load_v<E, D>(Vn, nv_next, tr);
+      if (t + 1 == t_win && t + 1 < j1) {          // window part done, pooled tiles follow
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) spare[n * D + 16 * dt + 4 * g + i] = acc_o[dt][i];
+          acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (g == 0) { spare[16 * D + 2 * n] = m_run; spare[16 * D + 2 * n + 1] = l_run; }
+        if (lane == 0) s_straddle = 1;
+        m_run = -INFINITY;
+        l_run = 0.f;
+      }
+      nv = nv_next;
+    }
+  }
   const int ns = slc_slots(p);
   const int mine[2] = {ns + local, ns + p.wg_wc + local};
-  const int wslot = j1 > j0 ? (is_win ? mine[0] : mine[1]) : -1;
-  merge_and_finish<E, D, NW>(p, unit, wslot, mine, 2, m_run, l_run, acc_o, smem, flag);
+  const int wslot = j1 > j0 ? ((j1 - 1) < t_win ? mine[0] : mine[1]) : -1;
+  merge_and_finish<E, D, NW>(p, unit, wslot, mine, 2, m_run, l_run, acc_o, smem, flag, spare, &s_straddle);
 }
 
 // ---------------------------------------------------------------------------
@@ -679,7 +780,7 @@ __device__ void wc_attention(const DecodeParams& p, int unit, int local, unsigne
 // selection.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int NW>
-__device__ void slc_attention(const DecodeParams& p, int unit, int local, unsigned char* smem, int* flag) {
+__device__ __forceinline__ void slc_attention(const DecodeParams& p, int unit, int local, unsigned char* smem, int* flag) {
   using T = AttnTiling<E, D>;
   const int wave = threadIdx.x >> 6;
   const int seq = unit / p.hkv, head = unit % p.hkv;
@@ -724,19 +825,26 @@ __device__ void slc_attention(const DecodeParams& p, int unit, int local, unsign
   merge_and_finish<E, D, NW>(p, unit, mine[0], mine, 1, m_run, l_run, acc_o, smem, flag);
 }
 
-template <typename E, int D>
-constexpr int waves_of() { return (E::kBytes == 4 && D == 128) ? 4 : 8; }
+// Waves per workgroup: 8 (one workgroup per CU: the selecting workgroup holds a whole
+// unit's scores) or 4 (two per CU, finer work for few units or long contexts); fp32
+// keys at d = 128 take 4 (their attention tile needs a SIMD's whole register file).
+template <typename E, int D, int NW>
+struct DecodeShape {
+  static constexpr bool kWide = E::kBytes == 4 && D == 128;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kMinBlocks = (NW == 4 && !kWide) ? 2 : 1;
+};
 
-template <typename E, int D, int KIND, int HV>
-__global__ __launch_bounds__((64 * waves_of<E, D>()), 1) void k_decode(DecodeParams p) {
-  constexpr int NW = waves_of<E, D>();
+template <typename E, int D, int KIND, int NW>
+__global__ __launch_bounds__((DecodeShape<E, D, NW>::kThreads), (DecodeShape<E, D, NW>::kMinBlocks))
+void k_decode(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int flag;
   __shared__ int s_sel[64];
   __shared__ int n_sel;
   const int i = blockIdx.x;
   if (i < p.sel_wgs) {
-    if (!select_role<E, D, KIND, HV, NW>(p, i / p.splits, i % p.splits, smem, s_sel, &n_sel)) return;
+    if (!select_role<E, D, KIND, NW>(p, i / p.splits, i % p.splits, smem, s_sel, &n_sel)) return;
     if constexpr (KIND != 2) {
       if (p.has_lead) lead_attention<E, D, NW>(p, i / p.splits, s_sel, n_sel, smem, &flag);
     }
@@ -753,62 +861,45 @@ __global__ __launch_bounds__((64 * waves_of<E, D>()), 1) void k_decode(DecodePar
   }
 }
 
-template <typename E, int D>
+template <typename E, int D, int NW>
 static size_t attn_role_lds_bytes(int P) {
-  constexpr int NW = waves_of<E, D>();
   const size_t merge = (size_t)NW * 16 * (D + 2) * sizeof(float) + NW * sizeof(int);
-  return std::max(std::max(attn_stage_bytes<E, D, NW>(), merge), (size_t)P * 48 * sizeof(float));
+  const size_t spare = NW == 8 ? ((size_t)16 * D + 32) * sizeof(float) : 0;   // a parked window partial
+  return std::max(std::max(attn_stage_bytes<E, D, NW>(), merge), (size_t)P * 48 * sizeof(float)) + spare;
 }
 
-template <typename E, int D, int KIND, int HV>
+template <typename E, int D, int KIND, int NW>
 static hipError_t launch_decode_t(const DecodeArgs& a, const DecodeParams& dp) {
-  constexpr int NW = waves_of<E, D>();
   const int total = dp.sel_wgs + dp.wc_wgs + dp.slc_wgs;
   size_t lds = 0;
   if (dp.sel_wgs) lds = std::max(lds, select_lds_bytes<NW>(dp.nb_pad, dp.splits == 1));
-  if (dp.do_attn) lds = std::max(lds, attn_role_lds_bytes<E, D>(dp.has_lead + dp.wg_slc + 2 * dp.wg_wc));
-  hipLaunchKernelGGL((k_decode<E, D, KIND, HV>), dim3(total), dim3(64 * NW), lds, a.stream, dp);
+  if (dp.do_attn) lds = std::max(lds, attn_role_lds_bytes<E, D, NW>(dp.has_lead + dp.wg_slc + 2 * dp.wg_wc));
+  hipLaunchKernelGGL((k_decode<E, D, KIND, NW>), dim3(total), dim3(64 * NW), lds, a.stream, dp);
   return hipGetLastError();
+}
+
+template <typename E, int D, int NW>
+static hipError_t launch_decode_kind(const DecodeArgs& a, const DecodeParams& dp) {
+  switch (a.so_kind) {
+    case 0: return launch_decode_t<E, D, 0, NW>(a, dp);
+    case 1: return launch_decode_t<E, D, 1, NW>(a, dp);
+    case 2: return launch_decode_t<E, D, 2, NW>(a, dp);   // exact masses: scoring roles only
+    case 3: return launch_decode_t<E, D, 3, NW>(a, dp);   // compressed storage
+    case 4: return launch_decode_t<E, D, 4, NW>(a, dp);   // rank-r fp32 in a query subspace
+    default: return launch_decode_t<E, D, 5, NW>(a, dp);  // compressed storage in a query subspace
+  }
 }
 
 template <typename E, int D>
 static hipError_t launch_decode_ed(const DecodeArgs& a, const DecodeParams& dp) {
-  const int hv = a.group <= 4 ? 1 : a.group <= 8 ? 2 : 4;
-  if (a.so_kind == 2) {                       // exact masses: scoring roles only
-    if (hv == 1) return launch_decode_t<E, D, 2, 1>(a, dp);
-    if (hv == 2) return launch_decode_t<E, D, 2, 2>(a, dp);
-    return launch_decode_t<E, D, 2, 4>(a, dp);
-  }
-  if (a.so_kind == 0) {
-    if (hv == 1) return launch_decode_t<E, D, 0, 1>(a, dp);
-    if (hv == 2) return launch_decode_t<E, D, 0, 2>(a, dp);
-    return launch_decode_t<E, D, 0, 4>(a, dp);
-  }
-  if (a.so_kind == 3) {                       // compressed storage
-    if (hv == 1) return launch_decode_t<E, D, 3, 1>(a, dp);
-    if (hv == 2) return launch_decode_t<E, D, 3, 2>(a, dp);
-    return launch_decode_t<E, D, 3, 4>(a, dp);
-  }
-  if (a.so_kind == 4) {                       // rank-r fp32 in a query subspace
-    if (hv == 1) return launch_decode_t<E, D, 4, 1>(a, dp);
-    if (hv == 2) return launch_decode_t<E, D, 4, 2>(a, dp);
-    return launch_decode_t<E, D, 4, 4>(a, dp);
-  }
-  if (a.so_kind == 5) {                       // compressed storage in a query subspace
-    if (hv == 1) return launch_decode_t<E, D, 5, 1>(a, dp);
-    if (hv == 2) return launch_decode_t<E, D, 5, 2>(a, dp);
-    return launch_decode_t<E, D, 5, 4>(a, dp);
-  }
-  if (hv == 1) return launch_decode_t<E, D, 1, 1>(a, dp);
-  if (hv == 2) return launch_decode_t<E, D, 1, 2>(a, dp);
-  return launch_decode_t<E, D, 1, 4>(a, dp);
+  if constexpr (DecodeShape<E, D, 8>::kWide) return launch_decode_kind<E, D, 4>(a, dp);
+  else return a.nw == 8 ? launch_decode_kind<E, D, 8>(a, dp) : launch_decode_kind<E, D, 4>(a, dp);
 }
 
-int decode_waves(bool bf16, int head_dim) { return (!bf16 && head_dim == 128) ? 4 : 8; }
+int decode_max_waves(bool bf16, int head_dim) { return (!bf16 && head_dim == 128) ? 4 : 8; }
 
-size_t decode_select_lds_bytes(bool bf16, int head_dim, int nb_pad, bool raw_in_lds) {
-  return decode_waves(bf16, head_dim) == 8 ? select_lds_bytes<8>(nb_pad, raw_in_lds)
-                                           : select_lds_bytes<4>(nb_pad, raw_in_lds);
+size_t decode_select_lds_bytes(int nw, int nb_pad, bool raw_in_lds) {
+  return nw == 8 ? select_lds_bytes<8>(nb_pad, raw_in_lds) : select_lds_bytes<4>(nb_pad, raw_in_lds);
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {

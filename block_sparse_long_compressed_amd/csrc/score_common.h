@@ -58,6 +58,7 @@ struct ScoreW {
   float quad[D / 16][4];
   u32x4 qb[D / 32];
   u32x4 qh[D / 32], ql[D / 32];
+  u32x4 q2h[D / 32], q2l[D / 32];     // diagonal kind, bf16 queries: q^2 as exact hi + lo bf16 parts
 };
 
 template <int D>
@@ -398,16 +399,71 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
   return acc + acc2;
 }
 
-// Whether a kind runs its contraction on the bf16 MFMA (compressed kinds, bf16 queries).
+// Whether a kind runs its contraction on the bf16 MFMA: the compressed kinds and the
+// diagonal kind, with bf16 queries.
 template <typename E, int KIND>
-constexpr bool kBf16Path = E::kBytes == 2 && Kind<KIND>::kFp4;
+constexpr bool kBf16Path = E::kBytes == 2 && (Kind<KIND>::kFp4 || KIND == 0);
+
+// x (eight fp32 values, two f32x4) as hi + lo bf16 parts: hi the nearest bf16 of x, lo
+// the nearest bf16 of x - hi, so hi + lo keeps 16 of x's 24 significand bits (the
+// dropped part is below 2^-16 of |x|).
+__device__ __forceinline__ void split_bf16x8(const f32x4& x, const f32x4& y, u32x4& h, u32x4& l) {
+  h = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  const float xs[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    l[e] = pack_bf16x2(xs[2 * e] - __uint_as_float(h[e] << 16), xs[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u));
+}
+
+// Diagonal kind with bf16 queries on v_mfma_f32_16x16x32_bf16: the tile's fp32 means
+// and variances split into hi + lo bf16 parts, q (bf16, exact) and q^2 (exact in fp32,
+// 16 significand bits, as an exact hi + lo pair) in the same chunk order (lane (n, g)'s
+// eight k-slots of chunk j are columns 16u + 4g + c for u = 2j, 2j+1, the columns its
+// fp32 summary loads hold).  Products are exact; sums accumulate in fp32.
+template <int D, int KIND>
+__device__ __forceinline__ f32x4 sum_tile_score_diag_split(const SumTile<D, KIND>& t, bool use_quad, float alpha,
+                                                           float scale, const ScoreW<D>& W) {
+  constexpr int NJ = D / 32;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    u32x4 mh, ml;
+    split_bf16x8(t.m4[2 * j], t.m4[2 * j + 1], mh, ml);
+    acc = mfma_bf16_16x16x32(mh, W.qb[j], acc);
+    acc = mfma_bf16_16x16x32(ml, W.qb[j], acc);
+  }
+  if (use_quad) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      u32x4 vh, vl;
+      split_bf16x8(t.v4[0][2 * j], t.v4[0][2 * j + 1], vh, vl);
+      acc2 = mfma_bf16_16x16x32(vh, W.q2h[j], acc2);
+      acc2 = mfma_bf16_16x16x32(vh, W.q2l[j], acc2);
+      acc2 = mfma_bf16_16x16x32(vl, W.q2h[j], acc2);
+      acc2 = mfma_bf16_16x16x32(vl, W.q2l[j], acc2);
+    }
+  }
+  return scale * acc + (0.5f * alpha * scale * scale) * acc2;
+}
 
 // The wave's query weights other than the subspace ones (which need the workgroup).
 template <typename E, int D, int KIND>
 __device__ __forceinline__ void prepare_weights(const void* Q, size_t q_base, int n, int g, int G, float scale,
                                                 ScoreW<D>& W) {
-  score_weights<E, D, KIND>(Q, q_base, n, g, G, scale, W.lin);
+  if constexpr (!(kBf16Path<E, KIND> && KIND == 0)) score_weights<E, D, KIND>(Q, q_base, n, g, G, scale, W.lin);
   if constexpr (kBf16Path<E, KIND>) score_weights_bf16<D>(Q, q_base, n, g, G, W.qb);
+  if constexpr (kBf16Path<E, KIND> && KIND == 0) {
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = __uint_as_float(W.qb[j][e] << 16), b = __uint_as_float(W.qb[j][e] & 0xFFFF0000u);
+        const float a2 = a * a, b2 = b * b;
+        W.q2h[j][e] = pack_bf16x2(a2, b2);
+        W.q2l[j][e] = pack_bf16x2(a2 - __uint_as_float(W.q2h[j][e] << 16), b2 - __uint_as_float(W.q2h[j][e] & 0xFFFF0000u));
+      }
+    }
+  }
 }
 
 // After W.quad holds scale * P q: its bf16 split for the bf16 path.
@@ -420,7 +476,9 @@ __device__ __forceinline__ void finish_subspace_weights(ScoreW<D>& W) {
 template <typename E, int D, int KIND>
 __device__ __forceinline__ f32x4 tile_score(SumTile<D, KIND>& t, const void* vrow, int rank, int vlen, int g,
                                             bool use_quad, float alpha, float scale, const ScoreW<D>& W) {
-  if constexpr (kBf16Path<E, KIND>)
+  if constexpr (kBf16Path<E, KIND> && KIND == 0)
+    return sum_tile_score_diag_split<D, KIND>(t, use_quad, alpha, scale, W);
+  else if constexpr (kBf16Path<E, KIND>)
     return sum_tile_score_bf16<D, KIND>(t, vrow, rank, vlen, g, use_quad, alpha, scale, W);
   else
     return sum_tile_score<D, KIND>(t, vrow, rank, vlen, g, use_quad, alpha, W.lin,
