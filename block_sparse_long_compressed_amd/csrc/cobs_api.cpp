@@ -77,7 +77,7 @@ constexpr int kSlcTilesPerWave = 2;     // selected tiles per wave of the other 
 constexpr int kLeadTilesPerWaveNarrow = 1;   // the same with four-wave workgroups
 constexpr int kSlcTilesPerWaveNarrow = 1;
 constexpr int kScoreTilesPerWave = 4;   // 16-block summary tiles per wave of a whole-unit scoring workgroup
-constexpr int kScoreWaves = 1024;       // scoring waves of a launch with split scoring
+constexpr int kScoreWaves = 2048;       // scoring waves of a launch with split scoring
 constexpr int kWcTilesPerWave = 5;      // target window/pooled tiles per wave (eight-wave workgroups)
 constexpr int kWcTilesPerWaveNarrow = 4;   // the same with four-wave workgroups
 constexpr int kFillWorkgroups = 256;    // workgroups that fill the chip once (one per CU)

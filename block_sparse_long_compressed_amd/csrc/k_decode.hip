@@ -27,6 +27,10 @@
 //   selected  `wg_slc` per unit: the selected blocks beyond the lead's share.  Each
 //             wave polls (bounded) the codes of its own tiles; with the caller's
 //             selection they read it directly.
+// Window/pooled and selected workgroups are numbered round-robin over the units
+// (every unit's l-th workgroup before any (l+1)-th), so that when the grid exceeds
+// what the chip holds at once, the shares dispatched as earlier workgroups retire
+// are spread over all units.
 // Workgroups are dispatched in index order on each XCD, so a unit's lead is resident
 // before any workgroup that waits on it.  The wait is capped regardless: a wave that
 // gives up treats the tile as empty and sets bit 0 of the workspace status word,
@@ -51,7 +55,7 @@ namespace cobs {
 constexpr int kSelMaxSplits = 64;              // scoring workgroups per unit
 
 struct DecodeParams {
-  int hkv, group, max_len, nb_max, nb_pad, top_k;
+  int units, hkv, group, max_len, nb_max, nb_pad, top_k;
   const int32_t* seq_lens;
   const void* Q;
   // scoring / selection
@@ -215,15 +219,14 @@ __device__ __forceinline__ void merge_and_finish(const DecodeParams& p, int unit
   const int G = p.group;
   const int P = n_slots(p);
 
+  constexpr int MS = D + 4;                          // padded row: the 16 rows of a wave hit distinct banks
   __syncthreads();                                   // every wave is done with its LDS slice
-  float* mo = reinterpret_cast<float*>(smem);        // [NW][16][D] then [NW][16][2], [NW] slots
-  float* mml = mo + (size_t)NW * 16 * D;
+  float* mo = reinterpret_cast<float*>(smem);        // [NW][16][MS] then [NW][16][2], [NW] slots
+  float* mml = mo + (size_t)NW * 16 * MS;
   int* wslot = reinterpret_cast<int*>(mml + NW * 32);
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mo[((size_t)wave * 16 + n) * D + 16 * dt + 4 * g + i] = acc_o[dt][i];
-  }
+  for (int dt = 0; dt < NDT; ++dt)
+    *reinterpret_cast<f32x4*>(mo + ((size_t)wave * 16 + n) * MS + 16 * dt + 4 * g) = acc_o[dt];
   if (g == 0) { mml[(wave * 16 + n) * 2] = m_run; mml[(wave * 16 + n) * 2 + 1] = l_run; }
   if (lane == 0) wslot[wave] = wave_slot;
   __syncthreads();
@@ -237,19 +240,29 @@ __device__ __forceinline__ void merge_and_finish(const DecodeParams& p, int unit
     const int slot = my_slots[which];
     const int h = r / (D / 4), d4 = (r % (D / 4)) * 4;
     const bool sp = use_spare && which == 0;
+    // every wave's (max, sum, O) of head h are read at once (one LDS round trip),
+    // those of other slots then drop out
+    float mw[NW], lw[NW];
+    f32x4 ow[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const bool in = wslot[w] == slot;
+      mw[w] = in ? mml[(w * 16 + h) * 2] : -INFINITY;
+      lw[w] = mml[(w * 16 + h) * 2 + 1];
+      ow[w] = *reinterpret_cast<const f32x4*>(mo + ((size_t)w * 16 + h) * MS + d4);
+    }
     float M = sp ? spare[16 * D + 2 * h] : -INFINITY;
-    for (int w = 0; w < NW; ++w)
-      if (wslot[w] == slot) M = fmaxf(M, mml[(w * 16 + h) * 2]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w]);
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     float Ls = 0.f;
     if (M != -INFINITY) {
+#pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = mml[(w * 16 + h) * 2];
-        if (wslot[w] != slot || mw == -INFINITY) continue;
-        const float f = fast_exp2(mw - M);
-        Ls += f * mml[(w * 16 + h) * 2 + 1];
-        const float* src = mo + ((size_t)w * 16 + h) * D + d4;
-        o[0] += f * src[0]; o[1] += f * src[1]; o[2] += f * src[2]; o[3] += f * src[3];
+        if (mw[w] == -INFINITY) continue;
+        const float f = fast_exp2(mw[w] - M);
+        Ls += f * lw[w];
+        o += f * ow[w];
       }
       if (sp && spare[16 * D + 2 * h] != -INFINITY) {
         const float f = fast_exp2(spare[16 * D + 2 * h] - M);
@@ -372,7 +385,9 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
 
   // ---- phase 1: scores of this workgroup's tiles -------------------------
   const int tiles_total = (ncand + 15) / 16;
-  const int tile0 = (split * NW + wave) * p.sel_tpw;
+  // the unit's tiles are dealt round-robin over its scoring waves, so a sequence
+  // shorter than max_len still keeps every wave busy
+  const int tile0 = split * NW + wave, tstride = p.splits * NW;
   float run_m = -INFINITY, run_s = 0.f;        // LSE partial of head n over this lane's blocks
   // scores s4[i] of blocks tile*16 + 4g + i for head n: running LSE and the block-major
   // raw scores (LDS with one scoring workgroup, the workspace otherwise)
@@ -415,7 +430,7 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
     const float scale_log2 = p.scale * kLog2e;
 #pragma unroll 1
     for (int j = 0; j < p.sel_tpw; ++j) {
-      const int tile = tile0 + j;
+      const int tile = tile0 + j * tstride;
       if (tile >= tiles_total) break;
       f32x4 s4 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll 1
@@ -454,9 +469,10 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
   } else {
     // Summary rows are requested before the query so that both arrive in one
     // round trip, and the wave keeps RING tiles in flight: each tile's slot is
-    // refilled with the tile RING ahead as soon as it is scored.  (A rank-r tile
-    // is already several times larger than a diagonal one.)
-    constexpr int RING = KIND == 0 ? 2 : 1;
+    // refilled with the tile RING ahead as soon as it is scored.  (A fp32 rank-r
+    // tile takes 160 registers, so it has one slot; deeper rings for the
+    // compressed tiles measured no faster.)
+    constexpr int RING = (KIND == 0 || Kind<KIND>::kFp4) ? 2 : 1;
     const bool use_quad = p.alpha != 0.f;
     const size_t sum_base = (size_t)unit * p.nb_max;
     auto rows_of = [&](int tile, const void*& mr, const void*& vr) {
@@ -468,9 +484,9 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
 #pragma unroll
     for (int r = 0; r < RING; ++r) {
       vrow[r] = nullptr;
-      if (r < p.sel_tpw && tile0 + r < tiles_total) {
+      if (r < p.sel_tpw && tile0 + r * tstride < tiles_total) {
         const void* mrow;
-        rows_of(tile0 + r, mrow, vrow[r]);
+        rows_of(tile0 + r * tstride, mrow, vrow[r]);
         sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
       }
     }
@@ -489,12 +505,12 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
     for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
-        const int j = j0 + r, tile = tile0 + j0 + r;
+        const int j = j0 + r, tile = tile0 + j * tstride;
         if (j < p.sel_tpw && tile < tiles_total) {
           const f32x4 s4 = tile_score<E, D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, p.scale, W);
-          if (j + RING < p.sel_tpw && tile + RING < tiles_total) {
+          if (j + RING < p.sel_tpw && tile + RING * tstride < tiles_total) {
             const void* mrow;
-            rows_of(tile + RING, mrow, vrow[r]);
+            rows_of(tile + RING * tstride, mrow, vrow[r]);
             sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
           }
           post(tile, s4, true);
@@ -853,17 +869,17 @@ void k_decode(DecodeParams p) {
   if constexpr (KIND != 2) {
     const int j = i - p.sel_wgs;
     if (j < p.wc_wgs) {
-      wc_attention<E, D, NW>(p, j / p.wg_wc, j % p.wg_wc, smem, &flag);
+      wc_attention<E, D, NW>(p, j % p.units, j / p.units, smem, &flag);
     } else {
       const int k = j - p.wc_wgs;
-      slc_attention<E, D, NW>(p, k / p.wg_slc, k % p.wg_slc, smem, &flag);
+      slc_attention<E, D, NW>(p, k % p.units, k / p.units, smem, &flag);
     }
   }
 }
 
 template <typename E, int D, int NW>
 static size_t attn_role_lds_bytes(int P) {
-  const size_t merge = (size_t)NW * 16 * (D + 2) * sizeof(float) + NW * sizeof(int);
+  const size_t merge = (size_t)NW * 16 * (D + 4 + 2) * sizeof(float) + NW * sizeof(int);
   const size_t spare = NW == 8 ? ((size_t)16 * D + 32) * sizeof(float) : 0;   // a parked window partial
   return std::max(std::max(attn_stage_bytes<E, D, NW>(), merge), (size_t)P * 48 * sizeof(float)) + spare;
 }
@@ -905,7 +921,7 @@ size_t decode_select_lds_bytes(int nw, int nb_pad, bool raw_in_lds) {
 hipError_t launch_decode(const DecodeArgs& a) {
   DecodeParams p;
   const int units = a.batch * a.hkv;
-  p.hkv = a.hkv; p.group = a.group; p.max_len = a.max_len; p.nb_max = a.nb_max;
+  p.units = units; p.hkv = a.hkv; p.group = a.group; p.max_len = a.max_len; p.nb_max = a.nb_max;
   p.nb_pad = (a.nb_max + 15) / 16 * 16; p.top_k = a.top_k; p.seq_lens = a.seq_lens; p.Q = a.Q;
   p.sel_wgs = a.do_select ? units * a.splits : 0;
   p.splits = a.splits; p.sel_tpw = a.sel_tpw; p.rank = a.rank; p.alpha = a.alpha; p.scale = a.scale;
