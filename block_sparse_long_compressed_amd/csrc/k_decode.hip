@@ -60,10 +60,10 @@ struct DecodeParams {
   const void* Q;
   // scoring / selection
   int sel_wgs, splits, sel_tpw, rank;
-  float alpha, scale;
   const void *mu, *so;
   const float* P;               // query subspaces [hkv][sub_s][d] (subspace score kinds)
   int sub_s, vlen;              // subspace dimension; length of a rank-r vector
+  float alpha, scale;
   int32_t* sel;                 // selection written by the lead
   float* sel_score;
   uint32_t* sel_counters;

@@ -103,6 +103,10 @@ struct Kind {
   static constexpr bool kFp4 = KIND == 3 || KIND == 5;
   static constexpr bool kSub = KIND == 4 || KIND == 5;
   static constexpr bool kRank = KIND == 1 || KIND >= 3;
+  static constexpr bool kRankF32 = KIND == 1 || KIND == 4;
+  // fp32 rank-r vectors held per scoring round: a group of four takes 128 registers;
+  // the subspace kind, which also holds the projected weights, takes two
+  static constexpr int kGroupF32 = KIND == 4 ? 2 : 4;
 };
 
 // Bytes of one block's compressed record: codes, exponents, padding to 16.
@@ -134,7 +138,7 @@ template <int D, int KIND>
 struct SumTile {
   static constexpr bool kF = Kind<KIND>::kFp4;
   f32x4 m4[kF ? 1 : D / 16];
-  f32x4 v4[(KIND == 1 || KIND == 4) ? kRankGroup : 1][kF ? 1 : D / 16];
+  f32x4 v4[Kind<KIND>::kRankF32 ? Kind<KIND>::kGroupF32 : 1][kF ? 1 : D / 16];
   uint2 mb[kF ? D / 16 : 1];           // bf16 mean columns 16u + 4g .. +3
   u32x4 code[kF ? kRankGroup : 1];     // this lane's vlen/4 codes of each vector of the group
   uint32_t ex[kF ? kRankGroup : 1];    // the vector's vlen/32 exponent bytes
@@ -197,7 +201,7 @@ __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, in
   } else {
     const float* vr = static_cast<const float*>(vrow);
 #pragma unroll
-    for (int rr = 0; rr < kRankGroup; ++rr) {
+    for (int rr = 0; rr < Kind<KIND>::kGroupF32; ++rr) {
       if (r0 + rr < rank) {
 #pragma unroll
         for (int u = 0; u < D / 16; ++u)
@@ -372,10 +376,10 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
     // (v_i . q)^2 for each scaled eigenvector v_i: the projection is a linear MFMA
     // chain with the weights, squared on the VALU
 #pragma unroll 1
-    for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
+    for (int r0 = 0; r0 < rank; r0 += Kind<KIND>::kGroupF32) {
       if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, vlen, g, t);
 #pragma unroll
-      for (int rr = 0; rr < kRankGroup; ++rr) {
+      for (int rr = 0; rr < Kind<KIND>::kGroupF32; ++rr) {
         if (r0 + rr < rank) {
           f32x4 pr = {0.f, 0.f, 0.f, 0.f}, pr2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
