@@ -237,7 +237,7 @@ __device__ __forceinline__ void merge_and_finish(const DecodeParams& p, int unit
   const int items = G * (D / 4);
   for (int idx = threadIdx.x; idx < nmine * items; idx += NT) {
     const int which = idx / items, r = idx % items;
-    const int slot = my_slots[which];
+    const int slot = which == 0 ? my_slots[0] : my_slots[1];   // (no dynamically indexed array)
     const int h = r / (D / 4), d4 = (r % (D / 4)) * 4;
     const bool sp = use_spare && which == 0;
     // every wave's (max, sum, O) of head h are read at once (one LDS round trip),
@@ -306,14 +306,15 @@ __device__ __forceinline__ void merge_and_finish(const DecodeParams& p, int unit
   }
   __syncthreads();
   const int ns = slc_slots(p);
-  const int pb[4] = {0, ns, ns + p.wg_wc, P};        // SLC, WIN, CMP partial ranges
   // merge factor of partial q for head h: gate / L_branch * 2^(m_q - M_branch)
   for (int i = threadIdx.x; i < 3 * G; i += NT) {
     const int br = i / G, h = i % G;
     const int hq = head * G + h;
     float gate = (br == 0) ? 1.f : 0.f;                 // gates absent: slc only
     if (p.gates) gate = p.gates[((size_t)seq * p.hkv * G + hq) * 3 + (br == 0 ? 1 : br == 1 ? 2 : 0)];
-    const int q0 = pb[br], q1 = pb[br + 1];
+    // partial ranges: SLC [0, ns), WIN [ns, ns + wg_wc), CMP [ns + wg_wc, P)
+    const int q0 = br == 0 ? 0 : br == 1 ? ns : ns + p.wg_wc;
+    const int q1 = br == 0 ? ns : br == 1 ? ns + p.wg_wc : P;
     float M = -INFINITY, Ls = 0.f;
     for (int c0 = q0; c0 < q1; c0 += 16) {            // all reads of a chunk in flight together
       float mv[16], lv[16];
@@ -358,6 +359,57 @@ __device__ __forceinline__ void merge_and_finish(const DecodeParams& p, int unit
   if (p.pub) {                                      // codes back to "not yet" for the next call
     const Coherent pc(p.pub + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
     for (int i = threadIdx.x; i < p.top_k; i += NT) pc.st1((uint32_t)(i * 4), 0.f);
+  }
+}
+
+// Group scores shat_b = ln sum_h exp(s_{h,b} - LSE_h) of this thread's blocks
+// [b0, b0 + per) from the raw scores (LDS or workspace, [nb_pad][16] block-major),
+// as keys for the radix select.  HV float4s of head scores per block; rounds of 32
+// float4 per thread; ready() runs after the first round's loads are issued and
+// leaves the heads' LSE in lse_sh.
+template <int HV, typename Ready>
+__device__ __forceinline__ void group_scores(bool in_lds, const Coherent& sc, const float* s_raw,
+                                             const float* lse_sh, int b0, int per, int ncand, int G, float* s_shat,
+                                             uint32_t* s_key, Ready&& ready) {
+  constexpr int KR = HV == 4 ? 2 : 16 / HV;       // blocks per round
+  f32x4 raw[KR][HV];
+  auto load_round = [&](int e0) {
+#pragma unroll
+    for (int e = 0; e < KR; ++e) {
+      const int b = b0 + e0 + e;
+      const bool ok = e0 + e < per && b < ncand;
+#pragma unroll
+      for (int v = 0; v < HV; ++v) {
+        if (in_lds) raw[e][v] = ok ? *reinterpret_cast<const f32x4*>(s_raw + b * 16 + 4 * v) : f32x4{0.f, 0.f, 0.f, 0.f};
+        else raw[e][v] = ok ? sc.ld4((uint32_t)((b * 16 + 4 * v) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  load_round(0);
+  ready();
+  float lse_r[4 * HV];
+#pragma unroll
+  for (int h = 0; h < 4 * HV; ++h) lse_r[h] = (h < G) ? lse_sh[h] : 0.f;
+#pragma unroll 1
+  for (int e0 = 0; e0 < per; e0 += KR) {
+    if (e0 > 0) load_round(e0);
+#pragma unroll
+    for (int e = 0; e < KR; ++e) {
+      const int b = b0 + e0 + e;
+      if (e0 + e < per && b < ncand) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 4 * HV; ++h)
+          if (h < G) M = fmaxf(M, raw[e][h >> 2][h & 3] - lse_r[h]);
+        float S = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4 * HV; ++h)
+          if (h < G) S += __expf(raw[e][h >> 2][h & 3] - lse_r[h] - M);
+        const float sh = M + __logf(S);
+        s_shat[b] = sh;
+        s_key[b] = orderable(sh);
+      }
+    }
   }
 }
 
@@ -479,6 +531,15 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
       const int brow = min(tile * 16 + n, ncand - 1);      // A-operand row (block) of this lane
       summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, p.vlen, mr, vr);
     };
+    // the subspace kinds request P's rows and the query first: scale * P q is formed
+    // (and exchanged between the waves) while the summary tiles are in flight
+    ScoreW<D> W;
+    SubspaceRows<D> prow;
+    const size_t q_base = ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D;
+    if constexpr (Kind<KIND>::kSub) {
+      subspace_rows_load<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, wave, NW, n, g, prow);
+      prepare_weights<E, D, KIND>(p.Q, q_base, n, g, G, p.scale, W);
+    }
     SumTile<D, KIND> st[RING];
     const void* vrow[RING];
 #pragma unroll
@@ -490,17 +551,13 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
         sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
       }
     }
-    ScoreW<D> W;
-    prepare_weights<E, D, KIND>(p.Q, ((size_t)seq * (size_t)(p.hkv * G) + (size_t)head * G) * D, n, g, G, p.scale,
-                                W);
     if constexpr (Kind<KIND>::kSub) {
-      // scale * P q: four waves split the column tiles and exchange them through LDS
-      // (waves 4.. repeat the first four and write the same values)
-      const float* Ph = p.P + (size_t)head * p.sub_s * D;
-      subspace_weights_part<D>(Ph, p.sub_s, p.vlen, wave & 3, 4, n, g, W.lin, sl.wsub_x, W.quad);
+      subspace_rows_project<D>(prow, p.vlen, wave, NW, n, g, W.lin, sl.wsub_x);
       __syncthreads();
-      subspace_weights_gather<D>(p.vlen, wave & 3, 4, n, g, sl.wsub_x, W.quad);
+      subspace_weights_gather<D>(p.vlen, -1, NW, n, g, sl.wsub_x, W.quad);
       finish_subspace_weights<E, D, KIND>(W);
+    } else {
+      prepare_weights<E, D, KIND>(p.Q, q_base, n, g, G, p.scale, W);
     }
     for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
 #pragma unroll
@@ -550,28 +607,13 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
 
   // phase 2 is latency-bound: with the scores in the workspace, the first round of
   // this thread's block scores and the LSE partials are fetched together, so both
-  // cost one memory round trip
+  // cost one memory round trip (a round is 32 float4 per thread, the whole share
+  // of a thread unless the context is long and the group large)
   const int per = (p.nb_max + NT - 1) / NT;
   const int b0 = threadIdx.x * per;
-  constexpr int HV = 4;                                          // float4s of head scores per block (G <= 16)
-  constexpr int kRound = 8 / HV;                                 // blocks per load round (8 float4)
-  f32x4 raw[kRound][HV];
-  auto load_round = [&](int e0) {
-#pragma unroll
-    for (int e = 0; e < kRound; ++e) {
-      const int b = b0 + e0 + e;
-      const bool ok = e0 + e < per && b < ncand;
-#pragma unroll
-      for (int v = 0; v < HV; ++v) {
-        if (in_lds) raw[e][v] = ok ? *reinterpret_cast<const f32x4*>(s_raw + b * 16 + 4 * v) : f32x4{0.f, 0.f, 0.f, 0.f};
-        else raw[e][v] = ok ? sc.ld4((uint32_t)((b * 16 + 4 * v) * 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-  if (in_lds) {
-    __syncthreads();                              // raw scores and the LSE are in LDS
-  } else {
-    load_round(0);
+  if (in_lds) __syncthreads();                    // raw scores and the LSE are in LDS
+  auto lse_ready = [&]() {
+    if (in_lds) return;
     for (int i = threadIdx.x; i < p.splits * 16; i += NT) {
       sl.red_part[2 * i] = lp.ld1((uint32_t)(i * 8));
       sl.red_part[2 * i + 1] = lp.ld1((uint32_t)(i * 8 + 4));
@@ -587,33 +629,11 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
       sl.lse_sh[threadIdx.x] = (M == -INFINITY) ? -INFINITY : M + __logf(S);
     }
     __syncthreads();
-  }
-
-  // ---- group scores: thread owns blocks [tid*per, tid*per + per) ------------
-  float lse_r[4 * HV];
-#pragma unroll
-  for (int h = 0; h < 4 * HV; ++h) lse_r[h] = (h < G) ? sl.lse_sh[h] : 0.f;
-#pragma unroll 1
-  for (int e0 = 0; e0 < per; e0 += kRound) {
-    if (e0 > 0 || in_lds) load_round(e0);
-#pragma unroll
-    for (int e = 0; e < kRound; ++e) {
-      const int b = b0 + e0 + e;
-      if (e0 + e < per && b < ncand) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < 4 * HV; ++h)
-          if (h < G) M = fmaxf(M, raw[e][h >> 2][h & 3] - lse_r[h]);
-        float S = 0.f;
-#pragma unroll
-        for (int h = 0; h < 4 * HV; ++h)
-          if (h < G) S += __expf(raw[e][h >> 2][h & 3] - lse_r[h] - M);
-        const float sh = M + __logf(S);
-        s_shat[b] = sh;
-        s_key[b] = orderable(sh);
-      }
-    }
-  }
+  };
+  const int hv = (G + 3) / 4;                     // float4s of head scores a block needs
+  if (hv == 1) group_scores<1>(in_lds, sc, s_raw, sl.lse_sh, b0, per, ncand, G, s_shat, s_key, lse_ready);
+  else if (hv == 2) group_scores<2>(in_lds, sc, s_raw, sl.lse_sh, b0, per, ncand, G, s_shat, s_key, lse_ready);
+  else group_scores<4>(in_lds, sc, s_raw, sl.lse_sh, b0, per, ncand, G, s_shat, s_key, lse_ready);
   __syncthreads();
   if (p.sel_score) {
     float* ss = p.sel_score + (size_t)unit * p.nb_max;

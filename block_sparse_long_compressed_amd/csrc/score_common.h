@@ -529,6 +529,48 @@ __device__ __forceinline__ void subspace_weights_part(const float* P, int s, int
   }
 }
 
+// The same split into a load step and a contraction step, so that a caller can put
+// other loads between them: P's rows of the column tiles u = part and part + nparts
+// (those below vlen), then scale * P q for them into `xch`; after a barrier every
+// wave takes all column tiles with subspace_weights_gather (part = -1).
+template <int D>
+struct SubspaceRows {
+  f32x4 r[2][D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void subspace_rows_load(const float* P, int s, int vlen, int part, int nparts, int n,
+                                                   int g, SubspaceRows<D>& pr) {
+  constexpr int NU = D / 16;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = part + k * nparts, row = 16 * u + n;
+    const bool ok = u < NU && 16 * u < vlen && row < s;
+#pragma unroll
+    for (int j = 0; j < NU; ++j)
+      pr.r[k][j] = ok ? ld_f32x4(P + (size_t)row * D + 16 * j + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void subspace_rows_project(const SubspaceRows<D>& pr, int vlen, int part, int nparts,
+                                                      int n, int g, const float (&wlin)[D / 16][4], f32x4* xch) {
+  constexpr int NU = D / 16;
+  const int lane = 16 * g + n;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = part + k * nparts;
+    if (u >= NU || 16 * u >= vlen) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma_f32_16x16x4(pr.r[k][j][c], wlin[j][c], acc);
+    }
+    xch[u * 64 + lane] = acc;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void subspace_weights_gather(int vlen, int part, int nparts, int n, int g,
                                                         const f32x4* xch, float (&wq)[D / 16][4]) {
