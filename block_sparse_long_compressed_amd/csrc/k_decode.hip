@@ -114,9 +114,11 @@ __host__ __device__ constexpr size_t select_lds_bytes(int nb_pad, bool raw_in_ld
 // keys of the wave's j-th tile (0: no more tiles; valid tiles form a prefix).  The
 // next tile's K loads go out once this tile's scores are formed (overlapping the
 // softmax and P V), its V loads after P V (overlapping the next scores).  The
-// group's queries (the B operand of S = K Q^T) are requested after the first tile,
-// so no round trip precedes the tile loads; columns n >= G repeat head G-1, whose
-// scores and outputs stay in their own columns and are never merged or written.
+// group's queries (the B operand of S = K Q^T; cached, they were read by the
+// scoring) are requested just before the first tile: loads return in order, so
+// the first scores then wait for Q and K only, not for V; columns n >= G repeat
+// head G-1, whose scores and outputs stay in their own columns and are never
+// merged or written.
 // ---------------------------------------------------------------------------
 template <typename E, int D, typename Src>
 __device__ __forceinline__ void wave_tiles(Src&& src, const typename E::storage* Qg, int G, float scale_log2,
@@ -134,14 +136,14 @@ __device__ __forceinline__ void wave_tiles(Src&& src, const typename E::storage*
   const typename E::storage *Kt = nullptr, *Vt = nullptr;
   int nv = src(0, Kt, Vt);
   if (nv <= 0) return;
-  tile_load_k<E, D>(Kt, nv, tr);
-  tile_load_v<E, D>(Vt, nv, tr);
   u32x4 qf[NCH];
   {
     const typename E::storage* Qh = Qg + (size_t)min(n, G - 1) * D;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
   }
+  tile_load_k<E, D>(Kt, nv, tr);
+  tile_load_v<E, D>(Vt, nv, tr);
   for (int j = 0; nv > 0; ++j) {
     f32x4 sc4[4];
     tile_scores<E, D>(tr, qf, sc4);
@@ -156,9 +158,9 @@ __device__ __forceinline__ void wave_tiles(Src&& src, const typename E::storage*
 }
 
 // The same for a wave with at most two tiles (the selecting workgroup's share of
-// the selected blocks): both tiles' K loads go out at once, so the second tile's
-// scores need no round trip of their own; its V loads follow once V of the first
-// tile is staged.
+// the selected blocks): Q, then both tiles' K loads and the first tile's V go out
+// at once, so the second tile's scores need no round trip of their own; its V
+// loads follow once V of the first tile is staged.
 template <typename E, int D, typename Src>
 __device__ __forceinline__ void wave_tiles_pair(Src&& src, const typename E::storage* Qg, int G, float scale_log2,
                                                 typename E::storage* lds, float& m_run, float& l_run,
@@ -176,15 +178,15 @@ __device__ __forceinline__ void wave_tiles_pair(Src&& src, const typename E::sto
   if (n0 <= 0) return;
   const int n1 = src(1, K1, V1);
   TileRegs<E, D> t0, t1;
-  tile_load_k<E, D>(K0, n0, t0);
-  tile_load_v<E, D>(V0, n0, t0);
-  if (n1 > 0) tile_load_k<E, D>(K1, n1, t1);
   u32x4 qf[NCH];
   {
     const typename E::storage* Qh = Qg + (size_t)min(n, G - 1) * D;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
   }
+  tile_load_k<E, D>(K0, n0, t0);
+  tile_load_v<E, D>(V0, n0, t0);
+  if (n1 > 0) tile_load_k<E, D>(K1, n1, t1);
   f32x4 sc4[4];
   tile_scores<E, D>(t0, qf, sc4);
   tile_stage_v<E, D>(t0, lds);
@@ -770,15 +772,15 @@ __device__ __forceinline__ void wc_attention(const DecodeParams& p, int unit, in
     TileRegs<E, D> tr;
     const typename E::storage *Kt = nullptr, *Vt = nullptr;
     int nv = src(j0, Kt, Vt);
-    tile_load_k<E, D>(Kt, nv, tr);
-    tile_load_v<E, D>(Vt, nv, tr);
-    u32x4 qf[NCH];
+    u32x4 qf[NCH];                                // Q first: the first scores wait for Q and K only
     {
       const typename E::storage* Qh = reinterpret_cast<const typename E::storage*>(p.Q) +
                                       ((size_t)seq * p.hkv * G + (size_t)head * G + min(n, G - 1)) * D;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) qf[c] = ld16(Qh + (4 * c + g) * EPL);
     }
+    tile_load_k<E, D>(Kt, nv, tr);
+    tile_load_v<E, D>(Vt, nv, tr);
     for (int t = j0; t < j1; ++t) {
       f32x4 sc4[4];
       tile_scores<E, D>(tr, qf, sc4);
