@@ -33,6 +33,7 @@
 namespace cobs {
 
 constexpr int kLrThreads = 256;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kN = 64;              // Gram size (keys per block)
 constexpr double kEps = 0x1p-52;          // fp64 unit roundoff (2^-53) times 2
 constexpr double kSafeMin = 0x1p-1021;    // safe minimum (1 / it does not overflow)
@@ -183,7 +184,7 @@ __device__ void quantize_record(const double (*vout)[D], int (*gexp)[D / 32], ui
   __syncthreads();
 }
 
-template <typename E, int D>
+template <typename E, int D, bool SUB>
 __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __restrict__ seq_lens,
                                                               const int32_t* __restrict__ old_lens, int max_len,
                                                               int nb_max, int rank,
@@ -193,7 +194,12 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
                                                               int vlen) {
   __shared__ double A[kN][kN + 1];      // Gram matrix, reduced in place (+1: bank spread)
   // the block's keys (fp32, exact for bf16) until G is built, then the Householder vectors
-  __shared__ union { float k[kN][D + 1]; double v[kN][kN + 1]; } kv;
+  // (with a query subspace, the projected keys Y = X P^T replace the keys before G)
+  __shared__ union {
+    float k[kN][D + 1];
+    double v[kN][kN + 1];
+    double y[SUB ? kN : 1][SUB ? D + 1 : 1];
+  } kv;
   __shared__ double mu[D];
   __shared__ double red[4];
   __shared__ double lam_sel[8];
@@ -238,58 +244,76 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
   }
   __syncthreads();
   // Gram matrix G = X X^T / n (or, with a query subspace P, G = Y Y^T / n for the
-  // projected keys Y = X P^T, whose covariance is P C P^T): each thread a 4x4 tile,
-  // zero outside the n x n corner
+  // projected keys Y = X P^T, whose covariance is P C P^T) on the fp64 MFMA
+  // (v_mfma_f64_16x16x4_f64: lane (r, q) = (lane % 16, lane / 16) holds A[r][q] and
+  // B[q][r] of a 16x16x4 step and rows q, q + 4, q + 8, q + 12 of column r of the
+  // 16x16 result):
+  // wave w forms rows 16w..16w+15, the four waves together the 64 x 64 corner
+  // (zero outside n x n, as the centred rows >= n are zero)
   {
-    const int ta = tid / 16, tb = tid % 16;
-    double acc[4][4];
+    const int lane = tid & 63, wv = tid >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int ra = 16 * wv + r16;
+    const double inv_n = 1.0 / (double)n;
+    auto xc = [&](int r, int c) -> double { return (r < n) ? (double)kv.k[r][c] - mu[c] : 0.0; };
+    f64x4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    if (Psub) {
-      // 16 columns of Y = X P^T at a time, staged in A's space (A is written after)
-      double (*ych)[17] = reinterpret_cast<double (*)[17]>(&A[0][0]);
+    for (int tj = 0; tj < 4; ++tj) acc[tj] = f64x4{0.0, 0.0, 0.0, 0.0};
+    if constexpr (SUB) {
+      // Y = X P^T, 16 columns per tile (columns >= sub_s are zero), into LDS over the keys
       const float* Pu = Psub + (size_t)head * sub_s * D;
-      for (int j0 = 0; j0 < sub_s; j0 += 16) {
-        for (int idx = tid; idx < kN * 16; idx += kLrThreads) {
-          const int r = idx / 16, jj = idx % 16, j = j0 + jj;
-          double y = 0.0;
-          if (r < n && j < sub_s) {
-            const float* pr = Pu + (size_t)j * D;
-            for (int c = 0; c < D; ++c) y += ((double)kv.k[r][c] - mu[c]) * (double)pr[c];
+      const int ntj = (sub_s + 15) / 16;
+      f64x4 yacc[D / 16];
+#pragma unroll
+      for (int tj = 0; tj < D / 16; ++tj) yacc[tj] = f64x4{0.0, 0.0, 0.0, 0.0};
+      // 32 columns of P per round: all their loads go out before the contraction
+      for (int c1 = 0; c1 < D; c1 += 32) {
+        float pb[8][D / 16];
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+#pragma unroll
+          for (int tj = 0; tj < D / 16; ++tj) {
+            const int j = 16 * tj + r16;
+            pb[s8][tj] = (tj < ntj && j < sub_s) ? Pu[(size_t)j * D + c1 + 4 * s8 + kq] : 0.f;
           }
-          ych[r][jj] = y;
         }
-        __syncthreads();
-        for (int jj = 0; jj < 16; ++jj) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const double a = xc(ra, c1 + 4 * s8 + kq);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] += ych[4 * ta + i][jj] * ych[4 * tb + j][jj];
+          for (int tj = 0; tj < D / 16; ++tj)
+            if (tj < ntj) yacc[tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)pb[s8][tj], yacc[tj], 0, 0, 0);
         }
-        __syncthreads();
+      }
+      __syncthreads();                             // every wave is done with the keys
+#pragma unroll
+      for (int tj = 0; tj < D / 16; ++tj) {
+        if (tj < ntj) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kv.y[16 * wv + kq + 4 * i][16 * tj + r16] = yacc[tj][i];
+        }
+      }
+      __syncthreads();
+      for (int j0 = 0; j0 < 16 * ntj; j0 += 4) {
+        const int j = j0 + kq;
+        const double a = kv.y[ra][j];
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj)
+          acc[tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, kv.y[16 * tj + r16][j], acc[tj], 0, 0, 0);
       }
     } else {
-      for (int c = 0; c < D; ++c) {
-        const double m = mu[c];
-        double xi[4], xj[4];
+      for (int c0 = 0; c0 < D; c0 += 4) {
+        const int c = c0 + kq;
+        const double a = xc(ra, c);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          xi[k] = (4 * ta + k < n) ? (double)kv.k[4 * ta + k][c] - m : 0.0;
-          xj[k] = (4 * tb + k < n) ? (double)kv.k[4 * tb + k][c] - m : 0.0;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] += xi[i] * xj[j];
+        for (int tj = 0; tj < 4; ++tj) acc[tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, xc(16 * tj + r16, c), acc[tj], 0, 0, 0);
       }
     }
-    const double inv_n = 1.0 / (double)n;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int tj = 0; tj < 4; ++tj) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) A[4 * ta + i][4 * tb + j] = acc[i][j] * inv_n;
+      for (int i = 0; i < 4; ++i) A[16 * wv + kq + 4 * i][16 * tj + r16] = acc[tj][i] * inv_n;
+    }
   }
   __syncthreads();
   // ---- top-r eigenpairs of G ------------------------------------------------
@@ -575,9 +599,16 @@ __global__ __launch_bounds__(kLrThreads) void k_build_lowrank(const int32_t* __r
 template <typename E, int D>
 static hipError_t launch_lr(const BuildArgs& a) {
   dim3 grid(a.old_lens ? a.touch_blocks : a.nb_max, a.hkv, a.batch);
-  hipLaunchKernelGGL((k_build_lowrank<E, D>), grid, dim3(kLrThreads), 0, a.stream, a.seq_lens, a.old_lens,
-                     a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank, a.fp4 ? 1 : 0,
-                     a.P, a.sub_s, a.vlen);
+  // the query-subspace build keeps the projected keys in LDS (its own instantiation,
+  // so the plain build keeps the smaller LDS footprint)
+  if (a.P)
+    hipLaunchKernelGGL((k_build_lowrank<E, D, true>), grid, dim3(kLrThreads), 0, a.stream, a.seq_lens, a.old_lens,
+                       a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank, a.fp4 ? 1 : 0,
+                       a.P, a.sub_s, a.vlen);
+  else
+    hipLaunchKernelGGL((k_build_lowrank<E, D, false>), grid, dim3(kLrThreads), 0, a.stream, a.seq_lens, a.old_lens,
+                       a.max_len, a.nb_max, a.rank, (const typename E::storage*)a.K, a.lowrank, a.fp4 ? 1 : 0,
+                       a.P, a.sub_s, a.vlen);
   return hipGetLastError();
 }
 
