@@ -26,8 +26,8 @@ def _step(p, g, s, ws):
 
 def test_wait_give_up_is_reported_and_harmless():
     torch.cuda.set_device(0)
-    # top-k 32 with groups of 16 heads: the selecting workgroup attends to the first
-    # 16 selected blocks and waiting workgroups take the rest
+    # top-k 32 with 8 units: the selecting workgroup attends to the first few selected
+    # blocks and waiting workgroups take the rest
     w = synth.Workload("status_b2_L3000", batch=2, max_len=3000, min_len=2200, n_q_heads=64, n_kv_heads=4,
                        head_dim=128, top_k=32, window=256, cmp_len=32, cmp_stride=16, so_kind="diag", rank=0,
                        alpha=1.0, dtype="bf16", needles=2)
