@@ -127,6 +127,11 @@ struct Coherent {
   __device__ __forceinline__ float ld1(uint32_t byte_off) const {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc, byte_off, 0, kCoherent));
   }
+  // the same load marked volatile (bit 31 of the cache-policy operand), for a value
+  // another workgroup publishes while this one polls: it is re-read on every call
+  __device__ __forceinline__ uint32_t poll1(uint32_t byte_off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, byte_off, 0, kCoherent | (int)0x80000000u);
+  }
 };
 
 // All threads: wait until this thread's coherent stores are acknowledged, then

@@ -837,7 +837,7 @@ __device__ __forceinline__ void slc_attention(const DecodeParams& p, int unit, i
       const Coherent pc(p.pub + (size_t)unit * p.top_k, (uint32_t)(p.top_k * 4));
       uint32_t code = 0;
       for (uint32_t it = 0; it < p.poll_cap; ++it) {
-        code = __float_as_uint(pc.ld1((uint32_t)(t * 4)));
+        code = pc.poll1((uint32_t)(t * 4));
         if (code != 0u) break;
         __builtin_amdgcn_s_sleep(1);
       }

@@ -68,7 +68,7 @@ def check_fp4(w, x, s, units=None, gap_min=1e-2):
     p = O.params_of(w)
     d, r, G = w.head_dim, w.rank, w.group
     vlen = -(-w.subspace // 32) * 32 if w.subspace else d
-    mu = s["mu"].float().cpu().numpy().astype(np.float64)
+    mu_dev = s["mu"]                       # blocks past a sequence's end are never written: sliced before any cast
     codes, exps = unpack_records(s["so"].cpu().numpy(), r, vlen)
     units = units or [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
     strict = loose = exempt = total = mu_equal = mu_total = 0
@@ -79,9 +79,11 @@ def check_fp4(w, x, s, units=None, gap_min=1e-2):
         Ph = None if not w.subspace else x["P"][h].astype(np.float64)
         rmu, rso, n = O.summaries(keys, L, "lowrank_fp4", r, Ph)
         nb = len(n)
+        mu_u = mu_dev[b, h, :nb].float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(mu_u).all(), (b, h)
         ulp = np.maximum(np.abs(rmu), 1e-38) * 2.0 ** -7
-        assert (np.abs(mu[b, h, :nb] - rmu) <= ulp * 1.0001).all(), (b, h)
-        mu_equal += int((mu[b, h, :nb] == rmu).sum())
+        assert (np.abs(mu_u - rmu) <= ulp * 1.0001).all(), (b, h)
+        mu_equal += int((mu_u == rmu).sum())
         mu_total += rmu.size
         q = x["Q"][b, 0, h * G:(h + 1) * G].astype(np.float64) * p["scale"]
         if Ph is not None:
