@@ -49,6 +49,7 @@
 #include "score_common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace cobs {
 
@@ -526,11 +527,16 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
     // refilled with the tile RING ahead as soon as it is scored.  (A fp32 rank-r
     // tile takes 160 registers, so it has one slot; deeper rings for the
     // compressed tiles measured no faster.)
+    // Every slot is refilled with the same loads whether or not its next tile exists
+    // (rows past the unit's candidates repeat the last one and are never posted),
+    // and use_quad is a compile-time constant of the loop: the compiler then knows
+    // how many loads were issued after each tile's, so a tile's scores wait for that
+    // tile only and not also for the tile requested behind it.  Only the last round
+    // requests nothing.
     constexpr int RING = (KIND == 0 || Kind<KIND>::kFp4) ? 2 : 1;
-    const bool use_quad = p.alpha != 0.f;
     const size_t sum_base = (size_t)unit * p.nb_max;
     auto rows_of = [&](int tile, const void*& mr, const void*& vr) {
-      const int brow = min(tile * 16 + n, ncand - 1);      // A-operand row (block) of this lane
+      const int brow = max(0, min(tile * 16 + n, ncand - 1));   // A-operand row (block) of this lane
       summary_rows<D, KIND>(p.mu, p.so, sum_base + brow, p.rank, p.vlen, mr, vr);
     };
     // the subspace kinds request P's rows and the query first: scale * P q is formed
@@ -542,40 +548,47 @@ __device__ __forceinline__ bool select_role(const DecodeParams& p, int unit, int
       subspace_rows_load<D>(p.P + (size_t)head * p.sub_s * D, p.sub_s, p.vlen, wave, NW, n, g, prow);
       prepare_weights<E, D, KIND>(p.Q, q_base, n, g, G, p.scale, W);
     }
-    SumTile<D, KIND> st[RING];
-    const void* vrow[RING];
+    auto ring = [&](auto quad_c) {
+      constexpr bool Q = decltype(quad_c)::value;
+      SumTile<D, KIND> st[RING];
+      const void* vrow[RING];
 #pragma unroll
-    for (int r = 0; r < RING; ++r) {
-      vrow[r] = nullptr;
-      if (r < p.sel_tpw && tile0 + r * tstride < tiles_total) {
+      for (int r = 0; r < RING; ++r) {
         const void* mrow;
         rows_of(tile0 + r * tstride, mrow, vrow[r]);
-        sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
+        sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, Q, st[r]);
       }
-    }
-    if constexpr (Kind<KIND>::kSub) {
-      subspace_rows_project<D>(prow, p.vlen, wave, NW, n, g, W.lin, sl.wsub_x);
-      __syncthreads();
-      subspace_weights_gather<D>(p.vlen, -1, NW, n, g, sl.wsub_x, W.quad);
-      finish_subspace_weights<E, D, KIND>(W);
-    } else {
-      prepare_weights<E, D, KIND>(p.Q, q_base, n, g, G, p.scale, W);
-    }
-    for (int j0 = 0; j0 < p.sel_tpw; j0 += RING) {
+      if constexpr (Kind<KIND>::kSub) {
+        subspace_rows_project<D>(prow, p.vlen, wave, NW, n, g, W.lin, sl.wsub_x);
+        __syncthreads();
+        subspace_weights_gather<D>(p.vlen, -1, NW, n, g, sl.wsub_x, W.quad);
+        finish_subspace_weights<E, D, KIND>(W);
+      } else {
+        prepare_weights<E, D, KIND>(p.Q, q_base, n, g, G, p.scale, W);
+      }
+      int j0 = 0;
+      for (; j0 + RING < p.sel_tpw; j0 += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) {
+          const int tile = tile0 + (j0 + r) * tstride;
+          const f32x4 s4 = tile_score<E, D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, Q, p.alpha, p.scale, W);
+          const void* mrow;
+          rows_of(tile + RING * tstride, mrow, vrow[r]);
+          sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, Q, st[r]);
+          if (tile < tiles_total) post(tile, s4, true);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < RING; ++r) {
         const int j = j0 + r, tile = tile0 + j * tstride;
         if (j < p.sel_tpw && tile < tiles_total) {
-          const f32x4 s4 = tile_score<E, D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, use_quad, p.alpha, p.scale, W);
-          if (j + RING < p.sel_tpw && tile + RING * tstride < tiles_total) {
-            const void* mrow;
-            rows_of(tile + RING * tstride, mrow, vrow[r]);
-            sum_tile_load<D, KIND>(mrow, vrow[r], p.rank, p.vlen, g, use_quad, st[r]);
-          }
+          const f32x4 s4 = tile_score<E, D, KIND>(st[r], vrow[r], p.rank, p.vlen, g, Q, p.alpha, p.scale, W);
           post(tile, s4, true);
         }
       }
-    }
+    };
+    if (p.alpha != 0.f) ring(std::true_type{});
+    else ring(std::false_type{});
   }
 #pragma unroll
   for (int m = 16; m < 64; m <<= 1) {

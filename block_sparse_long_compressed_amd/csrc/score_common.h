@@ -142,7 +142,17 @@ struct SumTile {
   uint2 mb[kF ? D / 16 : 1];           // bf16 mean columns 16u + 4g .. +3
   u32x4 code[kF ? kRankGroup : 1];     // this lane's vlen/4 codes of each vector of the group
   uint32_t ex[kF ? kRankGroup : 1];    // the vector's vlen/32 exponent bytes
+  // subspace kinds: the record's exponent block (a 32-byte window) as loaded; each
+  // vector's bytes are cut from it when the tile is scored (sub_tile_exponents)
+  u32x4 exw[kF && Kind<KIND>::kSub ? 2 : 1];
 };
+
+// 16 bytes from a 4-byte aligned address (one dwordx4 load).
+__device__ __forceinline__ u32x4 ld16_a4(const void* p) {
+  u32x4 v;
+  __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 16);
+  return v;
+}
 
 template <int D, int KIND>
 __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, int rank, int vlen, int g,
@@ -150,21 +160,21 @@ __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, in
   if constexpr (Kind<KIND>::kFp4) {
     const uint8_t* rec = static_cast<const uint8_t*>(vrow);
     // subspace kinds: the exponent block starts 16-aligned at rank * vlen/2 and the
-    // record extends at least 16 bytes past it (32 when it holds more than 16 bytes)
-    u32x4 e0 = {0u, 0u, 0u, 0u}, e1 = {0u, 0u, 0u, 0u};
+    // record extends at least 16 bytes past it (32 when it holds more than 16 bytes).
+    // Every load here is unconditional in its width and address (no branch on the
+    // runtime vlen), so no value is moved or cut before it has arrived and the tile's
+    // loads stay in flight while the wave scores other tiles.
     if constexpr (Kind<KIND>::kSub) {
       const uint8_t* ep = rec + rank * (vlen / 2);
-      e0 = *reinterpret_cast<const u32x4*>(ep);
-      if (rank * (vlen / 32) > 16) e1 = *reinterpret_cast<const u32x4*>(ep + 16);
+      t.exw[0] = *reinterpret_cast<const u32x4*>(ep);
+      t.exw[1] = *reinterpret_cast<const u32x4*>(ep + (rank * (vlen / 32) > 16 ? 16 : 0));
     }
-    auto ew = [&](int i) -> uint32_t {                // word i of the 32-byte exponent window
-      return i == 0 ? e0[0] : i == 1 ? e0[1] : i == 2 ? e0[2] : i == 3 ? e0[3]
-           : i == 4 ? e1[0] : i == 5 ? e1[1] : i == 6 ? e1[2] : e1[3];
-    };
+    // vectors past the rank repeat the last one (loaded, never scored), so a tile
+    // always has the same loads in flight
 #pragma unroll
     for (int rr = 0; rr < kRankGroup; ++rr) {
-      const int r = r0 + rr;
-      if (r < rank) {
+      const int r = min(r0 + rr, rank - 1);
+      {
         if constexpr (!Kind<KIND>::kSub) {
           const uint8_t* cp = rec + r * (D / 2) + g * (D / 8);
           if constexpr (D == 128) {
@@ -176,36 +186,25 @@ __device__ __forceinline__ void sum_tile_load_group(const void* vrow, int r0, in
             t.ex[rr] = *reinterpret_cast<const uint16_t*>(rec + rank * (D / 2) + r * (D / 32));
           }
         } else {
-          // vlen/32 code words per lane (one load of 1-4 dwords, 4-byte aligned) and
-          // vlen/32 exponent bytes per vector, cut from the record's exponent block
-          const int nw = vlen / 32;
-          const uint8_t* cp = rec + r * (vlen / 2) + g * (vlen / 8);
-          if (nw == 4) {
-            t.code[rr] = *reinterpret_cast<const u32x4*>(cp);
-          } else if (nw == 3) {
-            const uint3 c3 = *reinterpret_cast<const uint3*>(cp);
-            t.code[rr] = u32x4{c3.x, c3.y, c3.z, 0u};
-          } else if (nw == 2) {
-            const uint2 c2 = *reinterpret_cast<const uint2*>(cp);
-            t.code[rr] = u32x4{c2.x, c2.y, 0u, 0u};
-          } else {
-            t.code[rr] = u32x4{*reinterpret_cast<const uint32_t*>(cp), 0u, 0u, 0u};
-          }
-          const int o = r * nw, wi = o >> 2, sh = 8 * (o & 3);
-          const uint32_t lo = ew(wi), hi = ew(wi + 1);
-          const uint32_t ex = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
-          t.ex[rr] = nw == 4 ? ex : ex & ((1u << (8 * nw)) - 1u);
+          // the lane's vlen/32 code words: one 16-byte load at 4-byte alignment.  Below
+          // vlen = 128 it also reads up to 12 bytes that follow the run (the next lane's
+          // codes or the exponent block), inside the record for every rank 1-8 and
+          // vlen 32, 64, 96; words j >= vlen/32 are never decoded
+          t.code[rr] = ld16_a4(rec + r * (vlen / 2) + g * (vlen / 8));
         }
       }
     }
   } else {
+    // vectors past the rank and columns past vlen repeat the last ones (loaded, never
+    // scored), so a tile always has the same loads in flight
     const float* vr = static_cast<const float*>(vrow);
 #pragma unroll
     for (int rr = 0; rr < Kind<KIND>::kGroupF32; ++rr) {
-      if (r0 + rr < rank) {
+      const int r = min(r0 + rr, rank - 1);
 #pragma unroll
-        for (int u = 0; u < D / 16; ++u)
-          if (!Kind<KIND>::kSub || 16 * u < vlen) t.v4[rr][u] = ld_f32x4(vr + (r0 + rr) * vlen + 16 * u + 4 * g);
+      for (int u = 0; u < D / 16; ++u) {
+        const int ul = Kind<KIND>::kSub ? min(u, vlen / 16 - 1) : u;
+        t.v4[rr][u] = ld_f32x4(vr + r * vlen + 16 * ul + 4 * g);
       }
     }
   }
@@ -232,6 +231,28 @@ __device__ __forceinline__ void sum_tile_load(const void* mrow, const void* vrow
       } else {
         sum_tile_load_group<D, KIND>(vrow, 0, rank, vlen, g, t);
       }
+    }
+  }
+}
+
+// Subspace kinds: the vlen/32 exponent bytes of vectors r0 .. r0+3 from the loaded
+// exponent window (called when the tile is scored, its loads complete).
+template <int D, int KIND>
+__device__ __forceinline__ void sub_tile_exponents(SumTile<D, KIND>& t, int r0, int vlen) {
+  if constexpr (Kind<KIND>::kFp4 && Kind<KIND>::kSub) {
+    const int nw = vlen / 32;
+    const u32x4 a = t.exw[0], b = t.exw[1];
+    auto ew = [&](int i) -> uint32_t {                // word i (0-7) of the 32-byte exponent window
+      const u32x4 v = (i & 4) ? b : a;                // selects of values, no indexed memory
+      const uint32_t lo = (i & 1) ? v[1] : v[0], hi = (i & 1) ? v[3] : v[2];
+      return (i & 2) ? hi : lo;
+    };
+#pragma unroll
+    for (int rr = 0; rr < kRankGroup; ++rr) {
+      const int o = (r0 + rr) * nw, wi = o >> 2, sh = 8 * (o & 3);
+      const uint32_t lo = ew(wi), hi = ew(wi + 1);
+      const uint32_t ex = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
+      t.ex[rr] = nw == 4 ? ex : ex & ((1u << (8 * nw)) - 1u);
     }
   }
 }
@@ -263,6 +284,7 @@ __device__ __forceinline__ f32x4 sum_tile_score_bf16(SumTile<D, KIND>& t, const 
 #pragma unroll 1
   for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
     if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, vlen, g, t);
+    sub_tile_exponents<D, KIND>(t, r0, vlen);
 #pragma unroll
     for (int rr = 0; rr < kRankGroup; ++rr) {
       if (r0 + rr < rank) {
@@ -338,6 +360,7 @@ __device__ __forceinline__ f32x4 sum_tile_score(SumTile<D, KIND>& t, const void*
 #pragma unroll 1
     for (int r0 = 0; r0 < rank; r0 += kRankGroup) {
       if (r0 > 0) sum_tile_load_group<D, KIND>(vrow, r0, rank, vlen, g, t);
+      sub_tile_exponents<D, KIND>(t, r0, vlen);
 #pragma unroll
       for (int rr = 0; rr < kRankGroup; ++rr) {
         if (r0 + rr < rank) {
