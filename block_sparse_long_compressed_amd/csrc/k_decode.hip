@@ -794,16 +794,21 @@ __device__ __forceinline__ void wc_attention(const DecodeParams& p, int unit, in
     }
     tile_load_k<E, D>(Kt, nv, tr);
     tile_load_v<E, D>(Vt, nv, tr);
-    for (int t = j0; t < j1; ++t) {
+    // Every tile but the last requests the next one unconditionally (K after the
+    // scores, V as soon as this tile's V is staged, before P V), so the compiler's
+    // load counts are exact: staging waits for this tile's V only, not for the K
+    // just requested behind it.  The last tile is peeled off and requests nothing.
+    int t = j0;
+    for (; t + 1 < j1; ++t) {
       f32x4 sc4[4];
       tile_scores<E, D>(tr, qf, sc4);
       const typename E::storage *Kn = nullptr, *Vn = nullptr;
-      const int nv_next = (t + 1 < j1) ? src(t + 1, Kn, Vn) : 0;
-      if (nv_next > 0) tile_load_k<E, D>(Kn, nv_next, tr);
+      const int nv_next = src(t + 1, Kn, Vn);
+      tile_load_k<E, D>(Kn, nv_next, tr);
       tile_stage_v<E, D>(tr, lds);
+      tile_load_v<E, D>(Vn, nv_next, tr);
       tile_softmax_pv<E, D>(sc4, nv, p.scale_log2, lds, m_run, l_run, acc_o);
-      if (nv_next > 0) tile_load_v<E, D>(Vn, nv_next, tr);
-      if (t + 1 == t_win && t + 1 < j1) {          // window part done, pooled tiles follow
+      if (t + 1 == t_win) {                        // window part done, pooled tiles follow
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -817,6 +822,10 @@ __device__ __forceinline__ void wc_attention(const DecodeParams& p, int unit, in
       }
       nv = nv_next;
     }
+    f32x4 sc4[4];
+    tile_scores<E, D>(tr, qf, sc4);
+    tile_stage_v<E, D>(tr, lds);
+    tile_softmax_pv<E, D>(sc4, nv, p.scale_log2, lds, m_run, l_run, acc_o);
   }
   const int ns = slc_slots(p);
   const int mine[2] = {ns + local, ns + p.wg_wc + local};
