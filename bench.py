@@ -12,7 +12,7 @@ pooled tokens, Q, gates), with enough replicas that a step's bytes are not
 served from the 256 MB last-level cache by an earlier step; steps are issued as
 HIP graph replays so host launch overhead does not bound the GPU.
 
-Prints one JSON line (last line of stdout).  --gpus > 1 is refused: this build
+Prints one JSON line (last line of stdout).  --gpus > 1 is refused: the library
 runs on one GPU.
 """
 from __future__ import annotations
@@ -319,7 +319,7 @@ def main():
                          "copy (plain copy of known size, to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported; this build measures one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported; the library runs on one GPU "
               "(multi-GPU sharding is a design note only)", file=sys.stderr)
         sys.exit(2)
 
